@@ -1,0 +1,331 @@
+/*
+ * sconv_oracle.c -- plain, slow CPU oracle (see sconv_oracle.h).
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the product path.
+ *
+ * Each function is the definition written out as nested loops in the order
+ * the pages describe the computation: no blocking, no fusion, no reordering.
+ * Readings of points the pages leave open are marked "Reading:".
+ */
+#include "sconv_oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Element access.                                                     */
+/* ------------------------------------------------------------------ */
+
+double oracle_bf16_to_double(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16; /* bfloat16 is the top half of a float */
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Round a double to the nearest bfloat16 (8 significant bits, float's
+ * exponent range), ties to even, with gradual underflow and overflow to
+ * infinity.  Works on the value, not on float bits, so there is exactly one
+ * rounding step between the double result and the stored bfloat16. */
+uint16_t oracle_round_bf16(double v) {
+  uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+  double a = fabs(v);
+  if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);              /* 2^(e-1) <= a < 2^e */
+  int E = e - 1;             /* unbiased exponent */
+  if (E < -126) E = -126;    /* subnormal range: fixed quantum */
+  double q = ldexp(1.0, E - 7);          /* spacing of bfloat16 values here */
+  double r = nearbyint(a / q) * q;       /* default mode: ties to even */
+  const double max_bf16 = ldexp(255.0, 127 - 7); /* (2 - 2^-7) * 2^127 */
+  if (r > max_bf16) return (uint16_t)(sign | 0x7F80u);
+  float f = (float)r;        /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | (uint16_t)(u >> 16));
+}
+
+double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
+
+static size_t elem_size(int dtype) {
+  return dtype == ORC_F32 ? 4 : dtype == ORC_BF16 ? 2 : 8;
+}
+
+static double ld(const void* p, int dtype, int64_t i) {
+  if (dtype == ORC_F32) return (double)((const float*)p)[i];
+  if (dtype == ORC_BF16) return oracle_bf16_to_double(((const uint16_t*)p)[i]);
+  return ((const double*)p)[i];
+}
+
+static void st(void* p, int dtype, int64_t i, double v) {
+  if (dtype == ORC_F32)
+    ((float*)p)[i] = (float)v; /* C conversion: round to nearest even */
+  else if (dtype == ORC_BF16)
+    ((uint16_t*)p)[i] = oracle_round_bf16(v);
+  else
+    ((double*)p)[i] = v;
+}
+
+/* Bit-for-bit copy of one element (cache and state writes are copies). */
+static void copy_elem(void* dst, int64_t di, const void* src, int64_t si, int dtype) {
+  size_t es = elem_size(dtype);
+  memcpy((char*)dst + (size_t)di * es, (const char*)src + (size_t)si * es, es);
+}
+
+static void store_zero(void* dst, int64_t di, int dtype) {
+  size_t es = elem_size(dtype);
+  memset((char*)dst + (size_t)di * es, 0, es);
+}
+
+static int valid_dtype(int dtype) {
+  return dtype == ORC_F32 || dtype == ORC_BF16 || dtype == ORC_F64;
+}
+
+static double activate(double v, int act) {
+  return act == ORC_ACT_SILU ? oracle_silu(v) : v;
+}
+
+/* ------------------------------------------------------------------ */
+/* sconv_seq_metadata                                                  */
+/* ------------------------------------------------------------------ */
+
+int oracle_seq_metadata(const int32_t* qsl, int32_t num_reqs, int64_t num_actual,
+                        int64_t num_padded, int32_t* seq_idx_out,
+                        int32_t* query_start_out) {
+  if (num_actual < 0 || num_padded < num_actual) return ORC_ERR_ARGS;
+  if (num_actual > 0 && num_reqs < 1) return ORC_ERR_ARGS;
+  for (int64_t t = 0; t < num_actual; ++t) {
+    /* The request whose row range [qsl[r], qsl[r+1]) contains row t.
+     * An empty request has an empty range and never matches. */
+    int32_t r = -1;
+    for (int32_t rr = 0; rr < num_reqs; ++rr) {
+      if ((int64_t)qsl[rr] <= t && t < (int64_t)qsl[rr + 1]) {
+        r = rr;
+        break;
+      }
+    }
+    /* Reading: a row past the last request's end is clamped to the last
+     * request, as a sorted search followed by a clamp would do; a row before
+     * qsl[0] (never the case when qsl[0] == 0) goes to request 0. */
+    if (r < 0) r = (t >= (int64_t)qsl[num_reqs]) ? num_reqs - 1 : 0;
+    seq_idx_out[t] = r;
+    query_start_out[t] = qsl[r];
+  }
+  for (int64_t t = num_actual; t < num_padded; ++t) {
+    seq_idx_out[t] = 0;      /* padded rows are zero-filled */
+    query_start_out[t] = 0;
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* fused insert + depthwise causal conv over the paged cache           */
+/* ------------------------------------------------------------------ */
+
+int oracle_fused_insert_conv(const void* x, int64_t x_rs, const void* w, int64_t w_sc,
+                             int64_t w_sk, const void* cache_in, void* cache_out,
+                             int64_t num_blocks, int32_t H, int32_t N, int32_t D,
+                             int64_t cs0, int64_t cs1, int64_t cs2,
+                             const int64_t* positions, const int32_t* block_table,
+                             int64_t bt_rs, int32_t num_reqs, int32_t max_blocks,
+                             const int32_t* seq_idx, const int64_t* slot_mapping,
+                             const int32_t* query_start, void* out, int64_t out_rs,
+                             int64_t T, int32_t off_s, int32_t ws, int32_t W,
+                             int dtype, int act, int residual) {
+  if (!valid_dtype(dtype) || T < 0 || H < 1 || N < 1 || ws < 1 || W < 1 ||
+      off_s < 0 || off_s + ws > D)
+    return ORC_ERR_ARGS;
+
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t slot = slot_mapping[t];
+    /* Reading: a negative slot is PAD -- no cache write and no output. */
+    if (slot < 0) continue;
+    const int64_t pos = positions[t];
+    const int32_t r = seq_idx[t];
+    const int64_t q = query_start[t];
+    if (r < 0 || r >= num_reqs) return ORC_ERR_REQ;
+
+    for (int32_t h = 0; h < H; ++h) {
+      for (int32_t j = 0; j < ws; ++j) {
+        const int64_t c = (int64_t)h * ws + j; /* head-major channel */
+        double acc = 0.0;
+        /* Reading: weight column k multiplies the input at position
+         * pos - (W-1) + k, so the last column meets the current token. */
+        for (int32_t k = 0; k < W; ++k) {
+          const int64_t lag = W - 1 - k;
+          const int64_t src = pos - lag;
+          double v;
+          if (src < 0) {
+            v = 0.0; /* Reading: taps before position 0 are zero. */
+          } else if (t - lag >= q) {
+            /* Tap inside this forward: the input row lag rows earlier. */
+            const int64_t row = t - lag;
+            if (row < 0 || row >= T) return ORC_ERR_ROW;
+            v = ld(x, dtype, row * x_rs + c);
+          } else {
+            /* Tap from before this forward: the paged cache snapshot. */
+            const int64_t lblk = src / N;
+            if (lblk >= max_blocks) return ORC_ERR_BT_COL;
+            const int64_t pblk = block_table[(int64_t)r * bt_rs + lblk];
+            if (pblk < 0 || pblk >= num_blocks) return ORC_ERR_BLOCK;
+            v = ld(cache_in, dtype,
+                   pblk * cs0 + (int64_t)h * cs1 + (src % N) * cs2 + off_s + j);
+          }
+          acc += ld(w, dtype, c * w_sc + (int64_t)k * w_sk) * v;
+        }
+        double y = activate(acc, act);
+        /* Reading: the residual is the raw input, added after the
+         * activation. */
+        if (residual) y += ld(x, dtype, t * x_rs + c);
+        st(out, dtype, t * out_rs + c, y);
+      }
+    }
+
+    /* Insert: this token's input goes to its flat slot, stream sub-range
+     * [off_s, off_s + ws) of every head. */
+    const int64_t blk = slot / N;
+    const int64_t off = slot % N;
+    if (blk >= num_blocks) return ORC_ERR_BLOCK;
+    for (int32_t h = 0; h < H; ++h)
+      for (int32_t j = 0; j < ws; ++j)
+        copy_elem(cache_out, blk * cs0 + (int64_t)h * cs1 + off * cs2 + off_s + j, x,
+                  t * x_rs + (int64_t)h * ws + j, dtype);
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* varlen causal conv1d with a state pool                              */
+/* ------------------------------------------------------------------ */
+
+int oracle_causal_conv1d_varlen_fwd(const void* x, int64_t x_sc, int64_t x_st,
+                                    const void* w, int64_t w_sc, int64_t w_sk,
+                                    const void* bias, const void* st_in, void* st_out,
+                                    int64_t num_slots, int64_t ss_slot, int64_t ss_c,
+                                    int64_t ss_k, const int32_t* qsl, int32_t batch,
+                                    const int32_t* cache_indices,
+                                    const uint8_t* has_init, void* out, int64_t o_sc,
+                                    int64_t o_st, int32_t dim, int64_t total_T,
+                                    int32_t W, int dtype, int act, int32_t pad_slot_id) {
+  if (!valid_dtype(dtype) || batch < 0 || dim < 0 || W < 1 || total_T < 0)
+    return ORC_ERR_ARGS;
+  const int32_t S = W - 1; /* state length */
+
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t slot = cache_indices ? cache_indices[b] : b;
+    if (slot == pad_slot_id) continue; /* padded sequence: untouched */
+    if (slot < 0 || slot >= num_slots) return ORC_ERR_SLOT;
+    const int64_t start = qsl[b];
+    const int64_t L = (int64_t)qsl[b + 1] - start;
+    if (start < 0 || L < 0 || start + L > total_T) return ORC_ERR_ROW;
+    /* Reading: without an initial state the history is zeros and the pool
+     * slot is not read. */
+    const int init = has_init ? (has_init[b] != 0) : 0;
+
+    for (int32_t c = 0; c < dim; ++c) {
+      /* Logical input u(i): x for i >= 0, the initial state (oldest first)
+       * for -S <= i < 0. */
+#define U_VAL(i)                                                                  \
+  ((i) >= 0 ? ld(x, dtype, (int64_t)c * x_sc + (start + (i)) * x_st)              \
+            : (init ? ld(st_in, dtype, slot * ss_slot + (int64_t)c * ss_c +       \
+                                           (int64_t)(S + (i)) * ss_k)             \
+                    : 0.0))
+      for (int64_t i = 0; i < L; ++i) {
+        double acc = bias ? ld(bias, dtype, c) : 0.0;
+        for (int32_t k = 0; k < W; ++k) {
+          const int64_t ui = i - S + k;
+          acc += ld(w, dtype, (int64_t)c * w_sc + (int64_t)k * w_sk) * U_VAL(ui);
+        }
+        st(out, dtype, (int64_t)c * o_sc + (start + i) * o_st, activate(acc, act));
+      }
+      /* Final state: the last S logical inputs, copied bit for bit. */
+      for (int32_t m = 0; m < S; ++m) {
+        const int64_t ui = L - S + m;
+        const int64_t di = slot * ss_slot + (int64_t)c * ss_c + (int64_t)m * ss_k;
+        if (ui >= 0)
+          copy_elem(st_out, di, x, (int64_t)c * x_sc + (start + ui) * x_st, dtype);
+        else if (init)
+          copy_elem(st_out, di, st_in,
+                    slot * ss_slot + (int64_t)c * ss_c + (int64_t)(S + ui) * ss_k, dtype);
+        else
+          store_zero(st_out, di, dtype);
+      }
+#undef U_VAL
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* single decode step against the state pool                           */
+/* ------------------------------------------------------------------ */
+
+int oracle_causal_conv1d_update(const void* x, int64_t x_rs, const void* st_in,
+                                void* st_out, int64_t num_slots, int64_t ss_slot,
+                                int64_t ss_c, int64_t ss_k, const void* w, int64_t w_sc,
+                                int64_t w_sk, const void* bias,
+                                const int32_t* conv_state_indices, void* out,
+                                int64_t out_rs, int32_t batch, int32_t dim, int32_t W,
+                                int dtype, int act, int32_t pad_slot_id) {
+  if (!valid_dtype(dtype) || batch < 0 || dim < 0 || W < 1) return ORC_ERR_ARGS;
+  const int32_t S = W - 1;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t slot = conv_state_indices ? conv_state_indices[b] : b;
+    if (slot == pad_slot_id) continue;
+    if (slot < 0 || slot >= num_slots) return ORC_ERR_SLOT;
+    for (int32_t c = 0; c < dim; ++c) {
+      /* Window: the stored state (oldest first) followed by the new input. */
+      double acc = bias ? ld(bias, dtype, c) : 0.0;
+      for (int32_t k = 0; k < W; ++k) {
+        const double v =
+            k < S ? ld(st_in, dtype, slot * ss_slot + (int64_t)c * ss_c + (int64_t)k * ss_k)
+                  : ld(x, dtype, (int64_t)b * x_rs + c);
+        acc += ld(w, dtype, (int64_t)c * w_sc + (int64_t)k * w_sk) * v;
+      }
+      st(out, dtype, (int64_t)b * out_rs + c, activate(acc, act));
+      /* The state moves one step: window entries 1 .. W-1. */
+      for (int32_t m = 0; m < S; ++m) {
+        const int64_t di = slot * ss_slot + (int64_t)c * ss_c + (int64_t)m * ss_k;
+        if (m + 1 < S)
+          copy_elem(st_out, di, st_in,
+                    slot * ss_slot + (int64_t)c * ss_c + (int64_t)(m + 1) * ss_k, dtype);
+        else
+          copy_elem(st_out, di, x, (int64_t)b * x_rs + c, dtype);
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* conditional gather of conv windows                                  */
+/* ------------------------------------------------------------------ */
+
+int oracle_gather_conv_window(const void* src, int64_t seq_len, int32_t conv_dim,
+                              int64_t src_ss, int64_t src_sc, const int32_t* abs_positions,
+                              int32_t real_count, int32_t max_count, void* out,
+                              int64_t out_ss, int32_t d_conv, int dtype) {
+  if (!valid_dtype(dtype) || seq_len < 1 || conv_dim < 0 || max_count < 0 || d_conv < 1)
+    return ORC_ERR_ARGS;
+  /* Reading: a count outside [0, max_count] is clamped into it. */
+  int64_t n = real_count;
+  if (n < 0) n = 0;
+  if (n > max_count) n = max_count;
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t p = abs_positions[i];
+    for (int32_t c = 0; c < conv_dim; ++c) {
+      for (int32_t k = 0; k < d_conv; ++k) {
+        /* Window [p - d_conv, p), each row index clamped into the sequence. */
+        int64_t row = p - d_conv + k;
+        if (row < 0) row = 0;
+        if (row > seq_len - 1) row = seq_len - 1;
+        copy_elem(out, i * out_ss + (int64_t)c * d_conv + k, src,
+                  row * src_ss + (int64_t)c * src_sc, dtype);
+      }
+    }
+  }
+  return ORC_OK;
+}
