@@ -1,0 +1,26 @@
+"""libsconv: paged depthwise causal short convolution for AMD MI355X (gfx950).
+
+The compute lives in hand-written HIP kernels behind a C ABI
+(``include/sconv.h``, built into ``libsconv.so``); this package is the thin
+torch binding over it.  Importing it loads the library and fails loudly if
+it has not been built.
+"""
+from ._lib import LibsconvError, load
+from .ops import (
+    causal_conv1d_update,
+    causal_conv1d_varlen_fwd,
+    gather_intermediate_conv_window,
+    sconv_fused_insert_conv,
+    sconv_seq_metadata,
+)
+
+load()
+
+__all__ = [
+    "LibsconvError",
+    "causal_conv1d_update",
+    "causal_conv1d_varlen_fwd",
+    "gather_intermediate_conv_window",
+    "sconv_fused_insert_conv",
+    "sconv_seq_metadata",
+]

@@ -1,0 +1,327 @@
+// fused_insert_conv.hip -- single-launch insert + depthwise causal conv over
+// a paged cache (one conv stream), for gfx950.
+//
+// Source: vLLM page "vllm.models.inkling.nvidia.ops.sconv", module
+// description and function fused_sconv.  Per row: the input row is copied
+// to the row's cache slot, and the W taps ending at the row's absolute
+// position are convolved; taps inside the current forward come from the
+// immutable input x, earlier taps from the paged cache via the block table.
+// The slot written in a call is never read in that call, so one launch
+// serves prefill, decode and speculative rows alike.
+//
+// Work decomposition (MI355X):
+//   * one wave64 owns a tile of BT consecutive rows x a slab of 64*VEC
+//     channels; each lane owns VEC consecutive channels (16 bytes: 8 bf16 or
+//     4 fp32), so every x / out row access of a wave is one contiguous
+//     coalesced segment and every cache access is 16 bytes per lane;
+//   * the row index is wave-uniform, so positions / slots / request ids and
+//     block-table entries arrive through scalar loads (SGPRs) and every
+//     PAD / same-forward / pre-forward decision is a uniform branch;
+//   * the W-1 previous input rows a tap needs stay in the lane's registers:
+//     rows inside the tile are the tile's own loads, rows before the tile
+//     (the halo, at most W-1) are loaded once per tile only when a row of
+//     the tile reads them, and the XCD-contiguous workgroup order puts the
+//     tile that loaded them last in the same L2;
+//   * fp32 FMA accumulation in VGPRs, SiLU via exp2 + reciprocal, bf16
+//     rounding by v_cvt_pk_bf16_f32 (round to nearest even);
+//   * the grid depends only on T and C, so the decode path replays under a
+//     hipGraph without any data-dependent shape.
+#include "sconv_device.h"
+#include "sconv_host.h"
+
+namespace sconv {
+
+struct FusedParams {
+  const void* x;
+  const void* w;
+  void* cache;
+  const int64_t* positions;
+  const int32_t* bt;
+  const int32_t* seq_idx;
+  const int64_t* slot;
+  const int32_t* qs;
+  void* out;
+  int64_t x_rs, w_sc, w_sk, cs0, cs1, cs2, bt_rs, out_rs, T;
+  int64_t num_tiles;
+  int32_t C, ws, off_s, N, log2N, num_slabs;
+  int32_t silu, residual, w_packed;
+};
+
+enum TapKind { kZero = 0, kXRow = 1, kCache = 2 };
+
+template <typename D, int VEC, int W, int BT>
+__global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParams p) {
+  using S = typename D::storage;
+  using P = Pack<D, VEC>;
+  const S* __restrict__ x = static_cast<const S*>(p.x);
+  const S* __restrict__ wt = static_cast<const S*>(p.w);
+  S* __restrict__ cache = static_cast<S*>(p.cache);
+  S* __restrict__ out = static_cast<S*>(p.out);
+  const int64_t* __restrict__ positions = p.positions;
+  const int64_t* __restrict__ slots = p.slot;
+  const int32_t* __restrict__ seq_idx = p.seq_idx;
+  const int32_t* __restrict__ qstart = p.qs;
+  const int32_t* __restrict__ btab = p.bt;
+
+  const int lane = threadIdx.x & 63;
+  const int waves_per_group = blockDim.x >> 6;
+  const int64_t wave = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * waves_per_group +
+                       uniform(threadIdx.x >> 6);
+  if (wave >= p.num_tiles * p.num_slabs) return;
+  const int64_t tile = wave / p.num_slabs;
+  const int slab = (int)(wave - tile * p.num_slabs);
+
+  // This lane's channels c0 .. c0+VEC-1 lie in one head (ws % VEC == 0).
+  const int c0 = (slab * 64 + lane) * VEC;
+  const bool on = c0 < p.C;
+  const int h = on ? c0 / p.ws : 0;
+  const int j = c0 - h * p.ws;
+  const int64_t lane_off = (int64_t)h * p.cs1 + p.off_s + j;
+
+  // Filter taps of this lane's channels, fp32.
+  float wk[W][VEC];
+  if (on) {
+    constexpr int kChunk = 16 / (int)sizeof(S);
+    constexpr int kN = VEC * W;
+    if constexpr (kN % kChunk == 0) {
+      if (p.w_packed) {
+#pragma unroll
+        for (int ch = 0; ch < kN / kChunk; ++ch) {
+          Pack<D, kChunk> pk;
+          pk.load(wt + (int64_t)c0 * W + ch * kChunk);
+          float f[kChunk];
+          pk.to_float(f);
+#pragma unroll
+          for (int q = 0; q < kChunk; ++q) wk[(ch * kChunk + q) % W][(ch * kChunk + q) / W] = f[q];
+        }
+      }
+    }
+    if (!(kN % kChunk == 0) || !p.w_packed) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int k = 0; k < W; ++k)
+          wk[k][e] = load_as_float<D>(wt + (int64_t)(c0 + e) * p.w_sc + (int64_t)k * p.w_sk);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+      for (int k = 0; k < W; ++k) wk[k][e] = 0.f;
+  }
+
+  // Per-row metadata (scalar) and the tile's input rows.
+  const int64_t t0 = tile * BT;
+  const bool full = t0 + BT <= p.T;
+  int64_t pos[BT], slot[BT];
+  int32_t req[BT], qs[BT];
+  P xr[BT];
+#pragma unroll
+  for (int i = 0; i < BT; ++i) {
+    const int64_t t = t0 + i;
+    if (full || t < p.T) {
+      pos[i] = positions[t];
+      slot[i] = slots[t];
+      req[i] = seq_idx[t];
+      qs[i] = qstart[t];
+      if (on) xr[i].load(x + t * p.x_rs + c0); else xr[i].zero();
+    } else {
+      pos[i] = 0;
+      slot[i] = -1;
+      req[i] = 0;
+      qs[i] = 0;
+      xr[i].zero();
+    }
+  }
+
+  // Halo: input rows t0-m (m = 1..W-1) that a row of this tile reads as a
+  // same-forward tap.
+  constexpr int kHalo = W > 1 ? W - 1 : 1;
+  P halo[kHalo];
+#pragma unroll
+  for (int m = 1; m <= kHalo; ++m) {
+    bool need = false;
+    if (m <= W - 1) {
+#pragma unroll
+      for (int i = 0; i < BT && i <= W - 1 - m; ++i)
+        need |= slot[i] >= 0 && pos[i] - (i + m) >= 0 && t0 - m >= (int64_t)qs[i] && t0 - m >= 0;
+    }
+    if (need && on) halo[m - 1].load(x + (t0 - m) * p.x_rs + c0); else halo[m - 1].zero();
+  }
+
+  const bool pow2 = p.log2N >= 0;
+#pragma unroll
+  for (int i = 0; i < BT; ++i) {
+    if (slot[i] < 0) continue;  // PAD (or past T): no output, no insert
+    const int64_t t = t0 + i;
+
+    // Where each earlier tap comes from; block ids of pre-forward taps.
+    int kind[kHalo];
+    int64_t cblk[kHalo], coff[kHalo];
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k) {
+      const int lag = W - 1 - k;
+      const int64_t src = pos[i] - lag;
+      kind[k] = src < 0 ? kZero : (t - lag >= (int64_t)qs[i] ? kXRow : kCache);
+      cblk[k] = 0;
+      coff[k] = 0;
+      if (kind[k] == kCache) {
+        const int64_t lb = pow2 ? (src >> p.log2N) : src / p.N;
+        coff[k] = src - lb * p.N;
+        cblk[k] = btab[(int64_t)req[i] * p.bt_rs + lb];
+      }
+    }
+
+    float tap[W][VEC];
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k) {
+      const int lag = W - 1 - k;
+      if (kind[k] == kCache) {
+        P pk;
+        if (on) pk.load(cache + cblk[k] * p.cs0 + coff[k] * p.cs2 + lane_off); else pk.zero();
+        pk.to_float(tap[k]);
+      } else if (kind[k] == kXRow) {
+        if (i >= lag) xr[i - lag].to_float(tap[k]);
+        else halo[lag - i - 1].to_float(tap[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) tap[k][e] = 0.f;
+      }
+    }
+    xr[i].to_float(tap[W - 1]);
+
+    float y[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < W; ++k) acc = __builtin_fmaf(wk[k][e], tap[k][e], acc);
+      if (p.silu) acc = silu(acc);
+      if (p.residual) acc += tap[W - 1][e];
+      y[e] = acc;
+    }
+    if (on) {
+      P o;
+      o.from_float(y);
+      o.store(out + t * p.out_rs + c0);
+      const int64_t s = slot[i];
+      const int64_t blk = pow2 ? (s >> p.log2N) : s / p.N;
+      xr[i].store(cache + blk * p.cs0 + (s - blk * p.N) * p.cs2 + lane_off);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+template <typename D, int VEC, int W, int BT>
+static void launch(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
+  hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT>), dim3(grid), dim3(threads), 0, s,
+                     p);
+}
+
+template <typename D, int VEC, int W>
+static void launch_bt(int bt, const FusedParams& p, uint32_t g, uint32_t th, hipStream_t s) {
+  switch (bt) {
+    case 16: launch<D, VEC, W, 16>(p, g, th, s); break;
+    case 4: launch<D, VEC, W, 4>(p, g, th, s); break;
+    default: launch<D, VEC, W, 1>(p, g, th, s); break;
+  }
+}
+
+template <typename D, int VEC>
+static void launch_w(int W, int bt, const FusedParams& p, uint32_t g, uint32_t th, hipStream_t s) {
+  switch (W) {
+    case 1: launch_bt<D, VEC, 1>(bt, p, g, th, s); break;
+    case 2: launch_bt<D, VEC, 2>(bt, p, g, th, s); break;
+    case 3: launch_bt<D, VEC, 3>(bt, p, g, th, s); break;
+    default: launch_bt<D, VEC, 4>(bt, p, g, th, s); break;
+  }
+}
+
+// Tokens per wave: the largest of {16, 4, 1} that still yields enough
+// waves to cover the chip (256 CUs x 4 SIMDs, two waves each).
+static int pick_bt(int64_t T, int64_t slabs) {
+  const int64_t kEnough = 2048;
+  if (cdiv(T, 16) * slabs >= kEnough) return 16;
+  if (cdiv(T, 4) * slabs >= kEnough) return 4;
+  return 1;
+}
+
+}  // namespace sconv
+
+extern "C" int sconv_fused_insert_conv(
+    const void* x, int64_t x_row_stride, const void* weight, int64_t w_stride_c,
+    int64_t w_stride_k, void* cache, int64_t num_blocks, int32_t H, int32_t N, int32_t D,
+    int64_t cs0, int64_t cs1, int64_t cs2, const int64_t* positions,
+    const int32_t* block_table, int64_t bt_row_stride, int32_t max_blocks,
+    const int32_t* seq_idx, const int64_t* slot_mapping, const int32_t* query_start, void* out,
+    int64_t out_row_stride, int64_t T, int32_t off_s, int32_t ws, int32_t W, int32_t dtype,
+    int32_t activation, int32_t use_residual, hipStream_t stream) {
+  using namespace sconv;
+  clear_error();
+  const char* fn = "sconv_fused_insert_conv";
+  if (T < 0) return fail(SCONV_ERR_INVALID, "%s: T < 0", fn);
+  if (!valid_dtype(dtype)) return fail(SCONV_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (!valid_act(activation))
+    return fail(SCONV_ERR_INVALID, "%s: unknown activation %d", fn, activation);
+  if (W < 1 || W > 4) return fail(SCONV_ERR_INVALID, "%s: W=%d outside [1, 4]", fn, W);
+  if (H < 1 || N < 1 || ws < 1 || D < 1 || num_blocks < 1 || max_blocks < 1)
+    return fail(SCONV_ERR_INVALID, "%s: H, N, ws, D, num_blocks and max_blocks must be >= 1", fn);
+  if (off_s < 0 || (int64_t)off_s + ws > D)
+    return fail(SCONV_ERR_INVALID, "%s: stream range [%d, %d) outside D=%d", fn, off_s,
+                off_s + ws, D);
+  const int64_t C = (int64_t)H * ws;
+  if (C > INT32_MAX / 2) return fail(SCONV_ERR_UNSUPPORTED, "%s: C too large", fn);
+  if (x_row_stride < C || out_row_stride < C)
+    return fail(SCONV_ERR_INVALID, "%s: row strides must be >= C=%lld", fn, (long long)C);
+  if (cs2 < D || cs1 < 1 || cs0 < 1 || bt_row_stride < max_blocks || w_stride_c < 1 ||
+      w_stride_k < 1)
+    return fail(SCONV_ERR_INVALID, "%s: cache / block-table / weight strides too small", fn);
+  if (T == 0) return SCONV_OK;
+  if (!x || !weight || !cache || !positions || !block_table || !seq_idx || !slot_mapping ||
+      !query_start || !out)
+    return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
+  const int64_t es = elem_size(dtype);
+  const int64_t x_bytes = ((T - 1) * x_row_stride + C) * es;
+  const int64_t o_bytes = ((T - 1) * out_row_stride + C) * es;
+  const int64_t c_bytes = ((num_blocks - 1) * cs0 + (H - 1) * cs1 + (N - 1) * cs2 + D) * es;
+  if (overlap(out, o_bytes, x, x_bytes) || overlap(out, o_bytes, cache, c_bytes))
+    return fail(SCONV_ERR_INVALID, "%s: out overlaps x or the cache", fn);
+
+  const int vec16 = (int)(16 / es);
+  const bool vec = C % vec16 == 0 && ws % vec16 == 0 && off_s % vec16 == 0 &&
+                   x_row_stride % vec16 == 0 && out_row_stride % vec16 == 0 &&
+                   cs0 % vec16 == 0 && cs1 % vec16 == 0 && cs2 % vec16 == 0 && aligned16(x) &&
+                   aligned16(out) && aligned16(cache);
+  const int VEC = vec ? vec16 : 1;
+
+  FusedParams p;
+  p.x = x; p.w = weight; p.cache = cache; p.positions = positions; p.bt = block_table;
+  p.seq_idx = seq_idx; p.slot = slot_mapping; p.qs = query_start; p.out = out;
+  p.x_rs = x_row_stride; p.w_sc = w_stride_c; p.w_sk = w_stride_k;
+  p.cs0 = cs0; p.cs1 = cs1; p.cs2 = cs2; p.bt_rs = bt_row_stride; p.out_rs = out_row_stride;
+  p.T = T;
+  p.C = (int32_t)C; p.ws = ws; p.off_s = off_s; p.N = N;
+  p.log2N = (N & (N - 1)) == 0 ? __builtin_ctz((unsigned)N) : -1;
+  p.num_slabs = (int32_t)cdiv(C, 64 * VEC);
+  const int bt = pick_bt(T, p.num_slabs);
+  p.num_tiles = cdiv(T, bt);
+  p.silu = activation == SCONV_ACT_SILU;
+  p.residual = use_residual != 0;
+  p.w_packed = w_stride_c == W && w_stride_k == 1 && aligned16(weight) &&
+               ((int64_t)VEC * W * es) % 16 == 0;
+
+  const int64_t waves = p.num_tiles * p.num_slabs;
+  const uint32_t threads = waves >= 4096 ? 256 : 64;
+  const int64_t grid = cdiv(waves, threads / 64);
+  if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
+
+  if (dtype == SCONV_BF16) {
+    if (VEC == 8) launch_w<Bf16, 8>(W, bt, p, (uint32_t)grid, threads, stream);
+    else launch_w<Bf16, 1>(W, bt, p, (uint32_t)grid, threads, stream);
+  } else {
+    if (VEC == 4) launch_w<F32, 4>(W, bt, p, (uint32_t)grid, threads, stream);
+    else launch_w<F32, 1>(W, bt, p, (uint32_t)grid, threads, stream);
+  }
+  return check_launch(fn);
+}

@@ -1,0 +1,135 @@
+// gather_window.hip -- conditional gather of each slot's length-d_conv input
+// window, written transposed, with the live slot count read on the device.
+//
+// Source: Megatron-core page "core.ssm.ops.intermediate_extraction", module
+// description and scatter_intermediate_conv: the grid is sized for the
+// largest slot count when a graph is captured, each workgroup reads the real
+// count from a fixed device address when it runs, and workgroups of dead
+// slots leave before touching memory.  The window [pos - d_conv, pos) is
+// clamped into the sequence and stored as (conv_dim, d_conv) per slot.
+//
+// Each lane owns VEC channels of one slot: it loads the d_conv source rows
+// as 16-byte vectors and writes its VEC*d_conv output elements, which are
+// contiguous in the transposed layout, as 16-byte chunks.
+#include "sconv_device.h"
+#include "sconv_host.h"
+
+namespace sconv {
+
+struct GatherParams {
+  const void* src;
+  const int32_t* pos;
+  const int32_t* real_count;
+  void* out;
+  int64_t seq_len, src_ss, src_sc, out_ss;
+  int32_t conv_dim, max_count, cblocks, out_chunked;
+};
+
+template <typename D, int VEC, int DC>
+__global__ __launch_bounds__(256) void gather_window_kernel(const GatherParams p) {
+  using S = typename D::storage;
+  const S* __restrict__ src = static_cast<const S*>(p.src);
+  S* __restrict__ out = static_cast<S*>(p.out);
+  const int slot = (int)(blockIdx.x / (uint32_t)p.cblocks);
+  const int cb = (int)(blockIdx.x - (uint32_t)slot * p.cblocks);
+  int n = *p.real_count;
+  n = n < 0 ? 0 : (n > p.max_count ? p.max_count : n);
+  if (slot >= n) return;  // dead slot: no traffic
+  const int c0 = (cb * (int)blockDim.x + (int)threadIdx.x) * VEC;
+  if (c0 >= p.conv_dim) return;
+  const int64_t pend = p.pos[slot];
+
+  struct OutElems { S e[VEC * DC]; } oe;  // [c][k], k fastest
+#pragma unroll
+  for (int k = 0; k < DC; ++k) {
+    int64_t row = pend - DC + k;
+    row = row < 0 ? 0 : (row > p.seq_len - 1 ? p.seq_len - 1 : row);
+    Pack<D, VEC> pk;
+    if constexpr (VEC > 1) {
+      pk.load(src + row * p.src_ss + c0);
+    } else {
+      pk.raw = __builtin_bit_cast(typename Pack<D, 1>::raw_t, src[row * p.src_ss + (int64_t)c0 * p.src_sc]);
+    }
+    typename Pack<D, VEC>::Elems v = __builtin_bit_cast(typename Pack<D, VEC>::Elems, pk.raw);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) oe.e[e * DC + k] = v.e[e];
+  }
+
+  S* dst = out + (int64_t)slot * p.out_ss + (int64_t)c0 * DC;
+  constexpr int kChunkE = 16 / (int)sizeof(S);
+  constexpr bool kChunked = (VEC * DC) % kChunkE == 0;
+  if constexpr (kChunked) {
+    if (p.out_chunked) {
+#pragma unroll
+      for (int ch = 0; ch < VEC * DC / kChunkE; ++ch) {
+        typename Pack<D, kChunkE>::Elems v;
+#pragma unroll
+        for (int q = 0; q < kChunkE; ++q) v.e[q] = oe.e[ch * kChunkE + q];
+        Pack<D, kChunkE> pk;
+        pk.raw = __builtin_bit_cast(typename Pack<D, kChunkE>::raw_t, v);
+        pk.store(dst + ch * kChunkE);
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < VEC * DC; ++q) dst[q] = oe.e[q];
+}
+
+template <typename D, int VEC>
+static void launch_gather(int dc, const GatherParams& p, uint32_t g, uint32_t th, hipStream_t s) {
+  switch (dc) {
+    case 1: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 1>), dim3(g), dim3(th), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 2>), dim3(g), dim3(th), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 3>), dim3(g), dim3(th), 0, s, p); break;
+    default: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 4>), dim3(g), dim3(th), 0, s, p); break;
+  }
+}
+
+}  // namespace sconv
+
+extern "C" int gather_intermediate_conv_window(const void* src, int64_t seq_len,
+                                               int32_t conv_dim, int64_t src_stride_s,
+                                               int64_t src_stride_c,
+                                               const int32_t* abs_positions,
+                                               const int32_t* real_count_dev, int32_t max_count,
+                                               void* out, int64_t out_slot_stride,
+                                               int32_t d_conv, int32_t dtype,
+                                               hipStream_t stream) {
+  using namespace sconv;
+  clear_error();
+  const char* fn = "gather_intermediate_conv_window";
+  if (!valid_dtype(dtype)) return fail(SCONV_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (seq_len < 1) return fail(SCONV_ERR_INVALID, "%s: seq_len < 1", fn);
+  if (conv_dim < 0 || max_count < 0)
+    return fail(SCONV_ERR_INVALID, "%s: conv_dim and max_count must be >= 0", fn);
+  if (d_conv < 1 || d_conv > 4)
+    return fail(SCONV_ERR_UNSUPPORTED, "%s: d_conv=%d outside [1, 4]", fn, d_conv);
+  if (conv_dim == 0 || max_count == 0) return SCONV_OK;
+  if (!src || !abs_positions || !real_count_dev || !out)
+    return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
+  if (src_stride_s < 1 || src_stride_c < 1 || out_slot_stride < (int64_t)conv_dim * d_conv)
+    return fail(SCONV_ERR_INVALID, "%s: strides too small", fn);
+  const int64_t es = elem_size(dtype);
+  const int vec16 = (int)(16 / es);
+  const bool vec = src_stride_c == 1 && conv_dim % vec16 == 0 && src_stride_s % vec16 == 0 &&
+                   aligned16(src);
+  const int VEC = vec ? vec16 : 1;
+  GatherParams p;
+  p.src = src; p.pos = abs_positions; p.real_count = real_count_dev; p.out = out;
+  p.seq_len = seq_len; p.src_ss = src_stride_s; p.src_sc = src_stride_c;
+  p.out_ss = out_slot_stride; p.conv_dim = conv_dim; p.max_count = max_count;
+  p.out_chunked = aligned16(out) && out_slot_stride % vec16 == 0 && vec;
+  const uint32_t th = (int64_t)conv_dim >= 256 * VEC ? 256 : 64;
+  p.cblocks = (int32_t)cdiv(conv_dim, (int64_t)th * VEC);
+  const int64_t grid = (int64_t)max_count * p.cblocks;
+  if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  if (dtype == SCONV_BF16) {
+    if (vec) launch_gather<Bf16, 8>(d_conv, p, (uint32_t)grid, th, stream);
+    else launch_gather<Bf16, 1>(d_conv, p, (uint32_t)grid, th, stream);
+  } else {
+    if (vec) launch_gather<F32, 4>(d_conv, p, (uint32_t)grid, th, stream);
+    else launch_gather<F32, 1>(d_conv, p, (uint32_t)grid, th, stream);
+  }
+  return check_launch(fn);
+}

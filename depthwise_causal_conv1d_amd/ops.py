@@ -1,0 +1,231 @@
+"""Python binding of libsconv: torch tensors in, one C-ABI call out.
+
+Each function only checks what the C ABI cannot see (tensor dtype, device,
+dimensionality), turns tensors into pointers, element strides and the
+current HIP stream, and calls the library.  All computation happens in the
+HIP kernels; there is no CPU path.  Argument names follow the source pages.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"element type must be float32 or bfloat16, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _act(activation) -> int:
+    if activation in (None, False, "none"):
+        return _lib.ACT_NONE
+    if activation in (True, "silu", "swish"):
+        return _lib.ACT_SILU
+    raise ValueError(f"unknown activation {activation!r}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libsconv tensors must live on the GPU")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _vec(t: torch.Tensor, dtype: torch.dtype, name: str, min_len: int = 0):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 1 or (t.numel() > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous 1-D tensor")
+    if t.numel() < min_len:
+        raise ValueError(f"{name} has {t.numel()} entries, needs {min_len}")
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def sconv_seq_metadata(query_start_loc: torch.Tensor, num_reqs: int, num_actual_tokens: int,
+                       seq_idx_out: torch.Tensor, query_start_out: torch.Tensor,
+                       num_padded_tokens: Optional[int] = None) -> None:
+    """Fill the static per-token seq_idx / query_start buffers in one launch."""
+    if num_padded_tokens is None:
+        num_padded_tokens = num_actual_tokens
+    _dev(query_start_loc, seq_idx_out, query_start_out)
+    _vec(query_start_loc, torch.int32, "query_start_loc", num_reqs + 1 if num_actual_tokens else 0)
+    _vec(seq_idx_out, torch.int32, "seq_idx_out")
+    _vec(query_start_out, torch.int32, "query_start_out")
+    rc = _lib.load().sconv_seq_metadata(
+        _ptr(query_start_loc), int(num_reqs), int(num_actual_tokens), int(num_padded_tokens),
+        _ptr(seq_idx_out), seq_idx_out.numel(), _ptr(query_start_out), query_start_out.numel(),
+        _stream(seq_idx_out))
+    _lib.check(rc, "sconv_seq_metadata")
+
+
+def sconv_fused_insert_conv(x: torch.Tensor, weight: torch.Tensor, cache: torch.Tensor,
+                            positions: torch.Tensor, block_table: torch.Tensor,
+                            seq_idx: torch.Tensor, slot_mapping: torch.Tensor,
+                            query_start: torch.Tensor, off_s: int, ws: int, block_size: int,
+                            activation: Optional[str] = None, use_residual: bool = True,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Single-launch insert + depthwise causal conv1d over the paged cache.
+
+    x [T, H*ws], weight [H*ws, W], cache [num_blocks, H, N, D] (modified),
+    positions int64 [T], block_table int32 [num_reqs, max_blocks],
+    seq_idx / query_start int32 [T], slot_mapping int64 [T] (-1 = PAD).
+    Returns ``out`` (new [T, H*ws] tensor unless given; PAD rows untouched).
+    """
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if x.dim() != 2 or weight.dim() != 2 or cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("x [T, C], weight [C, W], cache [nb, H, N, D], block_table [R, M]")
+    if T == 0:
+        return out
+    _dev(x, weight, cache, positions, block_table, seq_idx, slot_mapping, query_start, out)
+    dt = _dtype(x)
+    if weight.dtype != x.dtype or cache.dtype != x.dtype or out.dtype != x.dtype:
+        raise TypeError("x, weight, cache and out must share one element type")
+    if x.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("x and out need contiguous channels")
+    if cache.stride(3) != 1:
+        raise ValueError("cache D-dim must be contiguous")
+    nb, H, N, D = cache.shape
+    if N != block_size:
+        raise ValueError(f"block_size {block_size} != cache block dim {N}")
+    if x.shape[1] != H * ws or weight.shape[0] != H * ws or out.shape != x.shape:
+        raise ValueError("x / weight / out channel dim must be H*ws")
+    if block_table.dtype != torch.int32:
+        raise TypeError("block_table must be int32")
+    _vec(positions, torch.int64, "positions", T)
+    _vec(slot_mapping, torch.int64, "slot_mapping", T)
+    _vec(seq_idx, torch.int32, "seq_idx", T)
+    _vec(query_start, torch.int32, "query_start", T)
+    rc = _lib.load().sconv_fused_insert_conv(
+        _ptr(x), x.stride(0), _ptr(weight), weight.stride(0), weight.stride(1),
+        _ptr(cache), nb, H, N, D, cache.stride(0), cache.stride(1), cache.stride(2),
+        _ptr(positions), _ptr(block_table), block_table.stride(0), block_table.shape[1],
+        _ptr(seq_idx), _ptr(slot_mapping), _ptr(query_start), _ptr(out), out.stride(0),
+        T, int(off_s), int(ws), weight.shape[1], dt, _act(activation), int(bool(use_residual)),
+        _stream(x))
+    _lib.check(rc, "sconv_fused_insert_conv")
+    return out
+
+
+def causal_conv1d_varlen_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                             conv_states: torch.Tensor, query_start_loc: torch.Tensor,
+                             cache_indices: Optional[torch.Tensor],
+                             has_initial_state: Optional[torch.Tensor], silu_activation: bool,
+                             pad_slot_id: int = -1, out: Optional[torch.Tensor] = None
+                             ) -> torch.Tensor:
+    """Varlen causal conv1d over channel-major x [dim, total_T].
+
+    conv_states [num_slots, dim, W-1] is updated in place.  With ``out`` None
+    the result overwrites x (in place, as the source op does) and x is
+    returned.
+    """
+    if out is None:
+        out = x
+    if x.dim() != 2 or weight.dim() != 2 or conv_states.dim() != 3:
+        raise ValueError("x [dim, total_T], weight [dim, W], conv_states [slots, dim, W-1]")
+    dim, total_T = x.shape
+    W = weight.shape[1]
+    batch = query_start_loc.numel() - 1
+    _dev(x, weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state, out)
+    dt = _dtype(x)
+    for t in (weight, conv_states, out) + ((bias,) if bias is not None else ()):
+        if t.dtype != x.dtype:
+            raise TypeError("x, weight, bias, conv_states and out must share one element type")
+    if weight.shape[0] != dim or conv_states.shape[1] != dim or conv_states.shape[2] != W - 1:
+        raise ValueError("weight / conv_states shapes do not match x")
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    if bias is not None:
+        _vec(bias, x.dtype, "bias", dim)
+    _vec(query_start_loc, torch.int32, "query_start_loc")
+    if cache_indices is not None:
+        _vec(cache_indices, torch.int32, "cache_indices", batch)
+    hi = None
+    if has_initial_state is not None:
+        hi = has_initial_state
+        if hi.dtype == torch.bool:
+            hi = hi.view(torch.uint8)
+        _vec(hi, torch.uint8, "has_initial_state", batch)
+    rc = _lib.load().causal_conv1d_varlen_fwd(
+        _ptr(x), x.stride(0), x.stride(1), _ptr(weight), weight.stride(0), weight.stride(1),
+        _ptr(bias), _ptr(conv_states), conv_states.shape[0], conv_states.stride(0),
+        conv_states.stride(1), conv_states.stride(2), _ptr(query_start_loc), batch,
+        _ptr(cache_indices), _ptr(hi), _ptr(out), out.stride(0), out.stride(1), dim, total_T,
+        W, dt, _lib.ACT_SILU if silu_activation else _lib.ACT_NONE, int(pad_slot_id), _stream(x))
+    _lib.check(rc, "causal_conv1d_varlen_fwd")
+    return out
+
+
+def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torch.Tensor,
+                         bias: Optional[torch.Tensor], silu_activation: bool,
+                         cache_seqlens: Optional[torch.Tensor] = None,
+                         conv_state_indices: Optional[torch.Tensor] = None,
+                         pad_slot_id: int = -1, out: Optional[torch.Tensor] = None
+                         ) -> torch.Tensor:
+    """One decode step: x [batch, dim]; conv_state [num_slots, dim, W-1]
+    updated in place.  With ``out`` None the result overwrites x."""
+    if out is None:
+        out = x
+    if x.dim() != 2 or weight.dim() != 2 or conv_state.dim() != 3:
+        raise ValueError("x [batch, dim], weight [dim, W], conv_state [slots, dim, W-1]")
+    batch, dim = x.shape
+    W = weight.shape[1]
+    _dev(x, conv_state, weight, bias, conv_state_indices, out)
+    dt = _dtype(x)
+    for t in (weight, conv_state, out) + ((bias,) if bias is not None else ()):
+        if t.dtype != x.dtype:
+            raise TypeError("x, weight, bias, conv_state and out must share one element type")
+    if x.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("x and out need contiguous channels")
+    if weight.shape[0] != dim or conv_state.shape[1] != dim or conv_state.shape[2] != W - 1:
+        raise ValueError("weight / conv_state shapes do not match x")
+    if bias is not None:
+        _vec(bias, x.dtype, "bias", dim)
+    if conv_state_indices is not None:
+        _vec(conv_state_indices, torch.int32, "conv_state_indices", batch)
+    rc = _lib.load().causal_conv1d_update(
+        _ptr(x), x.stride(0), _ptr(conv_state), conv_state.shape[0], conv_state.stride(0),
+        conv_state.stride(1), conv_state.stride(2), _ptr(weight), weight.stride(0),
+        weight.stride(1), _ptr(bias), _ptr(cache_seqlens), _ptr(conv_state_indices), _ptr(out),
+        out.stride(0), batch, dim, W, dt, _lib.ACT_SILU if silu_activation else _lib.ACT_NONE,
+        int(pad_slot_id), _stream(x))
+    _lib.check(rc, "causal_conv1d_update")
+    return out
+
+
+def gather_intermediate_conv_window(src: torch.Tensor, abs_positions: torch.Tensor,
+                                    real_count_gpu: torch.Tensor, out: torch.Tensor,
+                                    d_conv: int) -> None:
+    """Gather length-d_conv windows of src[0] ending before abs_positions
+    into out [max_count, conv_dim, d_conv] for the first real_count slots
+    (count read on the device)."""
+    if src.dim() != 3 or out.dim() != 3:
+        raise ValueError("src [batch, seq_len, conv_dim], out [max_count, conv_dim, d_conv]")
+    _dev(src, abs_positions, real_count_gpu, out)
+    dt = _dtype(src)
+    if out.dtype != src.dtype:
+        raise TypeError("src and out must share one element type")
+    max_count, conv_dim, dc = out.shape
+    if dc != d_conv or conv_dim != src.shape[2]:
+        raise ValueError("out must be [max_count, conv_dim, d_conv]")
+    if out.stride(2) != 1 or out.stride(1) != d_conv:
+        raise ValueError("out slots must be dense (conv_dim, d_conv)")
+    _vec(abs_positions, torch.int32, "abs_positions", max_count)
+    _vec(real_count_gpu, torch.int32, "real_count_gpu", 1)
+    rc = _lib.load().gather_intermediate_conv_window(
+        _ptr(src), src.shape[1], conv_dim, src.stride(1), src.stride(2), _ptr(abs_positions),
+        _ptr(real_count_gpu), max_count, _ptr(out), out.stride(0), d_conv, dt, _stream(src))
+    _lib.check(rc, "gather_intermediate_conv_window")

@@ -1,0 +1,238 @@
+/*
+ * sconv.h -- C ABI of libsconv: paged depthwise causal short convolution
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every function returns an int status: SCONV_OK (0) or one of the
+ *   SCONV_ERR_* codes below.  On error, sconv_last_error() returns a
+ *   thread-local message; nothing is launched.
+ * - Every buffer is a caller-owned DEVICE pointer (hipMalloc / torch).  The
+ *   library allocates nothing, never synchronizes and never reads device data
+ *   on the host: each call enqueues one kernel on `stream` (NULL = the null
+ *   stream) and returns.  This makes every call capturable in a hipGraph;
+ *   grids depend on host scalars only.
+ * - Strides are in ELEMENTS.  Only host scalars are validated.  Properties of
+ *   device data (index ranges, monotone offsets, distinct slots) are the
+ *   caller's contract and are stated per function; breaking them is
+ *   undefined behaviour.
+ * - Floating tensors of one call share one element type (sconv_dtype_t):
+ *   x, weight, bias, cache / state pool and out.  Arithmetic is fp32.
+ * - SCONV_ERR_HIP reports a launch error taken from hipGetLastError().
+ */
+#ifndef SCONV_H
+#define SCONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque HIP stream handle (identical to the one in hip_runtime_api.h). */
+typedef struct ihipStream_t* hipStream_t;
+
+enum {
+  SCONV_OK = 0,
+  SCONV_ERR_INVALID = 1,     /* bad host scalar, shape, stride or pointer */
+  SCONV_ERR_UNSUPPORTED = 2, /* valid request this build does not cover   */
+  SCONV_ERR_HIP = 3          /* the HIP runtime reported a launch error   */
+};
+
+typedef enum { SCONV_F32 = 0, SCONV_BF16 = 1 } sconv_dtype_t;
+typedef enum { SCONV_ACT_NONE = 0, SCONV_ACT_SILU = 1 } sconv_act_t;
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* sconv_last_error(void);
+
+/* Library version string. */
+const char* sconv_version(void);
+
+/*
+ * sconv_seq_metadata -- per-token request index and request start row.
+ *
+ * Source: vLLM page "vllm.models.inkling.nvidia.ops.sconv", function
+ * sconv_seq_metadata (docstring and wrapper source): one launch replaces the
+ * search-and-gather chain that builds the static per-token buffers.
+ *
+ * For rows t < num_actual_tokens:
+ *     seq_idx_out[t]     = the request r whose rows [qsl[r], qsl[r+1]) hold t
+ *                          (empty requests never match; rows at or beyond
+ *                          qsl[num_reqs] get num_reqs - 1)
+ *     query_start_out[t] = qsl[r]
+ * For rows num_actual_tokens <= t < num_padded_tokens both are 0 (such rows
+ * must carry slot_mapping == -1 in sconv_fused_insert_conv).
+ *
+ *   query_start_loc  int32 [num_reqs + 1], non-decreasing, qsl[0] == 0 (device)
+ *   seq_idx_out      int32 [seq_idx_len]     (device, written)
+ *   query_start_out  int32 [query_start_len] (device, written)
+ *
+ * Errors (SCONV_ERR_INVALID): num_padded_tokens < num_actual_tokens, either
+ * output shorter than num_padded_tokens, num_actual_tokens < 0, or
+ * num_reqs < 1 while num_actual_tokens > 0.  num_padded_tokens == 0 is a
+ * successful no-op.
+ */
+int sconv_seq_metadata(const int32_t* query_start_loc, int32_t num_reqs,
+                       int64_t num_actual_tokens, int64_t num_padded_tokens,
+                       int32_t* seq_idx_out, int64_t seq_idx_len,
+                       int32_t* query_start_out, int64_t query_start_len,
+                       hipStream_t stream);
+
+/*
+ * sconv_fused_insert_conv -- single-launch insert + depthwise causal conv
+ * over a paged cache, for one conv stream.
+ *
+ * Source: vLLM page "vllm.models.inkling.nvidia.ops.sconv", module
+ * description and function fused_sconv (signature, docstring, wrapper
+ * source).
+ *
+ * Layout:
+ *   x          [T, C] row stride x_row_stride, channels contiguous,
+ *              C = H * ws, channel c = h*ws + j (head-major)
+ *   weight     [C, W] strides (w_stride_c, w_stride_k); 1 <= W <= 4
+ *   cache      [num_blocks, H, N, D] strides (cs0, cs1, cs2, 1); this stream
+ *              owns columns [off_s, off_s + ws) of every head
+ *   positions  int64 [T]  absolute position of each row
+ *   block_table int32 [num_reqs, max_blocks] row stride bt_row_stride
+ *   seq_idx    int32 [T]  request of each row     (sconv_seq_metadata)
+ *   slot_mapping int64 [T] flat cache slot, < 0 = PAD
+ *   query_start int32 [T] first row of the row's request
+ *   out        [T, C] row stride out_row_stride (written, same dtype as x)
+ *
+ * For each row t with slot_mapping[t] >= 0, channel c, tap k in [0, W):
+ *   lag = W-1-k, src = positions[t] - lag, and the tap value is
+ *     0                                   if src < 0,
+ *     x[t - lag, c]                       if t - lag >= query_start[t],
+ *     cache[bt[seq_idx[t], src / N], h, src % N, off_s + j]   otherwise;
+ *   out[t, c] = act(sum_k weight[c, k] * tap_k) (+ x[t, c] if use_residual)
+ *   and x[t, :] is copied bit for bit to cache[slot / N, h, slot % N,
+ *   off_s + j].  PAD rows produce no output (out row untouched) and no
+ *   write, but their input still serves as a tap for later rows of their
+ *   request.
+ *
+ * Device-data contract: rows of a request are contiguous with consecutive
+ * positions; every block-table entry that is read lies in [0, num_blocks);
+ * non-PAD slots are distinct and none of them is read as a pre-forward tap
+ * in the same call (the cache is read and written in one launch).
+ *
+ * Host errors (SCONV_ERR_INVALID): T < 0, H, N, ws < 1, off_s < 0,
+ * off_s + ws > D, W outside [1, 4], strides smaller than the row they span,
+ * unknown dtype or activation, NULL pointer with T > 0, out overlapping x or
+ * cache.  T == 0 is a successful no-op.
+ */
+int sconv_fused_insert_conv(const void* x, int64_t x_row_stride,
+                            const void* weight, int64_t w_stride_c, int64_t w_stride_k,
+                            void* cache, int64_t num_blocks, int32_t H, int32_t N,
+                            int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
+                            const int64_t* positions, const int32_t* block_table,
+                            int64_t bt_row_stride, int32_t max_blocks,
+                            const int32_t* seq_idx, const int64_t* slot_mapping,
+                            const int32_t* query_start, void* out,
+                            int64_t out_row_stride, int64_t T, int32_t off_s,
+                            int32_t ws, int32_t W, int32_t dtype, int32_t activation,
+                            int32_t use_residual, hipStream_t stream);
+
+/*
+ * causal_conv1d_varlen_fwd -- causal depthwise conv over packed
+ * variable-length sequences, with a slot-indexed state pool.
+ *
+ * Source: leeroopedia page "Implementation:Sgl project Sglang Mamba Ops",
+ * causal_conv1d_fwd (Signature, I/O Contract, Usage Examples).
+ *
+ *   x        [dim, total_T] strides (x_stride_c, x_stride_t) (device)
+ *   weight   [dim, W] strides (w_stride_c, w_stride_k); bias [dim] or NULL
+ *   conv_states [num_slots, dim, W-1] strides (st_stride_slot, st_stride_c,
+ *            st_stride_k), oldest input first (read and written)
+ *   query_start_loc int32 [batch+1] sequence b = tokens [qsl[b], qsl[b+1])
+ *   cache_indices   int32 [batch] state slot of each sequence (NULL: b);
+ *            a sequence whose slot equals pad_slot_id is skipped entirely
+ *   has_initial_state uint8 [batch] (NULL: all 0); 0 = history is zeros and
+ *            the slot is not read
+ *   out      [dim, total_T] strides (out_stride_c, out_stride_t); may be x
+ *            itself (in-place), otherwise must not overlap it
+ *
+ * For each non-PAD sequence, with u the state (oldest first) followed by the
+ * sequence's inputs:  out[c, t] = act(bias[c] + sum_k weight[c, k] *
+ * u[t - (W-1) + k]), and the slot receives the last W-1 entries of u (a bit
+ * copy).
+ *
+ * Device-data contract: offsets non-decreasing within [0, total_T]; non-PAD
+ * slots distinct and in [0, num_slots).
+ *
+ * Host errors (SCONV_ERR_INVALID): batch, dim, total_T < 0, W outside
+ * [1, 4], NULL required pointer, unknown dtype or activation, partial overlap
+ * of out and x.  batch == 0 or dim == 0 is a successful no-op.
+ */
+int causal_conv1d_varlen_fwd(const void* x, int64_t x_stride_c, int64_t x_stride_t,
+                             const void* weight, int64_t w_stride_c, int64_t w_stride_k,
+                             const void* bias, void* conv_states, int64_t num_slots,
+                             int64_t st_stride_slot, int64_t st_stride_c,
+                             int64_t st_stride_k, const int32_t* query_start_loc,
+                             int32_t batch, const int32_t* cache_indices,
+                             const uint8_t* has_initial_state, void* out,
+                             int64_t out_stride_c, int64_t out_stride_t, int32_t dim,
+                             int64_t total_T, int32_t W, int32_t dtype,
+                             int32_t activation, int32_t pad_slot_id, hipStream_t stream);
+
+/*
+ * causal_conv1d_update -- one decode step against the state pool.
+ *
+ * Source: leeroopedia page "Implementation:Sgl project Sglang Mamba Ops",
+ * causal_conv1d_update (Signature, I/O Contract).
+ *
+ *   x        [batch, dim] row stride x_stride_b, channels contiguous
+ *   conv_states as in causal_conv1d_varlen_fwd (read and written)
+ *   cache_seqlens: must be NULL (circular-buffer states are not part of
+ *            this build; non-NULL returns SCONV_ERR_UNSUPPORTED)
+ *   conv_state_indices int32 [batch] (NULL: b); pad_slot_id skips a row
+ *   out      [batch, dim] row stride out_stride_b; may be x itself
+ *
+ * window = state[slot, c, 0..W-2] followed by x[b, c];
+ * out[b, c] = act(bias[c] + sum_k weight[c, k] * window[k]);
+ * state[slot, c, :] = window[1..W-1]  (bit copies).
+ *
+ * Host errors (SCONV_ERR_INVALID): batch, dim < 0, W outside [1, 4], NULL
+ * required pointer, unknown dtype or activation, partial overlap of out and x.
+ */
+int causal_conv1d_update(const void* x, int64_t x_stride_b, void* conv_states,
+                         int64_t num_slots, int64_t st_stride_slot, int64_t st_stride_c,
+                         int64_t st_stride_k, const void* weight, int64_t w_stride_c,
+                         int64_t w_stride_k, const void* bias,
+                         const int32_t* cache_seqlens, const int32_t* conv_state_indices,
+                         void* out, int64_t out_stride_b, int32_t batch, int32_t dim,
+                         int32_t W, int32_t dtype, int32_t activation,
+                         int32_t pad_slot_id, hipStream_t stream);
+
+/*
+ * gather_intermediate_conv_window -- conditional gather of the length-d_conv
+ * input window before each slot's position, written transposed.
+ *
+ * Source: Megatron-core page "core.ssm.ops.intermediate_extraction", module
+ * description, _scatter_intermediate_conv_kernel and scatter_intermediate_conv.
+ *
+ *   src            [seq_len, conv_dim] strides (src_stride_s, src_stride_c):
+ *                  batch row 0 of the pre-conv input (device)
+ *   abs_positions  int32 [max_count] window end of each slot (device)
+ *   real_count_dev int32 [1] number of live slots, read ON THE DEVICE when
+ *                  the kernel runs (clamped into [0, max_count]); the grid is
+ *                  sized by max_count, so the call is graph-replay safe
+ *   out            [max_count, conv_dim, d_conv], slot stride out_slot_stride,
+ *                  dense inside a slot
+ *
+ * For slot i < n: out[i, c, k] = src[clamp(abs_positions[i] - d_conv + k,
+ * 0, seq_len - 1), c]  (bit copies).  Slots i >= n are not written.
+ *
+ * Host errors (SCONV_ERR_INVALID): seq_len < 1, conv_dim < 0, max_count < 0,
+ * NULL pointer, unknown dtype.  d_conv outside [1, 4]: SCONV_ERR_UNSUPPORTED.
+ */
+int gather_intermediate_conv_window(const void* src, int64_t seq_len, int32_t conv_dim,
+                                    int64_t src_stride_s, int64_t src_stride_c,
+                                    const int32_t* abs_positions,
+                                    const int32_t* real_count_dev, int32_t max_count,
+                                    void* out, int64_t out_slot_stride, int32_t d_conv,
+                                    int32_t dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SCONV_H */

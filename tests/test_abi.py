@@ -1,0 +1,117 @@
+"""The C ABI library loads, exports every entry point the header declares,
+and rejects bad host arguments before touching the GPU (CPU only: no call
+here reaches a kernel launch)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sconv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from depthwise_causal_conv1d_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from depthwise_causal_conv1d_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_five_ops():
+    names = set(declared_functions())
+    assert {"sconv_seq_metadata", "sconv_fused_insert_conv", "causal_conv1d_varlen_fwd",
+            "causal_conv1d_update", "gather_intermediate_conv_window",
+            "sconv_last_error"} <= names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from depthwise_causal_conv1d_amd import _lib
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.EXPORTS)
+
+
+def test_version_and_clean_error(lib):
+    assert b"gfx950" in lib.sconv_version()
+
+
+NULL = None
+
+
+def test_metadata_rejects_bad_scalars(lib):
+    rc = lib.sconv_seq_metadata(NULL, 1, 10, 5, NULL, 10, NULL, 10, NULL)
+    assert rc == 1 and b"cover" in lib.sconv_last_error()
+    rc = lib.sconv_seq_metadata(NULL, 1, 4, 8, NULL, 7, NULL, 8, NULL)
+    assert rc == 1 and b"seq_idx_out is too small" in lib.sconv_last_error()
+    rc = lib.sconv_seq_metadata(NULL, 1, 4, 8, NULL, 8, NULL, 6, NULL)
+    assert rc == 1 and b"query_start_out is too small" in lib.sconv_last_error()
+    rc = lib.sconv_seq_metadata(NULL, 0, 4, 8, NULL, 8, NULL, 8, NULL)
+    assert rc == 1
+    # nothing to do is a success and launches nothing
+    assert lib.sconv_seq_metadata(NULL, 0, 0, 0, NULL, 0, NULL, 0, NULL) == 0
+
+
+def _fused(lib, **kw):
+    a = dict(x=NULL, xrs=16, w=NULL, wsc=4, wsk=1, cache=NULL, nb=8, H=2, N=16, D=32,
+             cs0=1024, cs1=512, cs2=32, pos=NULL, bt=NULL, btrs=4, mb=4, si=NULL, sm=NULL,
+             qs=NULL, out=NULL, ors=16, T=64, off=0, ws=8, W=4, dt=0, act=1, res=1)
+    a.update(kw)
+    return lib.sconv_fused_insert_conv(*a.values(), NULL)
+
+
+def test_fused_rejects_bad_scalars(lib):
+    assert _fused(lib, W=5) == 1 and b"W=5" in lib.sconv_last_error()
+    assert _fused(lib, W=0) == 1
+    assert _fused(lib, off=28) == 1 and b"outside D" in lib.sconv_last_error()
+    assert _fused(lib, dt=7) == 1
+    assert _fused(lib, act=3) == 1
+    assert _fused(lib, T=-1) == 1
+    assert _fused(lib, xrs=8) == 1            # row stride < C
+    assert _fused(lib, cs2=16) == 1           # D rows overlap
+    assert _fused(lib, T=0) == 0              # empty batch: no-op
+    assert _fused(lib) == 1 and b"NULL" in lib.sconv_last_error()
+    buf = (ctypes.c_uint8 * 64)()
+    p = ctypes.addressof(buf)
+    # out == x is rejected before anything runs
+    assert _fused(lib, x=p, w=p, cache=p + 4096 * 1024, pos=p, bt=p, si=p, sm=p, qs=p,
+                  out=p) == 1
+    assert b"overlaps" in lib.sconv_last_error()
+
+
+def test_ssm_ops_reject_bad_scalars(lib):
+    v = lib.causal_conv1d_varlen_fwd
+    assert v(NULL, 1, 1, NULL, 4, 1, NULL, NULL, 1, 1, 1, 1, NULL, 1, NULL, NULL, NULL, 1, 1, 8,
+             8, 5, 1, 1, -1, NULL) == 1
+    assert v(NULL, 1, 1, NULL, 4, 1, NULL, NULL, 1, 1, 1, 1, NULL, 0, NULL, NULL, NULL, 1, 1, 8,
+             8, 4, 1, 1, -1, NULL) == 0            # batch 0: no-op
+    u = lib.causal_conv1d_update
+    one = ctypes.c_int32(1)
+    assert u(NULL, 8, NULL, 1, 24, 3, 1, NULL, 4, 1, NULL, ctypes.addressof(one), NULL, NULL, 8,
+             1, 8, 4, 1, 1, -1, NULL) == 2          # cache_seqlens not supported
+    assert b"cache_seqlens" in lib.sconv_last_error()
+    assert u(NULL, 8, NULL, 1, 24, 3, 1, NULL, 4, 1, NULL, NULL, NULL, NULL, 8, 1, 8, 9, 1, 1,
+             -1, NULL) == 1
+    g = lib.gather_intermediate_conv_window
+    assert g(NULL, 10, 8, 8, 1, NULL, NULL, 4, NULL, 24, 5, 1, NULL) == 2   # d_conv 5
+    assert g(NULL, 0, 8, 8, 1, NULL, NULL, 4, NULL, 24, 3, 1, NULL) == 1    # seq_len 0
+    assert g(NULL, 10, 8, 8, 1, NULL, NULL, 0, NULL, 24, 3, 1, NULL) == 0   # no slots
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The binding has no CPU fallback: a missing library is an import error."""
+    from depthwise_causal_conv1d_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

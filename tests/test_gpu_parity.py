@@ -1,0 +1,474 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle.
+
+Outputs are compared element by element within the stated tolerance
+(fp32: rtol 1e-5 + atol 1e-6; bf16 I/O with fp32 accumulation: atol 1e-2,
+rtol 1.6e-2).  Integer metadata, cache contents, states and gathered windows
+must match bit for bit; PAD rows and dead slots must keep their sentinel.
+"""
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.gpu_util import SENTINEL, dtype_name, gpu_fused, live_rows, oracle_fused
+from tests.helpers import assert_bits_equal, assert_close, to_np
+
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("oracle_lib")]
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import depthwise_causal_conv1d_amd  # noqa: F401  (fails loudly if not built)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ metadata
+
+@pytest.mark.parametrize("seed,R,max_len,extra_pad", [
+    (0, 1, 64, 0), (1, 7, 9, 5), (2, 256, 3, 0), (3, 512, 8, 37), (4, 9000, 2, 11),
+    (5, 3, 0, 4)])
+def test_seq_metadata_bit_exact(seed, R, max_len, extra_pad):
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    say(f"metadata seed={seed} R={R}")
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, max_len + 1, R)
+    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    num_actual = int(qsl[-1]) + (2 if seed == 1 else 0)
+    num_padded = num_actual + extra_pad
+    si_ref, qs_ref = oracle.seq_metadata(qsl, R, num_actual, num_padded)
+    n = max(num_padded, 1) + 3
+    si = torch.full((n,), -9, dtype=torch.int32, device=DEV)
+    qs = torch.full((n,), -9, dtype=torch.int32, device=DEV)
+    lib.sconv_seq_metadata(torch.from_numpy(qsl).to(DEV), R, num_actual, si, qs, num_padded)
+    si_h, qs_h = to_np(si), to_np(qs)
+    np.testing.assert_array_equal(si_h[:num_padded], si_ref)
+    np.testing.assert_array_equal(qs_h[:num_padded], qs_ref)
+    assert (si_h[num_padded:] == -9).all() and (qs_h[num_padded:] == -9).all()
+
+
+def test_seq_metadata_errors():
+    import depthwise_causal_conv1d_amd as lib
+    qsl = torch.tensor([0, 4], dtype=torch.int32, device=DEV)
+    buf = torch.zeros(4, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="cover"):
+        lib.sconv_seq_metadata(qsl, 1, 4, buf, buf.clone(), 3)
+    with pytest.raises(ValueError, match="too small"):
+        lib.sconv_seq_metadata(qsl, 1, 4, buf[:3], buf.clone(), 4)
+
+
+# ------------------------------------------------------------------ fused insert + conv
+
+def check_fused(case, what, cache_compare="full"):
+    """Run both sides on one case and compare out, metadata and cache."""
+    say(f"fused {what}: T={case.T} C={case.C} W={case.W} N={case.block_size} "
+        f"dtype={case.x.dtype} off_s={case.off_s}")
+    out_g, cache_g, si_g, qs_g = gpu_fused(case)
+    if cache_compare == "full":
+        out_r, cache_r, si_r, qs_r = oracle_fused(case)
+        cache_gh = to_np(cache_g)
+    else:  # compact both sides to the referenced blocks
+        cc, bt, sm = case.compact()
+        out_r, cache_r, si_r, qs_r = oracle_fused(case, cache=cc, block_table=bt, slot_mapping=sm)
+        ids = case.used_blocks.to(cache_g.device)
+        cache_gh = to_np(cache_g[ids])
+        # blocks nobody references must still be untouched poison
+        untouched = torch.ones(cache_g.shape[0], dtype=torch.bool, device=cache_g.device)
+        untouched[ids] = False
+        if untouched.any():
+            assert torch.isnan(cache_g[untouched].float()).all(), "write outside referenced blocks"
+    np.testing.assert_array_equal(to_np(si_g), si_r)
+    np.testing.assert_array_equal(to_np(qs_g), qs_r)
+    live = live_rows(case)
+    out_gh = to_np(out_g)
+    assert_close(out_gh, out_r, dtype_name(case.x.dtype), f"{what} out", mask=live)
+    assert_bits_equal(out_gh[~live], out_r[~live], f"{what} PAD rows untouched")
+    assert_bits_equal(cache_gh, cache_r, f"{what} cache")
+    return out_g, cache_g
+
+
+SWEEP = [
+    # name, dtype, W, H, ws, D, off_s, N, new, ctx, pad, tail, act, res
+    ("bf16-vec", torch.bfloat16, 4, 4, 16, 48, 16, 16, [5, 40, 1, 17, 3], [0, 70, 2, 31, 15], 6, 3, "silu", True),
+    ("bf16-scalar", torch.bfloat16, 4, 3, 6, 16, 3, 16, [9, 1, 22], [4, 50, 0], 2, 0, "silu", True),
+    ("f32-vec", torch.float32, 4, 2, 8, 32, 8, 16, [12, 2, 30], [1, 9, 60], 3, 2, "silu", True),
+    ("f32-scalar", torch.float32, 3, 5, 3, 7, 2, 8, [6, 13], [3, 0], 1, 1, None, True),
+    ("n24-nonpow2", torch.bfloat16, 4, 2, 8, 16, 0, 24, [30, 7, 1], [50, 0, 23], 2, 0, "silu", False),
+    ("n1", torch.bfloat16, 4, 2, 8, 8, 0, 1, [6, 4], [5, 2], 0, 0, None, False),
+    ("n32-w2", torch.bfloat16, 2, 8, 16, 64, 32, 32, [20, 1, 3], [100, 31, 0], 2, 4, "silu", True),
+    ("w1", torch.float32, 1, 2, 8, 16, 8, 16, [7, 3], [9, 0], 1, 0, "silu", True),
+    ("w3-f32", torch.float32, 3, 4, 4, 12, 4, 4, [11, 2, 5], [0, 7, 3], 2, 1, "silu", True),
+]
+
+
+@pytest.mark.parametrize("spec", SWEEP, ids=[s[0] for s in SWEEP])
+def test_fused_sweep(spec):
+    name, dt, W, H, ws, D, off, N, new, ctx, pad, tail, act, res = spec
+    case = workloads.fused_case(zlib.crc32(name.encode()) % 1000, new, ctx, H=H, D=D, ws=ws, off_s=off,
+                                block_size=N, W=W, dtype=dt, pad_count=pad, tail_pad=tail,
+                                activation=act, use_residual=res)
+    check_fused(case, name)
+
+
+@pytest.mark.parametrize("T_total,C_heads", [(4507, 32), (2000, 32), (500, 32)])
+def test_fused_tile_shapes(T_total, C_heads):
+    """Token counts that select each rows-per-wave tile (16, 4, 1) with a
+    ragged tail, several requests per tile and requests straddling tiles."""
+    rng = np.random.default_rng(T_total)
+    R = 23
+    cuts = np.sort(rng.choice(np.arange(1, T_total), R - 1, replace=False))
+    new = np.diff(np.concatenate([[0], cuts, [T_total]])).tolist()
+    ctx = [int(v) for v in rng.integers(0, 300, R)]
+    case = workloads.fused_case(7, new, ctx, H=C_heads, D=256, ws=128, off_s=128,
+                                block_size=16, W=4, dtype=torch.bfloat16,
+                                pad_count=T_total // 10, tail_pad=5)
+    check_fused(case, f"tiles T={T_total}")
+
+
+def test_config_tiny_prefill():
+    case = workloads.tiny_prefill()
+    check_fused(case, "tiny prefill (fp32)")
+
+
+def test_config_batched_decode():
+    case = workloads.batched_decode()
+    check_fused(case, "batched decode", cache_compare="compact")
+
+
+def test_config_batched_decode_large_pool():
+    """Same decode batch with its blocks scattered over a 16k-block pool."""
+    case = workloads.batched_decode(pool_blocks=16384, device=DEV)
+    check_fused(case, "batched decode, large pool", cache_compare="compact")
+
+
+def test_config_mixed_prefill_four_streams():
+    """Four streams convolved in turn over one shared cache, 10% PAD rows."""
+    streams = workloads.mixed_prefill_streams()
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    base = streams[0]
+    say(f"mixed prefill T={base.T} C={base.C} blocks={base.cache.shape[0]}")
+    cache_g = base.cache.to(DEV).clone()
+    qsl = base.query_start_loc.to(DEV)
+    si = torch.empty(base.T, dtype=torch.int32, device=DEV)
+    qs = torch.empty_like(si)
+    lib.sconv_seq_metadata(qsl, base.num_reqs, base.num_actual, si, qs, base.T)
+    pos, bt, sm = base.positions.to(DEV), base.block_table.to(DEV), base.slot_mapping.to(DEV)
+    si_r, qs_r = oracle.seq_metadata(to_np(base.query_start_loc), base.num_reqs,
+                                     base.num_actual, base.T)
+    cache_r = to_np(base.cache)
+    live = live_rows(base)
+    for s, case in enumerate(streams):
+        out_g = torch.full_like(case.x, SENTINEL, device=DEV)
+        lib.sconv_fused_insert_conv(case.x.to(DEV), case.weight.to(DEV), cache_g, pos, bt, si,
+                                    sm, qs, case.off_s, case.ws, case.block_size, "silu", True,
+                                    out=out_g)
+        out_r, cache_r = oracle.fused_insert_conv(
+            to_np(case.x), to_np(case.weight), cache_r, to_np(base.positions),
+            to_np(base.block_table), si_r, to_np(base.slot_mapping), qs_r, case.off_s, case.ws,
+            case.block_size, "silu", True, out_init=np.full(case.x.shape, 0xC442, np.uint16))
+        out_h = to_np(out_g)
+        assert_close(out_h, out_r, "bf16", f"stream {s}", mask=live)
+        assert (out_h[~live] == 0xC442).all()   # bf16 bits of -777
+        say(f"  stream {s} ok")
+    assert_bits_equal(to_np(cache_g), cache_r, "shared cache after four streams")
+
+
+def test_config_spec_decode():
+    case = workloads.spec_decode()
+    check_fused(case, "spec decode", cache_compare="compact")
+
+
+# ------------------------------------------------------------------ hipGraph replay
+
+def test_graph_replay_decode_steps():
+    """Capture metadata + fused conv once for a decode batch; replay it for
+    successive steps with new inputs written into the captured buffers.
+    Each replay must equal the oracle; each step reads the previous steps'
+    cache writes."""
+    import depthwise_causal_conv1d_amd as lib
+    R, S = 64, 6
+    g = torch.Generator().manual_seed(17)
+    ctx = [int(v) for v in torch.randint(1, 700, (R,), generator=g)]
+    case = workloads.fused_case(17, [S] * R, ctx, H=8, D=64, ws=32, off_s=32, block_size=16,
+                                W=4, dtype=torch.bfloat16)
+    ref_out, ref_cache, _, _ = oracle_fused(case)     # one S-token call == S steps
+    qsl_h = case.query_start_loc
+    rows = lambda s: (qsl_h[:-1] + s).long()
+    x_b = torch.zeros(R, case.C, dtype=torch.bfloat16, device=DEV)
+    pos_b = torch.zeros(R, dtype=torch.int64, device=DEV)
+    sm_b = torch.zeros(R, dtype=torch.int64, device=DEV)
+    qsl_b = torch.arange(R + 1, dtype=torch.int32, device=DEV)
+    si_b = torch.zeros(R, dtype=torch.int32, device=DEV)
+    qs_b = torch.zeros(R, dtype=torch.int32, device=DEV)
+    out_b = torch.zeros_like(x_b)
+    w = case.weight.to(DEV)
+    cache = case.cache.to(DEV).clone()
+    bt = case.block_table.to(DEV)
+
+    def step():
+        lib.sconv_seq_metadata(qsl_b, R, R, si_b, qs_b, R)
+        lib.sconv_fused_insert_conv(x_b, w, cache, pos_b, bt, si_b, sm_b, qs_b, case.off_s,
+                                    case.ws, case.block_size, "silu", True, out=out_b)
+
+    def load(s):
+        x_b.copy_(case.x[rows(s)].to(DEV))
+        pos_b.copy_(case.positions[rows(s)].to(DEV))
+        sm_b.copy_(case.slot_mapping[rows(s)].to(DEV))
+
+    # warm up on a side stream, then restore the cache
+    cache0 = cache.clone()
+    load(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    cache.copy_(cache0)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    cache.copy_(cache0)
+    for s in range(S):
+        load(s)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_close(to_np(out_b), ref_out[rows(s).numpy()], "bf16", f"replay {s}")
+        say(f"  replay {s} ok")
+    assert_bits_equal(to_np(cache), ref_cache, "cache after replays")
+
+
+# ------------------------------------------------------------------ SSM-style ops
+
+def gpu_varlen(case, inplace=False):
+    import depthwise_causal_conv1d_amd as lib
+    x = case.x.to(DEV)
+    st = case.conv_states.to(DEV).clone()
+    out = x.clone() if inplace else torch.full_like(x, SENTINEL)
+    xin = out if inplace else x
+    lib.causal_conv1d_varlen_fwd(
+        xin, case.weight.to(DEV), None if case.bias is None else case.bias.to(DEV), st,
+        case.query_start_loc.to(DEV),
+        None if case.cache_indices is None else case.cache_indices.to(DEV),
+        None if case.has_initial_state is None else case.has_initial_state.to(DEV),
+        case.activation == "silu", case.pad_slot_id, out=out)
+    return out, st
+
+
+def oracle_varlen(case):
+    import oracle
+    return oracle.causal_conv1d_varlen_fwd(
+        to_np(case.x), to_np(case.weight), None if case.bias is None else to_np(case.bias),
+        to_np(case.conv_states), to_np(case.query_start_loc),
+        None if case.cache_indices is None else to_np(case.cache_indices),
+        None if case.has_initial_state is None else to_np(case.has_initial_state),
+        case.activation, case.pad_slot_id, out_init=_sentinel_like(case.x))
+
+
+def _sentinel_like(t):
+    return to_np(torch.full_like(t, SENTINEL))
+
+
+VARLEN = [
+    # name, dtype, lens, dim, W, init, pad, bias, act, x_padding
+    ("bf16-aligned", torch.bfloat16, [64, 128, 512, 8], 24, 4, 2, 0, 0.1, "silu", 0),
+    ("bf16-ragged", torch.bfloat16, [13, 1, 0, 700, 2, 91], 10, 4, 3, 1, 0.1, "silu", 0),
+    ("bf16-xpad", torch.bfloat16, [37, 200, 5], 16, 4, 1, 0, None, None, 11),
+    ("f32-ragged", torch.float32, [5, 300, 17, 1], 12, 4, 2, 1, 0.2, "silu", 0),
+    ("f32-w3", torch.float32, [9, 66], 8, 3, 1, 0, 0.2, "silu", 0),
+    ("bf16-w2", torch.bfloat16, [1, 9, 130], 8, 2, 2, 0, 0.1, None, 0),
+    ("bf16-w1", torch.bfloat16, [4, 20], 8, 1, 1, 0, 0.1, "silu", 0),
+]
+
+
+@pytest.mark.parametrize("spec", VARLEN, ids=[v[0] for v in VARLEN])
+def test_varlen_sweep(spec):
+    name, dt, lens, dim, W, init, pad, bias, act, xpad = spec
+    case = workloads.varlen_case(zlib.crc32(name.encode()) % 1000, lens, dim=dim, num_slots=len(lens) + 5, W=W,
+                                 dtype=dt, init_count=init, pad_seqs=pad, bias_std=bias,
+                                 activation=act, x_padding=xpad)
+    say(f"varlen {name}")
+    out_r, st_r = oracle_varlen(case)
+    for inplace in (False, True):
+        out_g, st_g = gpu_varlen(case, inplace=inplace)
+        ci = to_np(case.cache_indices)
+        qsl = to_np(case.query_start_loc)
+        mask = np.zeros(case.x.shape, bool)
+        for b in range(len(lens)):
+            if ci[b] != case.pad_slot_id:
+                mask[:, qsl[b]:qsl[b + 1]] = True
+        og = to_np(out_g)
+        assert_close(og, out_r, dtype_name(dt), f"{name} out inplace={inplace}", mask=mask)
+        if not inplace:
+            assert_bits_equal(og[~mask], out_r[~mask], "PAD sequences untouched")
+        assert_bits_equal(to_np(st_g), st_r, f"{name} states inplace={inplace}")
+
+
+def test_varlen_transposed_view_and_null_options():
+    """x given as a transposed view (token stride != 1): the scalar path;
+    no cache_indices / has_initial_state (slot b, zero history)."""
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    g = torch.Generator().manual_seed(3)
+    base = torch.randn(90, 12, generator=g).to(torch.bfloat16)      # [T, dim]
+    x = base.T                                                       # [dim, T] view
+    w = (torch.randn(12, 4, generator=g) * 0.5).to(torch.bfloat16)
+    st = torch.full((3, 12, 3), float("nan"), dtype=torch.bfloat16)
+    qsl = torch.tensor([0, 40, 41, 90], dtype=torch.int32)
+    out_r, st_r = oracle.causal_conv1d_varlen_fwd(to_np(x), to_np(w), None, to_np(st),
+                                                  to_np(qsl), None, None, "silu", -1)
+    xd = base.to(DEV).T
+    std = st.to(DEV)
+    out_g = torch.empty(12, 90, dtype=torch.bfloat16, device=DEV)
+    lib.causal_conv1d_varlen_fwd(xd, w.to(DEV), None, std, qsl.to(DEV), None, None, True, -1,
+                                 out=out_g)
+    assert_close(to_np(out_g), out_r, "bf16", "transposed view")
+    assert_bits_equal(to_np(std), st_r, "states")
+
+
+def test_config_ssm_varlen_and_updates():
+    """8 x 4096 tokens, dim 8192, pool of 1024 slots, then 64 decode steps."""
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    case = workloads.ssm_varlen()
+    say("ssm varlen: oracle")
+    out_r, st_r = oracle_varlen(case)
+    say("ssm varlen: gpu")
+    out_g, st_g = gpu_varlen(case)
+    assert_close(to_np(out_g), out_r, "bf16", "ssm varlen out")
+    assert_bits_equal(to_np(st_g), st_r, "ssm varlen states")
+    out_i, st_i = gpu_varlen(case, inplace=True)
+    assert_bits_equal(to_np(out_i), to_np(out_g), "in-place == out-of-place")
+    assert_bits_equal(to_np(st_i), to_np(st_g), "in-place states")
+    del out_i, st_i
+    say("ssm updates")
+    xs = workloads.update_inputs(3, 64, 8, 8192)
+    ci = case.cache_indices
+    w, b = case.weight, case.bias
+    st_cpu = st_r
+    wd, bd, cid = w.to(DEV), b.to(DEV), ci.to(DEV)
+    for s, xs_s in enumerate(xs):
+        y_r, st_cpu = oracle.causal_conv1d_update(to_np(xs_s), st_cpu, to_np(w), to_np(b), "silu",
+                                                  to_np(ci), -1)
+        y_g = lib.causal_conv1d_update(xs_s.to(DEV), st_g, wd, bd, True, None, cid, -1,
+                                       out=torch.empty(8, 8192, dtype=torch.bfloat16, device=DEV))
+        assert_close(to_np(y_g), y_r, "bf16", f"update step {s}")
+    assert_bits_equal(to_np(st_g), st_cpu, "states after 64 updates")
+
+
+@pytest.mark.parametrize("dt,W,dim,idx,inplace", [
+    (torch.bfloat16, 4, 64, True, False), (torch.bfloat16, 4, 60, True, True),
+    (torch.float32, 4, 32, False, False), (torch.float32, 2, 10, True, True),
+    (torch.bfloat16, 3, 40, True, False), (torch.bfloat16, 1, 16, True, False)])
+def test_update_sweep(dt, W, dim, idx, inplace):
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    g = torch.Generator().manual_seed(dim * 10 + W)
+    batch, slots = 7, 11
+    x = torch.randn(batch, dim, generator=g).to(dt)
+    w = (torch.randn(dim, W, generator=g) * 0.5).to(dt)
+    b = (torch.randn(dim, generator=g) * 0.1).to(dt)
+    st = torch.randn(slots, dim, W - 1, generator=g).to(dt)
+    ci = torch.randperm(slots, generator=g)[:batch].to(torch.int32)
+    ci[3] = -1
+    if not idx:
+        ci = None
+    out_r, st_r = oracle.causal_conv1d_update(to_np(x), to_np(st), to_np(w), to_np(b), "silu",
+                                              None if ci is None else to_np(ci), -1,
+                                              out_init=_sentinel_like(x))
+    xd = x.to(DEV)
+    std = st.to(DEV)
+    out = xd if inplace else torch.full_like(xd, SENTINEL)
+    lib.causal_conv1d_update(xd, std, w.to(DEV), b.to(DEV), True, None,
+                             None if ci is None else ci.to(DEV), -1, out=out)
+    live = np.ones(batch, bool)
+    if ci is not None:
+        live[3] = False
+    assert_close(to_np(out), out_r, dtype_name(dt), "update out", mask=live)
+    if not inplace and ci is not None:
+        assert_bits_equal(to_np(out)[3], out_r[3], "PAD row untouched")
+    assert_bits_equal(to_np(std), st_r, "states")
+
+
+# ------------------------------------------------------------------ gather
+
+@pytest.mark.parametrize("real_count", [0, 1, 256, 512, 600, -4])
+def test_config_spec_gather(real_count):
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    case = workloads.spec_decode()
+    gc = workloads.spec_gather(case, real_count=real_count)
+    say(f"gather real_count={real_count}")
+    out_r = oracle.gather_conv_window(to_np(gc.src), to_np(gc.abs_positions), gc.real_count,
+                                      to_np(gc.out_init), gc.d_conv)
+    out_g = gc.out_init.to(DEV).clone()
+    rc = torch.tensor([gc.real_count], dtype=torch.int32, device=DEV)
+    lib.gather_intermediate_conv_window(gc.src.to(DEV), gc.abs_positions.to(DEV), rc, out_g,
+                                        gc.d_conv)
+    assert_bits_equal(to_np(out_g), out_r, "gathered windows")
+
+
+@pytest.mark.parametrize("dt,conv_dim,d_conv,seq_len", [
+    (torch.bfloat16, 24, 3, 50), (torch.float32, 12, 4, 9), (torch.bfloat16, 7, 2, 30),
+    (torch.float32, 5, 1, 3)])
+def test_gather_sweep(dt, conv_dim, d_conv, seq_len):
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    g = torch.Generator().manual_seed(conv_dim)
+    src = torch.randn(1, seq_len, conv_dim, generator=g).to(dt)
+    mc = 19
+    pos = torch.randint(-3, seq_len + 5, (mc,), generator=g).to(torch.int32)
+    out0 = torch.full((mc, conv_dim, d_conv), SENTINEL).to(dt)
+    for n in (0, 7, mc):
+        out_r = oracle.gather_conv_window(to_np(src), to_np(pos), n, to_np(out0), d_conv)
+        out_g = out0.to(DEV).clone()
+        lib.gather_intermediate_conv_window(src.to(DEV), pos.to(DEV),
+                                            torch.tensor([n], dtype=torch.int32, device=DEV),
+                                            out_g, d_conv)
+        assert_bits_equal(to_np(out_g), out_r, f"gather n={n}")
+
+
+def test_gather_graph_replay_with_device_count():
+    """Grid fixed at capture (max_count); the live count changes between
+    replays through the fixed device buffer only."""
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    case = workloads.spec_decode()
+    gc = workloads.spec_gather(case, real_count=0)
+    src = gc.src.to(DEV)
+    pos = gc.abs_positions.to(DEV)
+    rc = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = gc.out_init.to(DEV).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lib.gather_intermediate_conv_window(src, pos, rc, out, 3)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lib.gather_intermediate_conv_window(src, pos, rc, out, 3)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(99)
+    for n in [0, 512, 3] + [int(v) for v in torch.randint(0, 513, (4,), generator=g)]:
+        out.copy_(gc.out_init.to(DEV))
+        rc.fill_(n)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        out_r = oracle.gather_conv_window(to_np(gc.src), to_np(gc.abs_positions), n,
+                                          to_np(gc.out_init), 3)
+        assert_bits_equal(to_np(out), out_r, f"replay n={n}")
