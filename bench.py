@@ -1,0 +1,580 @@
+"""Benchmark of the paged short-convolution hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload (the headline): batched decode -- 256 requests x 1 token,
+history lengths uniform in [1, 4096], H=32, D=128, ws=32 (C=1024), W=4,
+N=16, bf16, SiLU and residual.  One step is one pass of the hot path over one
+decode batch: sconv_seq_metadata + sconv_fused_insert_conv, replayed from a
+hipGraph.  Other workloads (same JSON shape, one line each):
+  mixed_prefill  16 requests, ~17-20k rows, 4 streams of C=4096 over one
+                 cache, 10% PAD rows; step = metadata + 4 fused launches
+  spec_decode    512 requests x 4 draft rows, C=4096, N=32; step = metadata
+                 + fused launch + conv-window gather (device real_count)
+  ssm_prefill    8 x 4096 tokens, dim 8192, channel-major, state pool of
+                 1024 slots; step = causal_conv1d_varlen_fwd
+  ssm_decode     8 rows x dim 8192 against the same pool; step =
+                 causal_conv1d_update
+
+Successive steps cycle through independent replicas of the workload's
+inputs (own inputs, outputs, tables and cache blocks) so that at least
+~512 MB separate two visits of the same bytes: every step reads HBM, not the
+L2s or the 256 MB MALL.
+
+Prints one JSON line.  `value` is tokens per second over the K timed steps
+(wall clock between two device synchronizations).  `roofline` describes the
+workload's dominant kernel: algorithmic bytes per launch divided by its
+average launch duration, timed with HIP events on the stream it runs on.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s and achieved HBM GB/s (% of peak) for fused paged sconv, decode + prefill"
+HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "depthwise_causal_conv1d_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+FLUSH_BYTES = 512 << 20   # bytes that must separate two visits of a replica
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """Hash of the GPU sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current sources."""
+    path = os.path.join(PROFILES, f"counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_sources:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.e+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_digest():
+        return None
+    return float(t.group(1))
+
+
+# ---------------------------------------------------------------- accounting
+
+def fused_algorithmic_bytes(case, rows=None) -> int:
+    """Bytes one fused launch over `rows` of case must move: input rows read
+    (each once), distinct pre-forward cache positions tapped, slot writes and
+    output writes of non-PAD rows, the weights, 24 B of per-row metadata and
+    the block-table entries followed."""
+    e = case.x.element_size()
+    C, W, N = case.C, case.W, case.block_size
+    pos = case.positions.numpy()
+    sm = case.slot_mapping.numpy()
+    qsl = case.query_start_loc.numpy()
+    lo, hi = rows if rows is not None else (0, case.T)
+    live = sm[lo:hi] >= 0
+    n_live = int(live.sum())
+    need = live.copy()
+    taps = 0
+    bt_entries = 0
+    for r in range(case.num_reqs):
+        a, b = max(int(qsl[r]), lo), min(int(qsl[r + 1]), hi)
+        if a >= b:
+            continue
+        first = int(pos[int(qsl[r])])
+        tapped = set()
+        for t in range(a, b):
+            if sm[t] < 0:
+                continue
+            for lag in range(1, W):
+                src = int(pos[t]) - lag
+                if src < 0:
+                    continue
+                if t - lag >= int(qsl[r]):
+                    need[t - lag - lo] = True
+                elif src < first:
+                    tapped.add(src)
+        taps += len(tapped)
+        bt_entries += len({p // N for p in tapped})
+    x_rows = int(need.sum())
+    return (x_rows + taps + 2 * n_live) * C * e + C * W * e + 24 * (hi - lo) + 4 * bt_entries
+
+
+def sub_case(case, rows, reqs, poison):
+    """The requests `reqs` (rows `rows`) of a multi-batch case as a case of
+    their own, for the oracle."""
+    import torch
+
+    import workloads
+    bt = case.block_table[reqs]
+    u = torch.unique(bt.long())
+    if not (u == poison).any():
+        u = torch.cat([u, torch.tensor([poison])])
+    qsl = case.query_start_loc[reqs.start:reqs.stop + 1] - case.query_start_loc[reqs.start]
+    return workloads.FusedCase(**{**case.__dict__, "x": case.x[rows],
+                                  "positions": case.positions[rows], "block_table": bt,
+                                  "slot_mapping": case.slot_mapping[rows],
+                                  "query_start_loc": qsl.to(torch.int32),
+                                  "num_reqs": reqs.stop - reqs.start,
+                                  "num_actual": rows.stop - rows.start,
+                                  "used_blocks": torch.sort(u).values})
+
+
+def time_oracle_fused(case, activation="silu"):
+    """Seconds the oracle spends on one fused launch of `case` (compact cache)."""
+    import oracle
+    from tests.helpers import to_np
+    cache, bt, sm = case.compact()
+    si, qs = oracle.seq_metadata(to_np(case.query_start_loc), case.num_reqs, case.num_actual,
+                                 case.T)
+    args = (to_np(case.x), to_np(case.weight), to_np(cache), to_np(case.positions), to_np(bt),
+            si, to_np(sm), qs, case.off_s, case.ws, case.block_size, activation,
+            case.use_residual)
+    t0 = time.perf_counter()
+    oracle.fused_insert_conv(*args)
+    return time.perf_counter() - t0
+
+
+# ---------------------------------------------------------------- workloads
+
+class Workload:
+    kernel_name = "fused_insert_conv_kernel"
+    bound = "hbm"
+    dtype = "bf16"
+
+    def kernel(self, i):          # the dominant kernel alone
+        raise NotImplementedError
+
+    def kernels_per_call(self):   # launches of it per kernel(i)
+        return 1
+
+
+class DecodeBench(Workload):
+    """R independent decode batches of 256 requests sharing one large cache."""
+
+    B = 256
+
+    def __init__(self, dev="cuda"):
+        import torch
+
+        import depthwise_causal_conv1d_amd as lib
+        import workloads
+        self.lib = lib
+        B = self.B
+        probe = 3_161_224  # algorithmic bytes of one batch (checked below)
+        self.R = max(2, -(-FLUSH_BYTES // probe) + 16)
+        t = time.time()
+        self.case = workloads.batched_decode(device=dev, num_reqs=B * self.R,
+                                             pool_blocks=int(B * self.R * 2 * 1.25) + 1)
+        c = self.case
+        log(f"batched_decode: {self.R} batches in {time.time() - t:.1f}s, cache "
+            f"{c.cache.numel() * c.cache.element_size() / 2**30:.1f} GiB")
+        self.x, self.w, self.cache = c.x.to(dev), c.weight.to(dev), c.cache
+        self.pos, self.sm, self.bt = c.positions.to(dev), c.slot_mapping.to(dev), c.block_table.to(dev)
+        self.out = torch.empty_like(self.x)
+        self.qsl = torch.arange(B + 1, dtype=torch.int32, device=dev)
+        self.si = torch.empty(B, dtype=torch.int32, device=dev)
+        self.qs = torch.empty(B, dtype=torch.int32, device=dev)
+        self.bytes_per_launch = fused_algorithmic_bytes(c, (0, B))
+        self.tokens_per_step = B
+
+    def rows(self, i):
+        return slice(i * self.B, (i + 1) * self.B)
+
+    def kernel(self, i):
+        s, c = self.rows(i), self.case
+        self.lib.sconv_fused_insert_conv(self.x[s], self.w, self.cache, self.pos[s], self.bt[s],
+                                         self.si, self.sm[s], self.qs, c.off_s, c.ws,
+                                         c.block_size, "silu", True, out=self.out[s])
+
+    def step(self, i):
+        self.lib.sconv_seq_metadata(self.qsl, self.B, self.B, self.si, self.qs, self.B)
+        self.kernel(i)
+
+    def config(self):
+        return {"workload": "batched_decode", "requests": 256, "tokens_per_step": 256,
+                "history": "uniform[1,4096]", "H": 32, "D": 128, "ws": 32, "C": 1024,
+                "W": 4, "block_size": 16, "activation": "silu", "residual": True,
+                "graph": "hipGraph", "replicas": self.R}
+
+    def oracle_sample(self, budget):
+        done, spent, i = 0, 0.0, 0
+        while i < self.R and (spent < budget or done == 0):
+            sub = sub_case(self.case, self.rows(i), self.rows(i), self.case.poison_block)
+            spent += time_oracle_fused(sub)
+            done += self.B
+            i += 1
+        return done / spent, f"{i} whole decode batches ({done} tokens)", spent
+
+
+class MixedPrefillBench(Workload):
+    """Four streams of one layer convolved in turn over one shared cache."""
+
+    def __init__(self, dev="cuda"):
+        import torch
+
+        import depthwise_causal_conv1d_amd as lib
+        import workloads
+        self.lib = lib
+        t = time.time()
+        self.streams = workloads.mixed_prefill_streams()
+        b = self.streams[0]
+        log(f"mixed_prefill: T={b.T} generated in {time.time() - t:.1f}s")
+        self.bytes_per_launch = fused_algorithmic_bytes(b)
+        self.R = 1   # one step moves ~4 x bytes_per_launch >> MALL
+        self.cache = b.cache.to(dev)
+        self.xs = [s.x.to(dev) for s in self.streams]
+        self.ws_ = [s.weight.to(dev) for s in self.streams]
+        self.outs = [torch.empty_like(x) for x in self.xs]
+        self.pos, self.sm, self.bt = b.positions.to(dev), b.slot_mapping.to(dev), b.block_table.to(dev)
+        self.qsl = b.query_start_loc.to(dev)
+        self.si = torch.empty(b.T, dtype=torch.int32, device=dev)
+        self.qs = torch.empty(b.T, dtype=torch.int32, device=dev)
+        self.live = int((b.slot_mapping >= 0).sum())
+        self.tokens_per_step = self.live
+
+    def kernel(self, i):
+        b = self.streams[0]
+        for s, st in enumerate(self.streams):
+            self.lib.sconv_fused_insert_conv(self.xs[s], self.ws_[s], self.cache, self.pos, self.bt,
+                                             self.si, self.sm, self.qs, st.off_s, st.ws,
+                                             b.block_size, "silu", True, out=self.outs[s])
+
+    def kernels_per_call(self):
+        return 4
+
+    def step(self, i):
+        b = self.streams[0]
+        self.lib.sconv_seq_metadata(self.qsl, b.num_reqs, b.num_actual, self.si, self.qs, b.T)
+        self.kernel(i)
+
+    def config(self):
+        b = self.streams[0]
+        return {"workload": "mixed_prefill", "requests": 16, "rows": b.T,
+                "non_pad_tokens": self.live, "streams": 4, "H": 32, "D": 512, "ws": 128,
+                "C": 4096, "W": 4, "block_size": 16, "pad_fraction": 0.1,
+                "activation": "silu", "residual": True}
+
+    def oracle_sample(self, budget):
+        # Stream 0 in full; the other three streams cost the same.
+        spent = time_oracle_fused(self.streams[0])
+        return self.live / (4 * spent), "stream 0 of 4, all rows, time x4", spent
+
+
+class SpecDecodeBench(Workload):
+    """Speculative decode (512 x 4 drafts) plus the conv-window gather."""
+
+    B = 2048
+
+    def __init__(self, dev="cuda"):
+        import torch
+
+        import depthwise_causal_conv1d_amd as lib
+        import workloads
+        self.lib = lib
+        first = workloads.spec_decode()
+        self.bytes_per_launch = fused_algorithmic_bytes(first)
+        self.R = max(2, -(-FLUSH_BYTES // self.bytes_per_launch) + 2)
+        t = time.time()
+        reqs = 512 * self.R
+        self.case = workloads.spec_decode(device=dev, num_reqs=reqs,
+                                          pool_blocks=int(reqs * 2 * 1.25) + 1)
+        c = self.case
+        log(f"spec_decode: {self.R} batches in {time.time() - t:.1f}s")
+        self.x, self.w, self.cache = c.x.to(dev), c.weight.to(dev), c.cache
+        self.pos, self.sm, self.bt = c.positions.to(dev), c.slot_mapping.to(dev), c.block_table.to(dev)
+        self.out = torch.empty_like(self.x)
+        self.qsl = torch.arange(0, self.B + 1, 4, dtype=torch.int32, device=dev)
+        self.si = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.qs = torch.empty(self.B, dtype=torch.int32, device=dev)
+        gc = workloads.spec_gather(first)
+        self.gpos = gc.abs_positions.to(dev)
+        self.rc = torch.tensor([gc.real_count], dtype=torch.int32, device=dev)
+        self.gout = torch.empty(self.R, 512, c.C, 3, dtype=torch.bfloat16, device=dev)
+        self.real_count = gc.real_count
+        self.tokens_per_step = self.B
+
+    def rows(self, i):
+        return slice(i * self.B, (i + 1) * self.B)
+
+    def kernel(self, i):
+        s, c = self.rows(i), self.case
+        self.lib.sconv_fused_insert_conv(self.x[s], self.w, self.cache, self.pos[s],
+                                         self.bt[512 * i:512 * (i + 1)], self.si, self.sm[s],
+                                         self.qs, c.off_s, c.ws, c.block_size, "silu", True,
+                                         out=self.out[s])
+
+    def step(self, i):
+        self.lib.sconv_seq_metadata(self.qsl, 512, self.B, self.si, self.qs, self.B)
+        self.kernel(i)
+        self.lib.gather_intermediate_conv_window(self.x[self.rows(i)].view(1, self.B, -1),
+                                                 self.gpos, self.rc, self.gout[i], 3)
+
+    def config(self):
+        return {"workload": "spec_decode", "requests": 512, "drafts": 4, "tokens_per_step": 2048,
+                "positions": "uniform[1,131072)", "H": 64, "D": 64, "ws": 64, "C": 4096,
+                "W": 4, "block_size": 32, "gather": {"max_count": 512, "d_conv": 3,
+                                                     "real_count": self.real_count},
+                "activation": "silu", "residual": True, "graph": "hipGraph",
+                "replicas": self.R}
+
+    def oracle_sample(self, budget):
+        done, spent, i = 0, 0.0, 0
+        while i < self.R and (spent < budget or done == 0):
+            sub = sub_case(self.case, self.rows(i), slice(512 * i, 512 * (i + 1)),
+                           self.case.poison_block)
+            spent += time_oracle_fused(sub)
+            done += self.B
+            i += 1
+        return done / spent, f"fused conv of {i} whole spec batches ({done} tokens)", spent
+
+
+class SsmPrefillBench(Workload):
+    kernel_name = "varlen_fwd_kernel"
+
+    def __init__(self, dev="cuda"):
+        import torch
+
+        import depthwise_causal_conv1d_amd as lib
+        import workloads
+        self.lib = lib
+        t = time.time()
+        self.case = workloads.ssm_varlen()
+        c = self.case
+        log(f"ssm_prefill generated in {time.time() - t:.1f}s")
+        self.R = 1   # one step moves ~1.07 GB
+        self.x = c.x.to(dev)
+        self.out = torch.empty_like(self.x)
+        self.w, self.b = c.weight.to(dev), c.bias.to(dev)
+        self.st = c.conv_states.to(dev)
+        self.qsl = c.query_start_loc.to(dev)
+        self.ci = c.cache_indices.to(dev)
+        self.hi = c.has_initial_state.to(dev)
+        dim, T = c.x.shape
+        e = 2
+        n_init = int(c.has_initial_state.sum())
+        self.bytes_per_launch = (2 * dim * T + (n_init + 8) * dim * 3 + dim * 5) * e + 4 * 9
+        self.tokens_per_step = T
+
+    def kernel(self, i):
+        self.lib.causal_conv1d_varlen_fwd(self.x, self.w, self.b, self.st, self.qsl, self.ci,
+                                          self.hi, True, -1, out=self.out)
+
+    step = kernel
+
+    def config(self):
+        return {"workload": "ssm_prefill", "sequences": 8, "seq_len": 4096, "dim": 8192,
+                "W": 4, "layout": "channel-major", "state_slots": 1024, "with_state": 4,
+                "activation": "silu", "bias": True}
+
+    def oracle_sample(self, budget):
+        import oracle
+        from tests.helpers import to_np
+        c = self.case
+        # Two of the eight sequences (one with a state, one without).
+        keep = [int(torch_where(c.has_initial_state)[0]), int(torch_where(~c.has_initial_state)[0])]
+        L = 4096
+        xs = to_np(c.x)
+        import numpy as np
+        x2 = np.ascontiguousarray(np.concatenate([xs[:, k * L:(k + 1) * L] for k in keep], 1))
+        args = (x2, to_np(c.weight), to_np(c.bias), to_np(c.conv_states),
+                np.array([0, L, 2 * L], np.int32), to_np(c.cache_indices)[keep],
+                to_np(c.has_initial_state)[keep], "silu", -1)
+        t0 = time.perf_counter()
+        oracle.causal_conv1d_varlen_fwd(*args)
+        spent = time.perf_counter() - t0
+        return 2 * L / spent, "2 of the 8 sequences (8192 tokens, all channels)", spent
+
+
+class SsmDecodeBench(Workload):
+    kernel_name = "update_kernel"
+
+    def __init__(self, dev="cuda"):
+        import torch
+
+        import depthwise_causal_conv1d_amd as lib
+        import workloads
+        self.lib = lib
+        c = workloads.ssm_varlen()
+        self.case = c
+        xs = workloads.update_inputs(3, 64, 8, 8192)
+        self.R = 64
+        self.x = torch.stack(xs).to(dev)
+        self.out = torch.empty_like(self.x)
+        self.w, self.b = c.weight.to(dev), c.bias.to(dev)
+        self.st = c.conv_states.to(dev)
+        self.ci = c.cache_indices.to(dev)
+        self.bytes_per_launch = (8 * 8192 * 2 + 8 * 8192 * 3 * 2) * 2 + 8192 * 5 * 2 + 32
+        self.tokens_per_step = 8
+
+    def kernel(self, i):
+        self.lib.causal_conv1d_update(self.x[i], self.st, self.w, self.b, True, None, self.ci, -1,
+                                      out=self.out[i])
+
+    step = kernel
+
+    def config(self):
+        return {"workload": "ssm_decode", "batch": 8, "dim": 8192, "W": 4,
+                "state_slots": 1024, "activation": "silu", "bias": True,
+                "graph": "hipGraph", "steps_per_graph": 64}
+
+    def oracle_sample(self, budget):
+        import oracle
+        from tests.helpers import to_np
+        c = self.case
+        st = to_np(c.conv_states)
+        x = to_np(self.x[0])
+        t0 = time.perf_counter()
+        oracle.causal_conv1d_update(x, st, to_np(c.weight), to_np(c.bias), "silu",
+                                    to_np(c.cache_indices), -1)
+        spent = time.perf_counter() - t0
+        return 8 / spent, "one decode step (8 rows)", spent
+
+
+def torch_where(mask):
+    import torch
+    return torch.nonzero(mask).flatten()
+
+
+WORKLOADS = {
+    "batched_decode": DecodeBench,
+    "mixed_prefill": MixedPrefillBench,
+    "spec_decode": SpecDecodeBench,
+    "ssm_prefill": SsmPrefillBench,
+    "ssm_decode": SsmDecodeBench,
+}
+
+DEFAULT_STEPS = {"batched_decode": 19200, "mixed_prefill": 200, "spec_decode": 2000,
+                 "ssm_prefill": 200, "ssm_decode": 6400}
+
+
+# ---------------------------------------------------------------- timing
+
+def capture(fn, indices):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in indices:
+            fn(i)
+    return g
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="batched_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time for the CPU baseline (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the op shards per request or per head with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]()
+    R = wl.R
+    K = args.steps if args.steps is not None else DEFAULT_STEPS[args.workload]
+    Wm = args.warmup if args.warmup is not None else max(R, K // 50)
+
+    # Touch every replica once eagerly, then capture on a side stream.
+    for i in range(R):
+        wl.step(i)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g_all = capture(wl.step, range(R))
+        rem = K % R
+        g_rem = capture(wl.step, range(rem)) if rem else None
+        g_kern = capture(wl.kernel, range(R))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def run_steps(n):
+        for _ in range(n // R):
+            g_all.replay()
+        if n % R:
+            g_rem.replay()
+
+    run_steps(Wm - Wm % R if Wm >= R else R)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(K)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # Average duration of one launch of the dominant kernel: graphs holding
+    # only that kernel (R calls per replay), bracketed by HIP events on the
+    # stream the kernels run on.
+    reps = max(3, min(200, K // R))
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(reps):
+        g_kern.replay()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    launches = reps * R * wl.kernels_per_call()
+    kern_us = k0.elapsed_time(k1) * 1e3 / launches
+    achieved = wl.bytes_per_launch / (kern_us * 1e-6) / 1e9
+
+    cpu = None
+    if args.cpu_budget > 0:
+        v, sample, spent = wl.oracle_sample(args.cpu_budget)
+        cpu = {"value": round(v, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{sample}; {spent:.1f} s single-threaded"}
+
+    traffic = stored_traffic(args.workload)
+    value = wl.tokens_per_step * K / wall
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(wall * 1e3 / K, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": wl.config(),
+        "roofline": {"bound": wl.bound, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": wl.kernel_name,
+                     "bytes_per_launch": wl.bytes_per_launch, "launch_us": round(kern_us, 3)},
+        "cpu_baseline": cpu,
+        "kernel_sources": kernel_source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
