@@ -21,6 +21,14 @@
 
 namespace sconv {
 
+// Build-time tuning knobs (defaults chosen by measurement on MI355X).
+#ifndef SCONV_VARLEN_GROUP
+#define SCONV_VARLEN_GROUP 4       // chunks loaded together per wave
+#endif
+#ifndef SCONV_VARLEN_NT_STORES
+#define SCONV_VARLEN_NT_STORES 1   // streaming stores of the outputs
+#endif
+
 struct VarlenParams {
   const void* x;
   const void* w;
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(const VarlenParams p) {
 #pragma unroll
   for (int m = 0; m < SA; ++m) {
     const int64_t i = L - SL + m;  // logical index, >= -SL
-    fin[m] = (m < SL) ? (i >= 0 ? xrow[(start + i) * p.x_st] : sraw[m < SL ? SL + i : 0]) : (S)0;
+    fin[m] = (m < SL) ? (i >= 0 ? xrow[(start + i) * p.x_st] : pick(sraw, (int)(SL + i))) : (S)0;
   }
 
   S* orow = out + (int64_t)c * p.o_sc;
@@ -125,65 +133,89 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(const VarlenParams p) {
 #pragma unroll
   for (int m = 0; m < SA; ++m) {
     const int64_t i = base - start - SL + m;  // < 0
-    carry[m] = (m < SL && i >= -SL) ? s0[SL + i] : 0.f;
+    carry[m] = (m < SL && i >= -SL) ? pick(s0, (int)(SL + i)) : 0.f;
   }
 
-  P nxt = load_span<D, VEC>(xrow, p.x_st, base + lane * VEC, start, end);
-  for (; base < end; base += kChunk) {
-    const P cur = nxt;
-    if (base + kChunk < end)
-      nxt = load_span<D, VEC>(xrow, p.x_st, base + kChunk + lane * VEC, start, end);
-    const int64_t tk = base + lane * VEC;
-    float f[VEC];
-    cur.to_float(f);
+  // Chunks are processed in groups of G; the next group's loads are issued
+  // before the current group is computed, so up to 2G chunks are in flight.
+  constexpr int G = SCONV_VARLEN_GROUP;
+  P buf[G];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int64_t i = tk + e - start;
-      if (i < 0) f[e] = (i >= -SL) ? s0[SL + i] : 0.f;
+  for (int u = 0; u < G; ++u)
+    buf[u] = load_span<D, VEC>(xrow, p.x_st, base + u * kChunk + lane * VEC, start, end);
+  for (; base < end; base += G * kChunk) {
+    P cur[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) cur[u] = buf[u];
+    if (base + G * kChunk < end) {
+#pragma unroll
+      for (int u = 0; u < G; ++u)
+        buf[u] = load_span<D, VEC>(xrow, p.x_st, base + (G + u) * kChunk + lane * VEC, start, end);
     }
-    // prev[m]: input at token tk - SL + m.
-    float prev[SA];
 #pragma unroll
-    for (int m = 0; m < SL; ++m) {
-      const int d = SL - m;
-      if constexpr (VEC == 1) {
-        const float v = lane_shift_up(f[0], d);
-        prev[m] = lane >= d ? v : carry[SL + lane - d < 0 ? 0 : SL + lane - d];
-      } else {
-        const float v = lane_shift_up(f[VEC - d], 1);
-        prev[m] = lane >= 1 ? v : carry[m];
-      }
-    }
-    if (SL == 0) prev[0] = 0.f;
-    // Carry for the next chunk: the last SL inputs of this one.
-#pragma unroll
-    for (int m = 0; m < SL; ++m) {
-      if constexpr (VEC == 1) carry[m] = read_lane63(lane_shift_up(f[0], SL - 1 - m));
-      else carry[m] = read_lane63(f[VEC - SL + m]);
-    }
-
-    float y[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float acc = bc;
-#pragma unroll
-      for (int k = 0; k < W; ++k) {
-        const int o = e - SL + k;  // offset from tk
-        const float v = o >= 0 ? f[o < 0 ? 0 : o] : prev[SL + o < 0 ? 0 : SL + o];
-        acc = __builtin_fmaf(wk[k], v, acc);
-      }
-      y[e] = p.silu ? silu(acc) : acc;
-    }
-    P o;
-    o.from_float(y);
-    if (tk >= start && tk + VEC <= end) {
-      if constexpr (VEC > 1) o.store(orow + tk); else o.store(orow + tk * p.o_st);
-    } else {
-      typename P::Elems v = __builtin_bit_cast(typename P::Elems, o.raw);
+    for (int u = 0; u < G; ++u) {
+      const int64_t cb = base + u * kChunk;
+      if (cb >= end) break;
+      const int64_t tk = cb + lane * VEC;
+      float f[VEC];
+      cur[u].to_float(f);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const int64_t tok = tk + e;
-        if (tok >= start && tok < end) orow[tok * p.o_st] = v.e[e];
+        const int64_t i = tk + e - start;
+        if (i < 0) f[e] = (i >= -SL) ? pick(s0, (int)(SL + i)) : 0.f;
+      }
+      // prev[m]: input at token tk - SL + m.
+      float prev[SA];
+#pragma unroll
+      for (int m = 0; m < SL; ++m) {
+        const int d = SL - m;
+        if constexpr (VEC == 1) {
+          const float v = lane_shift_up(f[0], d);
+          prev[m] = lane >= d ? v : pick(carry, SL + lane - d);
+        } else {
+          const float v = lane_shift_up(f[VEC - d], 1);
+          prev[m] = lane >= 1 ? v : carry[m];
+        }
+      }
+      if (SL == 0) prev[0] = 0.f;
+      // Carry for the next chunk: the last SL inputs of this one.
+#pragma unroll
+      for (int m = 0; m < SL; ++m) {
+        if constexpr (VEC == 1) carry[m] = read_lane63(lane_shift_up(f[0], SL - 1 - m));
+        else carry[m] = read_lane63(f[VEC - SL + m]);
+      }
+
+      float y[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float acc = bc;
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          const int o = e - SL + k;  // offset from tk
+          const float v = o >= 0 ? f[o < 0 ? 0 : o] : prev[SL + o < 0 ? 0 : SL + o];
+          acc = __builtin_fmaf(wk[k], v, acc);
+        }
+        y[e] = p.silu ? silu(acc) : acc;
+      }
+      P o;
+      o.from_float(y);
+      if (tk >= start && tk + VEC <= end) {
+        if constexpr (VEC > 1) {
+#if SCONV_VARLEN_NT_STORES
+          o.store_nt(orow + tk);
+#else
+          o.store(orow + tk);
+#endif
+        } else {
+          o.store(orow + tk * p.o_st);
+        }
+      } else {
+        typename P::Elems v = __builtin_bit_cast(typename P::Elems, o.raw);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int64_t tok = tk + e;
+          if (tok >= start && tok < end) orow[tok * p.o_st] = v.e[e];
+        }
       }
     }
   }

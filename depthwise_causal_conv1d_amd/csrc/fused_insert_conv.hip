@@ -43,11 +43,31 @@ struct FusedParams {
   void* out;
   int64_t x_rs, w_sc, w_sk, cs0, cs1, cs2, bt_rs, out_rs, T;
   int64_t num_tiles;
-  int32_t C, ws, off_s, N, log2N, num_slabs;
+  int32_t C, ws, off_s, N, num_slabs;
+  // Division by N of non-negative 32-bit positions and slots: a shift when
+  // N is a power of two (n_shift >= 0), else multiply-high by a magic
+  // number (Granlund & Montgomery, round-up variant; exact for all uint32).
+  int32_t n_shift;
+  uint32_t n_magic, n_magic_shift;
   int32_t silu, residual, w_packed;
 };
 
-enum TapKind { kZero = 0, kXRow = 1, kCache = 2 };
+__device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
+  if (p.n_shift >= 0) return v >> p.n_shift;
+  const uint32_t t = __umulhi(v, p.n_magic);
+  return (t + ((v - t) >> 1)) >> p.n_magic_shift;
+}
+
+// Build-time tuning knobs (defaults chosen by measurement on MI355X).
+#ifndef SCONV_FUSED_BT_MAX
+#define SCONV_FUSED_BT_MAX 8       // largest rows-per-wave tile
+#endif
+#ifndef SCONV_FUSED_NT_STORES
+#define SCONV_FUSED_NT_STORES 1    // streaming (non-temporal) out / cache stores
+#endif
+#ifndef SCONV_FUSED_ENOUGH_WAVES
+#define SCONV_FUSED_ENOUGH_WAVES 4096
+#endif
 
 template <typename D, int VEC, int W, int BT>
 __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParams p) {
@@ -113,15 +133,17 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   // Per-row metadata (scalar) and the tile's input rows.
   const int64_t t0 = tile * BT;
   const bool full = t0 + BT <= p.T;
-  int64_t pos[BT], slot[BT];
-  int32_t req[BT], qs[BT];
+  // Positions and slots are below max_blocks*N and num_blocks*N, both
+  // checked on the host to fit in 31 bits; a negative 64-bit slot is PAD.
+  int32_t pos[BT], slot[BT], req[BT], qs[BT];
   P xr[BT];
 #pragma unroll
   for (int i = 0; i < BT; ++i) {
     const int64_t t = t0 + i;
     if (full || t < p.T) {
-      pos[i] = positions[t];
-      slot[i] = slots[t];
+      pos[i] = (int32_t)positions[t];
+      const int64_t s64 = slots[t];
+      slot[i] = s64 < 0 ? -1 : (int32_t)s64;
       req[i] = seq_idx[t];
       qs[i] = qstart[t];
       if (on) xr[i].load(x + t * p.x_rs + c0); else xr[i].zero();
@@ -149,64 +171,104 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     if (need && on) halo[m - 1].load(x + (t0 - m) * p.x_rs + c0); else halo[m - 1].zero();
   }
 
-  const bool pow2 = p.log2N >= 0;
+  // History rows 1..W-1 of the current request, in named registers (an
+  // array indexed by a run-time value would be demoted to LDS).
+  P hist1, hist2, hist3;
+  hist1.zero();
+  hist2.zero();
+  hist3.zero();
+  int32_t hist_req = -1;  // request whose history rows are held
 #pragma unroll
   for (int i = 0; i < BT; ++i) {
     if (slot[i] < 0) continue;  // PAD (or past T): no output, no insert
     const int64_t t = t0 + i;
 
-    // Where each earlier tap comes from; block ids of pre-forward taps.
-    int kind[kHalo];
-    int64_t cblk[kHalo], coff[kHalo];
+    // Pre-forward taps of a row are its request's history: the cache rows
+    // at positions first-1 .. first-(W-1), first = the request's first
+    // position in this call.  Rows of one request share them, so they are
+    // fetched once, by the request's first row in the tile (the one that
+    // needs the most of them), and kept in registers for the others.
+    const int32_t d = (int32_t)(t - qs[i]);  // row offset inside its request
+    if (d < W - 1 && req[i] != hist_req) {
+      const int32_t first = pos[i] - d;
+      int32_t hblk[kHalo], hoff[kHalo];
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) {
-      const int lag = W - 1 - k;
-      const int64_t src = pos[i] - lag;
-      kind[k] = src < 0 ? kZero : (t - lag >= (int64_t)qs[i] ? kXRow : kCache);
-      cblk[k] = 0;
-      coff[k] = 0;
-      if (kind[k] == kCache) {
-        const int64_t lb = pow2 ? (src >> p.log2N) : src / p.N;
-        coff[k] = src - lb * p.N;
-        cblk[k] = btab[(int64_t)req[i] * p.bt_rs + lb];
+      for (int m = 1; m <= W - 1; ++m) {
+        hblk[m - 1] = -1;
+        hoff[m - 1] = 0;
+        const int32_t src = first - m;
+        if (m <= W - 1 - d && src >= 0) {
+          const uint32_t lb = div_n((uint32_t)src, p);
+          hoff[m - 1] = src - (int32_t)lb * p.N;
+          hblk[m - 1] = btab[(int64_t)req[i] * p.bt_rs + lb];
+        }
       }
+      auto fetch = [&](int m, P& dst) {
+        if (hblk[m - 1] >= 0 && on)
+          dst.load(cache + (int64_t)hblk[m - 1] * p.cs0 + (int64_t)hoff[m - 1] * p.cs2 + lane_off);
+        else
+          dst.zero();
+      };
+      if constexpr (W > 1) fetch(1, hist1);
+      if constexpr (W > 2) fetch(2, hist2);
+      if constexpr (W > 3) fetch(3, hist3);
+      hist_req = req[i];
     }
 
-    float tap[W][VEC];
+    // Taps, oldest first: pick the raw 16 bytes (uniform choice), widen,
+    // accumulate in fp32.
+    float acc[VEC];
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) {
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
       const int lag = W - 1 - k;
-      if (kind[k] == kCache) {
-        P pk;
-        if (on) pk.load(cache + cblk[k] * p.cs0 + coff[k] * p.cs2 + lane_off); else pk.zero();
-        pk.to_float(tap[k]);
-      } else if (kind[k] == kXRow) {
-        if (i >= lag) xr[i - lag].to_float(tap[k]);
-        else halo[lag - i - 1].to_float(tap[k]);
+      P src;
+      if (lag == 0) {
+        src = xr[i];
+      } else if (pos[i] - lag < 0) {
+        src.zero();                                   // before position 0
+      } else if (lag <= d) {
+        src = i >= lag ? xr[i >= lag ? i - lag : 0]   // same forward: x row t-lag
+                       : halo[lag - i - 1 >= 0 ? lag - i - 1 : 0];
       } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) tap[k][e] = 0.f;
+        const int m = lag - d;                        // before this forward
+        if (m == 1) src = hist1;
+        else if (m == 2) src = hist2;
+        else src = hist3;
       }
+      float f[VEC];
+      src.to_float(f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(wk[k][e], f[e], acc[e]);
     }
-    xr[i].to_float(tap[W - 1]);
-
     float y[VEC];
+    {
+      float cur[VEC];
+      xr[i].to_float(cur);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < W; ++k) acc = __builtin_fmaf(wk[k][e], tap[k][e], acc);
-      if (p.silu) acc = silu(acc);
-      if (p.residual) acc += tap[W - 1][e];
-      y[e] = acc;
+      for (int e = 0; e < VEC; ++e) {
+        float v = acc[e];
+        if (p.silu) v = silu(v);
+        if (p.residual) v += cur[e];
+        y[e] = v;
+      }
     }
     if (on) {
       P o;
       o.from_float(y);
+#if SCONV_FUSED_NT_STORES
+      o.store_nt(out + t * p.out_rs + c0);
+#else
       o.store(out + t * p.out_rs + c0);
-      const int64_t s = slot[i];
-      const int64_t blk = pow2 ? (s >> p.log2N) : s / p.N;
-      xr[i].store(cache + blk * p.cs0 + (s - blk * p.N) * p.cs2 + lane_off);
+#endif
+      const uint32_t blk = div_n((uint32_t)slot[i], p);
+      const int32_t off = slot[i] - (int32_t)blk * p.N;
+#if SCONV_FUSED_NT_STORES
+      xr[i].store_nt(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
+#else
+      xr[i].store(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
+#endif
     }
   }
 }
@@ -223,6 +285,7 @@ template <typename D, int VEC, int W>
 static void launch_bt(int bt, const FusedParams& p, uint32_t g, uint32_t th, hipStream_t s) {
   switch (bt) {
     case 16: launch<D, VEC, W, 16>(p, g, th, s); break;
+    case 8: launch<D, VEC, W, 8>(p, g, th, s); break;
     case 4: launch<D, VEC, W, 4>(p, g, th, s); break;
     default: launch<D, VEC, W, 1>(p, g, th, s); break;
   }
@@ -238,12 +301,14 @@ static void launch_w(int W, int bt, const FusedParams& p, uint32_t g, uint32_t t
   }
 }
 
-// Tokens per wave: the largest of {16, 4, 1} that still yields enough
-// waves to cover the chip (256 CUs x 4 SIMDs, two waves each).
+// Rows per wave: the largest tile (up to SCONV_FUSED_BT_MAX) that still
+// yields enough waves to keep every SIMD of the 256 CUs busy several times
+// over; small batches fall back to one row per wave for parallelism.
 static int pick_bt(int64_t T, int64_t slabs) {
-  const int64_t kEnough = 2048;
-  if (cdiv(T, 16) * slabs >= kEnough) return 16;
-  if (cdiv(T, 4) * slabs >= kEnough) return 4;
+  const int64_t kEnough = SCONV_FUSED_ENOUGH_WAVES;
+  if (SCONV_FUSED_BT_MAX >= 16 && cdiv(T, 16) * slabs >= kEnough) return 16;
+  if (SCONV_FUSED_BT_MAX >= 8 && cdiv(T, 8) * slabs >= kEnough) return 8;
+  if (SCONV_FUSED_BT_MAX >= 4 && cdiv(T, 4) * slabs >= kEnough) return 4;
   return 1;
 }
 
@@ -274,6 +339,9 @@ extern "C" int sconv_fused_insert_conv(
   if (C > INT32_MAX / 2) return fail(SCONV_ERR_UNSUPPORTED, "%s: C too large", fn);
   if (x_row_stride < C || out_row_stride < C)
     return fail(SCONV_ERR_INVALID, "%s: row strides must be >= C=%lld", fn, (long long)C);
+  if ((int64_t)num_blocks * N > INT32_MAX || (int64_t)max_blocks * N > INT32_MAX)
+    return fail(SCONV_ERR_UNSUPPORTED, "%s: more than 2^31 cache slots or positions", fn);
+  if (T > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: T above 2^31", fn);
   if (cs2 < D || cs1 < 1 || cs0 < 1 || bt_row_stride < max_blocks || w_stride_c < 1 ||
       w_stride_k < 1)
     return fail(SCONV_ERR_INVALID, "%s: cache / block-table / weight strides too small", fn);
@@ -302,7 +370,16 @@ extern "C" int sconv_fused_insert_conv(
   p.cs0 = cs0; p.cs1 = cs1; p.cs2 = cs2; p.bt_rs = bt_row_stride; p.out_rs = out_row_stride;
   p.T = T;
   p.C = (int32_t)C; p.ws = ws; p.off_s = off_s; p.N = N;
-  p.log2N = (N & (N - 1)) == 0 ? __builtin_ctz((unsigned)N) : -1;
+  if ((N & (N - 1)) == 0) {
+    p.n_shift = __builtin_ctz((unsigned)N);
+    p.n_magic = 0;
+    p.n_magic_shift = 0;
+  } else {
+    const uint32_t l = 32 - __builtin_clz((unsigned)(N - 1));  // ceil(log2 N)
+    p.n_shift = -1;
+    p.n_magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - N)) / N + 1);
+    p.n_magic_shift = l - 1;
+  }
   p.num_slabs = (int32_t)cdiv(C, 64 * VEC);
   const int bt = pick_bt(T, p.num_slabs);
   p.num_tiles = cdiv(T, bt);

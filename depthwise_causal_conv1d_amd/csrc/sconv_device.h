@@ -48,6 +48,10 @@ struct Pack {
   __device__ __forceinline__ void store(S* p) const {
     *reinterpret_cast<raw_t*>(p) = raw;
   }
+  // Streaming store: nothing will read these bytes again in this kernel.
+  __device__ __forceinline__ void store_nt(S* p) const {
+    __builtin_nontemporal_store(raw, reinterpret_cast<raw_t*>(p));
+  }
   __device__ __forceinline__ void zero() { raw = raw_t{}; }
 
   __device__ __forceinline__ void to_float(float (&f)[VEC]) const {
@@ -101,6 +105,18 @@ __device__ __forceinline__ float load_as_float(const typename D::storage* p) {
 // v -> -inf gives -0 (or NaN at -inf itself, as the definition does).
 __device__ __forceinline__ float silu(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+}
+
+// a[idx] for a run-time idx in [0, N), as a chain of selects over constant
+// indices: an array indexed by a run-time value would be demoted to scratch
+// or LDS memory.
+template <typename T, int N>
+__device__ __forceinline__ T pick(const T (&a)[N], int idx) {
+  T r = a[0];
+#pragma unroll
+  for (int q = 1; q < N; ++q)
+    if (idx == q) r = a[q];
+  return r;
 }
 
 // ---------------------------------------------------------------- launch order
