@@ -483,6 +483,9 @@ def main():
     ap.add_argument("--workload", default="batched_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the CPU baseline (0: skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -493,6 +496,16 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        evict = torch.empty(4 * n, dtype=torch.uint8, device="cuda").fill_(2)  # push src out of L2/MALL
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read, {n} bytes written")
+        del src, dst, evict
     wl = WORKLOADS[args.workload]()
     R = wl.R
     K = args.steps if args.steps is not None else DEFAULT_STEPS[args.workload]
