@@ -166,24 +166,22 @@ class Workload:
 
 
 class DecodeBench(Workload):
-    """R independent decode batches of 256 requests sharing one large cache."""
+    """R independent decode batches of B requests sharing one large cache."""
 
-    B = 256
-
-    def __init__(self, dev="cuda"):
+    def __init__(self, dev="cuda", requests: int = 256):
         import torch
 
         import depthwise_causal_conv1d_amd as lib
         import workloads
         self.lib = lib
-        B = self.B
-        probe = 3_161_224  # algorithmic bytes of one batch (checked below)
-        self.R = max(2, -(-FLUSH_BYTES // probe) + 16)
+        self.B = B = requests
+        per_batch = B * 12_350  # ~algorithmic bytes of one batch (exact value below)
+        self.R = max(2, -(-FLUSH_BYTES // per_batch) + 16 * (B <= 256))
         t = time.time()
         self.case = workloads.batched_decode(device=dev, num_reqs=B * self.R,
                                              pool_blocks=int(B * self.R * 2 * 1.25) + 1)
         c = self.case
-        log(f"batched_decode: {self.R} batches in {time.time() - t:.1f}s, cache "
+        log(f"batched_decode: {self.R} batches of {B} in {time.time() - t:.1f}s, cache "
             f"{c.cache.numel() * c.cache.element_size() / 2**30:.1f} GiB")
         self.x, self.w, self.cache = c.x.to(dev), c.weight.to(dev), c.cache
         self.pos, self.sm, self.bt = c.positions.to(dev), c.slot_mapping.to(dev), c.block_table.to(dev)
@@ -208,19 +206,22 @@ class DecodeBench(Workload):
         self.kernel(i)
 
     def config(self):
-        return {"workload": "batched_decode", "requests": 256, "tokens_per_step": 256,
+        return {"workload": "batched_decode", "requests": self.B, "tokens_per_step": self.B,
                 "history": "uniform[1,4096]", "H": 32, "D": 128, "ws": 32, "C": 1024,
                 "W": 4, "block_size": 16, "activation": "silu", "residual": True,
                 "graph": "hipGraph", "replicas": self.R}
 
     def oracle_sample(self, budget):
+        # Whole sub-batches of 256 requests, until the budget is spent.
         done, spent, i = 0, 0.0, 0
-        while i < self.R and (spent < budget or done == 0):
-            sub = sub_case(self.case, self.rows(i), self.rows(i), self.case.poison_block)
+        n_sub = self.R * self.B // 256
+        while i < n_sub and (spent < budget or done == 0):
+            rows = slice(256 * i, 256 * (i + 1))
+            sub = sub_case(self.case, rows, rows, self.case.poison_block)
             spent += time_oracle_fused(sub)
-            done += self.B
+            done += 256
             i += 1
-        return done / spent, f"{i} whole decode batches ({done} tokens)", spent
+        return done / spent, f"{i} decode sub-batches of 256 requests ({done} tokens)", spent
 
 
 class MixedPrefillBench(Workload):
@@ -483,6 +484,8 @@ def main():
     ap.add_argument("--workload", default="batched_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the CPU baseline (0: skip)")
+    ap.add_argument("--requests", type=int, default=256,
+                    help="batched_decode only: requests per decode batch (batch-size sweep)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "reference for hardware byte counters)")
@@ -506,7 +509,10 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: {n} bytes read, {n} bytes written")
         del src, dst, evict
-    wl = WORKLOADS[args.workload]()
+    if args.workload == "batched_decode":
+        wl = DecodeBench(requests=args.requests)
+    else:
+        wl = WORKLOADS[args.workload]()
     R = wl.R
     K = args.steps if args.steps is not None else DEFAULT_STEPS[args.workload]
     Wm = args.warmup if args.warmup is not None else max(R, K // 50)
