@@ -168,12 +168,13 @@ class Workload:
 class DecodeBench(Workload):
     """R independent decode batches of B requests sharing one large cache."""
 
-    def __init__(self, dev="cuda", requests: int = 256):
+    def __init__(self, dev="cuda", requests: int = 256, fold: bool = False):
         import torch
 
         import depthwise_causal_conv1d_amd as lib
         import workloads
         self.lib = lib
+        self.fold = fold
         self.B = B = requests
         per_batch = B * 12_350  # ~algorithmic bytes of one batch (exact value below)
         self.R = max(2, -(-FLUSH_BYTES // per_batch) + 16 * (B <= 256))
@@ -197,16 +198,24 @@ class DecodeBench(Workload):
 
     def kernel(self, i):
         s, c = self.rows(i), self.case
+        if self.fold:
+            self.lib.sconv_fused_insert_conv_qsl(self.x[s], self.w, self.cache, self.pos[s],
+                                                 self.bt[s], self.qsl, self.B, self.sm[s],
+                                                 c.off_s, c.ws, c.block_size, "silu", True,
+                                                 out=self.out[s])
+            return
         self.lib.sconv_fused_insert_conv(self.x[s], self.w, self.cache, self.pos[s], self.bt[s],
                                          self.si, self.sm[s], self.qs, c.off_s, c.ws,
                                          c.block_size, "silu", True, out=self.out[s])
 
     def step(self, i):
-        self.lib.sconv_seq_metadata(self.qsl, self.B, self.B, self.si, self.qs, self.B)
+        if not self.fold:
+            self.lib.sconv_seq_metadata(self.qsl, self.B, self.B, self.si, self.qs, self.B)
         self.kernel(i)
 
     def config(self):
         return {"workload": "batched_decode", "requests": self.B, "tokens_per_step": self.B,
+                "metadata": "folded into the fused launch" if self.fold else "separate launch",
                 "history": "uniform[1,4096]", "H": 32, "D": 128, "ws": 32, "C": 1024,
                 "W": 4, "block_size": 16, "activation": "silu", "residual": True,
                 "graph": "hipGraph", "replicas": self.R}
@@ -227,12 +236,13 @@ class DecodeBench(Workload):
 class MixedPrefillBench(Workload):
     """Four streams of one layer convolved in turn over one shared cache."""
 
-    def __init__(self, dev="cuda"):
+    def __init__(self, dev="cuda", fold: bool = False):
         import torch
 
         import depthwise_causal_conv1d_amd as lib
         import workloads
         self.lib = lib
+        self.fold = fold
         t = time.time()
         self.streams = workloads.mixed_prefill_streams()
         b = self.streams[0]
@@ -253,6 +263,12 @@ class MixedPrefillBench(Workload):
     def kernel(self, i):
         b = self.streams[0]
         for s, st in enumerate(self.streams):
+            if self.fold:
+                self.lib.sconv_fused_insert_conv_qsl(self.xs[s], self.ws_[s], self.cache, self.pos,
+                                                     self.bt, self.qsl, b.num_reqs, self.sm,
+                                                     st.off_s, st.ws, b.block_size, "silu", True,
+                                                     out=self.outs[s])
+                continue
             self.lib.sconv_fused_insert_conv(self.xs[s], self.ws_[s], self.cache, self.pos, self.bt,
                                              self.si, self.sm, self.qs, st.off_s, st.ws,
                                              b.block_size, "silu", True, out=self.outs[s])
@@ -262,12 +278,14 @@ class MixedPrefillBench(Workload):
 
     def step(self, i):
         b = self.streams[0]
-        self.lib.sconv_seq_metadata(self.qsl, b.num_reqs, b.num_actual, self.si, self.qs, b.T)
+        if not self.fold:
+            self.lib.sconv_seq_metadata(self.qsl, b.num_reqs, b.num_actual, self.si, self.qs, b.T)
         self.kernel(i)
 
     def config(self):
         b = self.streams[0]
         return {"workload": "mixed_prefill", "requests": 16, "rows": b.T,
+                "metadata": "folded into the fused launches" if self.fold else "separate launch",
                 "non_pad_tokens": self.live, "streams": 4, "H": 32, "D": 512, "ws": 128,
                 "C": 4096, "W": 4, "block_size": 16, "pad_fraction": 0.1,
                 "activation": "silu", "residual": True}
@@ -283,12 +301,13 @@ class SpecDecodeBench(Workload):
 
     B = 2048
 
-    def __init__(self, dev="cuda"):
+    def __init__(self, dev="cuda", fold: bool = False):
         import torch
 
         import depthwise_causal_conv1d_amd as lib
         import workloads
         self.lib = lib
+        self.fold = fold
         first = workloads.spec_decode()
         self.bytes_per_launch = fused_algorithmic_bytes(first)
         self.R = max(2, -(-FLUSH_BYTES // self.bytes_per_launch) + 2)
@@ -316,19 +335,26 @@ class SpecDecodeBench(Workload):
 
     def kernel(self, i):
         s, c = self.rows(i), self.case
-        self.lib.sconv_fused_insert_conv(self.x[s], self.w, self.cache, self.pos[s],
-                                         self.bt[512 * i:512 * (i + 1)], self.si, self.sm[s],
-                                         self.qs, c.off_s, c.ws, c.block_size, "silu", True,
-                                         out=self.out[s])
+        bt = self.bt[512 * i:512 * (i + 1)]
+        if self.fold:
+            self.lib.sconv_fused_insert_conv_qsl(self.x[s], self.w, self.cache, self.pos[s], bt,
+                                                 self.qsl, 512, self.sm[s], c.off_s, c.ws,
+                                                 c.block_size, "silu", True, out=self.out[s])
+            return
+        self.lib.sconv_fused_insert_conv(self.x[s], self.w, self.cache, self.pos[s], bt, self.si,
+                                         self.sm[s], self.qs, c.off_s, c.ws, c.block_size, "silu",
+                                         True, out=self.out[s])
 
     def step(self, i):
-        self.lib.sconv_seq_metadata(self.qsl, 512, self.B, self.si, self.qs, self.B)
+        if not self.fold:
+            self.lib.sconv_seq_metadata(self.qsl, 512, self.B, self.si, self.qs, self.B)
         self.kernel(i)
         self.lib.gather_intermediate_conv_window(self.x[self.rows(i)].view(1, self.B, -1),
                                                  self.gpos, self.rc, self.gout[i], 3)
 
     def config(self):
         return {"workload": "spec_decode", "requests": 512, "drafts": 4, "tokens_per_step": 2048,
+                "metadata": "folded into the fused launch" if self.fold else "separate launch",
                 "positions": "uniform[1,131072)", "H": 64, "D": 64, "ws": 64, "C": 4096,
                 "W": 4, "block_size": 32, "gather": {"max_count": 512, "d_conv": 3,
                                                      "real_count": self.real_count},
@@ -484,6 +510,9 @@ def main():
     ap.add_argument("--workload", default="batched_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the CPU baseline (0: skip)")
+    ap.add_argument("--metadata", choices=("separate", "folded"), default="separate",
+                    help="per-row request search: its own sconv_seq_metadata launch per step, "
+                         "or inside the fused launch (sconv_fused_insert_conv_qsl)")
     ap.add_argument("--requests", type=int, default=256,
                     help="batched_decode only: requests per decode batch (batch-size sweep)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -509,8 +538,11 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: {n} bytes read, {n} bytes written")
         del src, dst, evict
+    fold = args.metadata == "folded"
     if args.workload == "batched_decode":
-        wl = DecodeBench(requests=args.requests)
+        wl = DecodeBench(requests=args.requests, fold=fold)
+    elif args.workload in ("mixed_prefill", "spec_decode"):
+        wl = WORKLOADS[args.workload](fold=fold)
     else:
         wl = WORKLOADS[args.workload]()
     R = wl.R

@@ -11,6 +11,7 @@ from .ops import (
     causal_conv1d_varlen_fwd,
     gather_intermediate_conv_window,
     sconv_fused_insert_conv,
+    sconv_fused_insert_conv_qsl,
     sconv_seq_metadata,
 )
 
@@ -22,5 +23,6 @@ __all__ = [
     "causal_conv1d_varlen_fwd",
     "gather_intermediate_conv_window",
     "sconv_fused_insert_conv",
+    "sconv_fused_insert_conv_qsl",
     "sconv_seq_metadata",
 ]

@@ -24,6 +24,7 @@ EXPORTS = (
     "sconv_version",
     "sconv_seq_metadata",
     "sconv_fused_insert_conv",
+    "sconv_fused_insert_conv_qsl",
     "causal_conv1d_varlen_fwd",
     "causal_conv1d_update",
     "gather_intermediate_conv_window",
@@ -38,6 +39,9 @@ _SIGS = {
     "sconv_fused_insert_conv": [P, I64, P, I64, I64, P, I64, I32, I32, I32, I64, I64, I64,
                                 P, P, I64, I32, P, P, P, P, I64, I64, I32, I32, I32, I32,
                                 I32, I32, P],
+    "sconv_fused_insert_conv_qsl": [P, I64, P, I64, I64, P, I64, I32, I32, I32, I64, I64, I64,
+                                    P, P, I64, I32, P, I32, P, P, I64, I64, I32, I32, I32,
+                                    I32, I32, I32, P],
     "causal_conv1d_varlen_fwd": [P, I64, I64, P, I64, I64, P, P, I64, I64, I64, I64, P, I32,
                                  P, P, P, I64, I64, I32, I64, I32, I32, I32, I32, P],
     "causal_conv1d_update": [P, I64, P, I64, I64, I64, I64, P, I64, I64, P, P, P, P, I64,

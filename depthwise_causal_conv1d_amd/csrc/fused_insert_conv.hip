@@ -32,30 +32,60 @@
 namespace sconv {
 
 struct FusedParams {
+  // Small fields first: they are needed before anything else and then come
+  // in with the first scalar load of the parameters.
+  uint32_t num_groups;      // grid size in workgroups
+  int32_t waves_per_group;  // workgroup size / 64
+  int32_t num_slabs;
+  int32_t C, ws, off_s, N;
+  // Division by N of non-negative 32-bit positions and slots, branch-free:
+  // q = (t + ((v - t) >> n_s1)) >> n_s2 with t = mulhi(v, n_magic)
+  // (Granlund & Montgomery, round-up variant; exact for every uint32 v).
+  // N = 1: (0, 0, 0); N = 2^k: (1, 1, k-1); otherwise the magic number.
+  uint32_t n_magic, n_s1, n_s2;
+  int32_t silu, residual;
+  int32_t num_reqs;         // with qsl
+  int32_t qsl_in_lds;       // offsets staged in dynamic LDS (else searched in memory)
+  int32_t pad0;
   const void* x;
   const void* w;
   void* cache;
   const int64_t* positions;
   const int32_t* bt;
-  const int32_t* seq_idx;
+  const int32_t* seq_idx;   // per-row request (NULL: search qsl)
   const int64_t* slot;
-  const int32_t* qs;
+  const int32_t* qs;        // per-row request start (NULL: search qsl)
+  const int32_t* qsl;       // request row offsets [num_reqs + 1] (or NULL)
   void* out;
   int64_t x_rs, w_sc, w_sk, cs0, cs1, cs2, bt_rs, out_rs, T;
   int64_t num_tiles;
-  int32_t C, ws, off_s, N, num_slabs;
-  // Division by N of non-negative 32-bit positions and slots: a shift when
-  // N is a power of two (n_shift >= 0), else multiply-high by a magic
-  // number (Granlund & Montgomery, round-up variant; exact for all uint32).
-  int32_t n_shift;
-  uint32_t n_magic, n_magic_shift;
-  int32_t silu, residual, w_packed;
 };
 
+// Request of row t: the last r in [0, n) with off[r] <= t (rows past the
+// end clamp to the last request, empty requests never match; r = 0 if
+// off[0] > t).  A 64-way search: each round the 64 lanes probe 64 evenly
+// spaced offsets of the remaining span, and since the offsets are
+// non-decreasing the lanes that see off <= t form a prefix whose length
+// (ballot + popcount) names the sub-span to keep.  Two rounds cover 4096
+// requests.  `off` is LDS or global memory; the result is wave-uniform.
+template <typename Ptr>
+__device__ __forceinline__ int32_t find_request(Ptr off, int32_t n, int64_t t, int lane) {
+  int32_t base = 0, span = n;
+  while (span > 1) {
+    const int32_t stride = (span + 63) >> 6;
+    const int32_t probe = lane * stride;
+    const bool le = probe < span && (int64_t)off[base + (probe < span ? probe : 0)] <= t;
+    const int32_t k = (int32_t)__popcll(__ballot(le)) - 1;
+    if (k < 0) break;  // off[base] > t: only possible for base 0
+    base += k * stride;
+    span = (k * stride + stride <= span) ? stride : span - k * stride;
+  }
+  return uniform(base);
+}
+
 __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
-  if (p.n_shift >= 0) return v >> p.n_shift;
   const uint32_t t = __umulhi(v, p.n_magic);
-  return (t + ((v - t) >> 1)) >> p.n_magic_shift;
+  return (t + ((v - t) >> p.n_s1)) >> p.n_s2;
 }
 
 // Build-time tuning knobs (defaults chosen by measurement on MI355X).
@@ -69,7 +99,9 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_ENOUGH_WAVES 4096
 #endif
 
-template <typename D, int VEC, int W, int BT>
+// QSL: rows find their request in the offsets p.qsl inside the kernel
+// (otherwise they read the per-row seq_idx / query_start buffers).
+template <typename D, int VEC, int W, int BT, bool QSL>
 __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParams p) {
   using S = typename D::storage;
   using P = Pack<D, VEC>;
@@ -84,77 +116,138 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   const int32_t* __restrict__ btab = p.bt;
 
   const int lane = threadIdx.x & 63;
-  const int waves_per_group = blockDim.x >> 6;
-  const int64_t wave = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * waves_per_group +
-                       uniform(threadIdx.x >> 6);
-  if (wave >= p.num_tiles * p.num_slabs) return;
-  const int64_t tile = wave / p.num_slabs;
-  const int slab = (int)(wave - tile * p.num_slabs);
+  // The launch geometry comes in the parameters (loaded with them in one
+  // batch) rather than from the implicit arguments, which would cost a
+  // second dependent round trip before any data load could start.
+  // Wave counts are below 2^31 (checked on the host): 32-bit arithmetic.
+  uint32_t wave = xcd_contiguous(blockIdx.x, p.num_groups) * (uint32_t)p.waves_per_group +
+                  (uint32_t)uniform(threadIdx.x >> 6);
+  // A wave past the end works on the last tile and writes nothing (no early
+  // return: it would also split the parameter loads around the branch, and
+  // with offsets staged in LDS every wave must reach the barrier).
+  const uint32_t total_waves = (uint32_t)p.num_tiles * (uint32_t)p.num_slabs;
+  const bool live_wave = wave < total_waves;
+  if (!live_wave) wave = total_waves - 1;
+  const uint32_t tile = wave / (uint32_t)p.num_slabs;
+  const int slab = (int)(wave - tile * (uint32_t)p.num_slabs);
+  const int64_t t0 = (int64_t)tile * BT;
 
-  // This lane's channels c0 .. c0+VEC-1 lie in one head (ws % VEC == 0).
-  const int c0 = (slab * 64 + lane) * VEC;
+  // Row metadata of the whole tile in one gather: lane L loads field L % F
+  // of row t0 + L / F (position, slot low and high words, and without QSL
+  // the request index and request start), then every value is broadcast to
+  // scalar registers.  One instruction cannot be split or sunk below the
+  // PAD tests, so the whole tile's metadata costs one round trip.
+  // Every load below is unconditional, from an address clamped into the
+  // buffers (rows past T, lanes past C): a conditional load would join its
+  // value with a default and force an immediate wait for it.
+  const int64_t t_last = p.T - 1;
+  constexpr int F = QSL ? 3 : 5;
+  constexpr int NM = F * BT;
+  constexpr int NI = (NM + 63) / 64;
+  int32_t mv[NI];
+#pragma unroll
+  for (int g = 0; g < NI; ++g) {
+    const int L = g * 64 + lane;
+    const int r = L / F;
+    const int f = L - r * F;
+    const int64_t t = t0 + r < t_last ? t0 + r : t_last;
+    const int32_t* src =
+        f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
+              : (f == 3 ? seq_idx : qstart) + t;
+    mv[g] = *src;
+  }
+
+  // The tile's input rows (16 bytes per lane).
+  const int c0 = (slab * 64 + lane) * VEC;  // lane's channels lie in one head
   const bool on = c0 < p.C;
+  const int cl = on ? c0 : 0;               // clamped for the loads
+  P xr[BT];
+#pragma unroll
+  for (int i = 0; i < BT; ++i) {
+    const int64_t t = t0 + i < t_last ? t0 + i : t_last;
+    xr[i].load(x + t * p.x_rs + cl);
+  }
   const int h = on ? c0 / p.ws : 0;
   const int j = c0 - h * p.ws;
   const int64_t lane_off = (int64_t)h * p.cs1 + p.off_s + j;
 
-  // Filter taps of this lane's channels, fp32.
-  float wk[W][VEC];
-  if (on) {
-    constexpr int kChunk = 16 / (int)sizeof(S);
-    constexpr int kN = VEC * W;
-    if constexpr (kN % kChunk == 0) {
-      if (p.w_packed) {
+  // Filter taps of this lane's channels, as raw elements [e][k]; widened to
+  // fp32 after the metadata is in.  The 16-byte-lane kernels take packed
+  // [C, W] weights (VEC*W consecutive elements per lane, moved as 16-byte
+  // chunks); the one-channel kernels read any strides.
+  constexpr int kChunk = 16 / (int)sizeof(S);
+  constexpr int kN = VEC * W;
+  struct WRaw { S e[kN]; } wr;
+  if constexpr (VEC > 1) {
+    static_assert(kN % kChunk == 0, "packed weights come in whole 16-byte chunks");
 #pragma unroll
-        for (int ch = 0; ch < kN / kChunk; ++ch) {
-          Pack<D, kChunk> pk;
-          pk.load(wt + (int64_t)c0 * W + ch * kChunk);
-          float f[kChunk];
-          pk.to_float(f);
+    for (int ch = 0; ch < kN / kChunk; ++ch) {
+      Pack<D, kChunk> pk;
+      pk.load(wt + (int64_t)cl * W + ch * kChunk);
+      typename Pack<D, kChunk>::Elems v =
+          __builtin_bit_cast(typename Pack<D, kChunk>::Elems, pk.raw);
 #pragma unroll
-          for (int q = 0; q < kChunk; ++q) wk[(ch * kChunk + q) % W][(ch * kChunk + q) / W] = f[q];
-        }
-      }
-    }
-    if (!(kN % kChunk == 0) || !p.w_packed) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-#pragma unroll
-        for (int k = 0; k < W; ++k)
-          wk[k][e] = load_as_float<D>(wt + (int64_t)(c0 + e) * p.w_sc + (int64_t)k * p.w_sk);
+      for (int q = 0; q < kChunk; ++q) wr.e[ch * kChunk + q] = v.e[q];
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
-#pragma unroll
-      for (int k = 0; k < W; ++k) wk[k][e] = 0.f;
+    for (int k = 0; k < W; ++k) wr.e[k] = wt[(int64_t)cl * p.w_sc + (int64_t)k * p.w_sk];
   }
 
-  // Per-row metadata (scalar) and the tile's input rows.
-  const int64_t t0 = tile * BT;
-  const bool full = t0 + BT <= p.T;
-  // Positions and slots are below max_blocks*N and num_blocks*N, both
-  // checked on the host to fit in 31 bits; a negative 64-bit slot is PAD.
+  // The parameters needed from here on (addressing, epilogue flags) must
+  // arrive while the loads above are in flight; fetched at first use they
+  // would add a dependent round trip after the metadata returns.  An empty
+  // statement taking them as scalar inputs pins their loads here.
+  asm volatile("" ::"s"(p.n_magic), "s"(p.n_s1), "s"(p.n_s2), "s"(p.N),
+               "s"(p.silu), "s"(p.residual), "s"(p.cs0), "s"(p.cs2), "s"(p.bt_rs),
+               "s"(p.out_rs));
+
+  // Broadcast the metadata.  Positions and slots are below max_blocks*N and
+  // num_blocks*N, both checked on the host to fit in 31 bits; a negative
+  // 64-bit slot is PAD, and so is every row of a wave past the end.
   int32_t pos[BT], slot[BT], req[BT], qs[BT];
-  P xr[BT];
 #pragma unroll
   for (int i = 0; i < BT; ++i) {
-    const int64_t t = t0 + i;
-    if (full || t < p.T) {
-      pos[i] = (int32_t)positions[t];
-      const int64_t s64 = slots[t];
-      slot[i] = s64 < 0 ? -1 : (int32_t)s64;
-      req[i] = seq_idx[t];
-      qs[i] = qstart[t];
-      if (on) xr[i].load(x + t * p.x_rs + c0); else xr[i].zero();
+    const int b = F * i;
+    pos[i] = __builtin_amdgcn_readlane(mv[b / 64], b % 64);
+    const int32_t lo = __builtin_amdgcn_readlane(mv[(b + 1) / 64], (b + 1) % 64);
+    const int32_t hi = __builtin_amdgcn_readlane(mv[(b + 2) / 64], (b + 2) % 64);
+    slot[i] = (hi < 0 || !live_wave || t0 + i > t_last) ? -1 : lo;
+    if constexpr (!QSL) {
+      req[i] = __builtin_amdgcn_readlane(mv[(b + 3) / 64], (b + 3) % 64);
+      qs[i] = __builtin_amdgcn_readlane(mv[(b + 4) / 64], (b + 4) % 64);
     } else {
-      pos[i] = 0;
-      slot[i] = -1;
       req[i] = 0;
       qs[i] = 0;
-      xr[i].zero();
     }
   }
+  if constexpr (QSL) {
+    // Request of each row from the offsets: the workgroup stages them in LDS
+    // once (after the loads above are issued), then each wave searches.
+    extern __shared__ int32_t s_qsl[];
+    if (p.qsl_in_lds) {
+      for (int r = threadIdx.x; r < p.num_reqs; r += p.waves_per_group * 64) s_qsl[r] = p.qsl[r];
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      if (slot[i] < 0) continue;
+      const int64_t t = t0 + i;
+      if (p.qsl_in_lds) {
+        req[i] = find_request(s_qsl, p.num_reqs, t, lane);
+        qs[i] = uniform(s_qsl[req[i]]);
+      } else {
+        req[i] = find_request(p.qsl, p.num_reqs, t, lane);
+        qs[i] = uniform(p.qsl[req[i]]);
+      }
+    }
+  }
+
+  float wk[W][VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e)
+#pragma unroll
+    for (int k = 0; k < W; ++k) wk[k][e] = to_float<D>(wr.e[e * W + k]);
 
   // Halo: input rows t0-m (m = 1..W-1) that a row of this tile reads as a
   // same-forward tap.
@@ -189,25 +282,30 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     // fetched once, by the request's first row in the tile (the one that
     // needs the most of them), and kept in registers for the others.
     const int32_t d = (int32_t)(t - qs[i]);  // row offset inside its request
-    if (d < W - 1 && req[i] != hist_req) {
+    if (d < W - 1 && req[i] != hist_req && pos[i] - d > 0) {
+      // first > 0, so history row 1 (position first-1) is read by this row
+      // and its block-table entry is valid.  Every lookup and load below is
+      // unconditional (a load inside a branch would wait for its value at
+      // the join): rows this request does not read, m > W-1-d or before
+      // position 0, are fetched from history row 1's address instead.
       const int32_t first = pos[i] - d;
       int32_t hblk[kHalo], hoff[kHalo];
 #pragma unroll
       for (int m = 1; m <= W - 1; ++m) {
-        hblk[m - 1] = -1;
-        hoff[m - 1] = 0;
-        const int32_t src = first - m;
-        if (m <= W - 1 - d && src >= 0) {
-          const uint32_t lb = div_n((uint32_t)src, p);
-          hoff[m - 1] = src - (int32_t)lb * p.N;
-          hblk[m - 1] = btab[(int64_t)req[i] * p.bt_rs + lb];
+        const int32_t src = first - m >= 0 ? first - m : 0;
+        const uint32_t lb = div_n((uint32_t)src, p);
+        hoff[m - 1] = src - (int32_t)lb * p.N;
+        hblk[m - 1] = btab[(int64_t)req[i] * p.bt_rs + lb];
+      }
+#pragma unroll
+      for (int m = 2; m <= W - 1; ++m) {
+        if (!(m <= W - 1 - d && first - m >= 0)) {
+          hblk[m - 1] = hblk[0];
+          hoff[m - 1] = hoff[0];
         }
       }
       auto fetch = [&](int m, P& dst) {
-        if (hblk[m - 1] >= 0 && on)
-          dst.load(cache + (int64_t)hblk[m - 1] * p.cs0 + (int64_t)hoff[m - 1] * p.cs2 + lane_off);
-        else
-          dst.zero();
+        dst.load(cache + (int64_t)hblk[m - 1] * p.cs0 + (int64_t)hoff[m - 1] * p.cs2 + (on ? lane_off : 0));
       };
       if constexpr (W > 1) fetch(1, hist1);
       if constexpr (W > 2) fetch(2, hist2);
@@ -277,8 +375,14 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 
 template <typename D, int VEC, int W, int BT>
 static void launch(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
-  hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT>), dim3(grid), dim3(threads), 0, s,
-                     p);
+  if (p.qsl) {
+    const size_t lds = p.qsl_in_lds ? (size_t)p.num_reqs * sizeof(int32_t) : 0;
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, true>), dim3(grid),
+                       dim3(threads), lds, s, p);
+  } else {
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, false>), dim3(grid),
+                       dim3(threads), 0, s, p);
+  }
 }
 
 template <typename D, int VEC, int W>
@@ -314,17 +418,19 @@ static int pick_bt(int64_t T, int64_t slabs) {
 
 }  // namespace sconv
 
-extern "C" int sconv_fused_insert_conv(
-    const void* x, int64_t x_row_stride, const void* weight, int64_t w_stride_c,
-    int64_t w_stride_k, void* cache, int64_t num_blocks, int32_t H, int32_t N, int32_t D,
-    int64_t cs0, int64_t cs1, int64_t cs2, const int64_t* positions,
+namespace sconv {
+
+// Shared launcher of both entry points: per-row metadata (seq_idx,
+// query_start) or request offsets (qsl, num_reqs) searched in the kernel.
+static int fused_launch(
+    const char* fn, const void* x, int64_t x_row_stride, const void* weight,
+    int64_t w_stride_c, int64_t w_stride_k, void* cache, int64_t num_blocks, int32_t H,
+    int32_t N, int32_t D, int64_t cs0, int64_t cs1, int64_t cs2, const int64_t* positions,
     const int32_t* block_table, int64_t bt_row_stride, int32_t max_blocks,
-    const int32_t* seq_idx, const int64_t* slot_mapping, const int32_t* query_start, void* out,
-    int64_t out_row_stride, int64_t T, int32_t off_s, int32_t ws, int32_t W, int32_t dtype,
-    int32_t activation, int32_t use_residual, hipStream_t stream) {
-  using namespace sconv;
-  clear_error();
-  const char* fn = "sconv_fused_insert_conv";
+    const int32_t* seq_idx, const int32_t* query_start, const int32_t* qsl, int32_t num_reqs,
+    const int64_t* slot_mapping, void* out, int64_t out_row_stride, int64_t T, int32_t off_s,
+    int32_t ws, int32_t W, int32_t dtype, int32_t activation, int32_t use_residual,
+    hipStream_t stream) {
   if (T < 0) return fail(SCONV_ERR_INVALID, "%s: T < 0", fn);
   if (!valid_dtype(dtype)) return fail(SCONV_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
   if (!valid_act(activation))
@@ -346,9 +452,11 @@ extern "C" int sconv_fused_insert_conv(
       w_stride_k < 1)
     return fail(SCONV_ERR_INVALID, "%s: cache / block-table / weight strides too small", fn);
   if (T == 0) return SCONV_OK;
-  if (!x || !weight || !cache || !positions || !block_table || !seq_idx || !slot_mapping ||
-      !query_start || !out)
+  if (!x || !weight || !cache || !positions || !block_table || !slot_mapping || !out ||
+      (qsl ? false : (!seq_idx || !query_start)))
     return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
+  if (qsl && num_reqs < 1)
+    return fail(SCONV_ERR_INVALID, "%s: num_reqs < 1 with %lld rows", fn, (long long)T);
   const int64_t es = elem_size(dtype);
   const int64_t x_bytes = ((T - 1) * x_row_stride + C) * es;
   const int64_t o_bytes = ((T - 1) * out_row_stride + C) * es;
@@ -357,41 +465,49 @@ extern "C" int sconv_fused_insert_conv(
     return fail(SCONV_ERR_INVALID, "%s: out overlaps x or the cache", fn);
 
   const int vec16 = (int)(16 / es);
-  const bool vec = C % vec16 == 0 && ws % vec16 == 0 && off_s % vec16 == 0 &&
+  const bool w_packed = w_stride_c == W && w_stride_k == 1 && aligned16(weight);
+  const bool vec = w_packed && C % vec16 == 0 && ws % vec16 == 0 && off_s % vec16 == 0 &&
                    x_row_stride % vec16 == 0 && out_row_stride % vec16 == 0 &&
                    cs0 % vec16 == 0 && cs1 % vec16 == 0 && cs2 % vec16 == 0 && aligned16(x) &&
                    aligned16(out) && aligned16(cache);
   const int VEC = vec ? vec16 : 1;
 
-  FusedParams p;
+  FusedParams p = {};
   p.x = x; p.w = weight; p.cache = cache; p.positions = positions; p.bt = block_table;
   p.seq_idx = seq_idx; p.slot = slot_mapping; p.qs = query_start; p.out = out;
+  p.qsl = qsl;
+  p.num_reqs = qsl ? num_reqs : 0;
+  // Offsets of up to 4096 requests (16 KB) are staged in LDS; beyond that
+  // each wave searches them in memory (the separate metadata launch is then
+  // the faster choice for the caller).
+  p.qsl_in_lds = qsl && num_reqs <= 4096;
   p.x_rs = x_row_stride; p.w_sc = w_stride_c; p.w_sk = w_stride_k;
   p.cs0 = cs0; p.cs1 = cs1; p.cs2 = cs2; p.bt_rs = bt_row_stride; p.out_rs = out_row_stride;
   p.T = T;
   p.C = (int32_t)C; p.ws = ws; p.off_s = off_s; p.N = N;
-  if ((N & (N - 1)) == 0) {
-    p.n_shift = __builtin_ctz((unsigned)N);
-    p.n_magic = 0;
-    p.n_magic_shift = 0;
+  if (N == 1) {
+    p.n_magic = 0; p.n_s1 = 0; p.n_s2 = 0;
+  } else if ((N & (N - 1)) == 0) {
+    p.n_magic = 1; p.n_s1 = 1; p.n_s2 = (uint32_t)__builtin_ctz((unsigned)N) - 1;
   } else {
     const uint32_t l = 32 - __builtin_clz((unsigned)(N - 1));  // ceil(log2 N)
-    p.n_shift = -1;
     p.n_magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - N)) / N + 1);
-    p.n_magic_shift = l - 1;
+    p.n_s1 = 1;
+    p.n_s2 = l - 1;
   }
   p.num_slabs = (int32_t)cdiv(C, 64 * VEC);
   const int bt = pick_bt(T, p.num_slabs);
   p.num_tiles = cdiv(T, bt);
   p.silu = activation == SCONV_ACT_SILU;
   p.residual = use_residual != 0;
-  p.w_packed = w_stride_c == W && w_stride_k == 1 && aligned16(weight) &&
-               ((int64_t)VEC * W * es) % 16 == 0;
 
   const int64_t waves = p.num_tiles * p.num_slabs;
+  if (waves > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
   const uint32_t threads = waves >= 4096 ? 256 : 64;
   const int64_t grid = cdiv(waves, threads / 64);
   if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  p.num_groups = (uint32_t)grid;
+  p.waves_per_group = (int32_t)(threads / 64);
 
   if (dtype == SCONV_BF16) {
     if (VEC == 8) launch_w<Bf16, 8>(W, bt, p, (uint32_t)grid, threads, stream);
@@ -401,4 +517,40 @@ extern "C" int sconv_fused_insert_conv(
     else launch_w<F32, 1>(W, bt, p, (uint32_t)grid, threads, stream);
   }
   return check_launch(fn);
+}
+
+}  // namespace sconv
+
+extern "C" int sconv_fused_insert_conv(
+    const void* x, int64_t x_row_stride, const void* weight, int64_t w_stride_c,
+    int64_t w_stride_k, void* cache, int64_t num_blocks, int32_t H, int32_t N, int32_t D,
+    int64_t cs0, int64_t cs1, int64_t cs2, const int64_t* positions,
+    const int32_t* block_table, int64_t bt_row_stride, int32_t max_blocks,
+    const int32_t* seq_idx, const int64_t* slot_mapping, const int32_t* query_start, void* out,
+    int64_t out_row_stride, int64_t T, int32_t off_s, int32_t ws, int32_t W, int32_t dtype,
+    int32_t activation, int32_t use_residual, hipStream_t stream) {
+  sconv::clear_error();
+  return sconv::fused_launch("sconv_fused_insert_conv", x, x_row_stride, weight, w_stride_c,
+                             w_stride_k, cache, num_blocks, H, N, D, cs0, cs1, cs2, positions,
+                             block_table, bt_row_stride, max_blocks, seq_idx, query_start,
+                             nullptr, 0, slot_mapping, out, out_row_stride, T, off_s, ws, W,
+                             dtype, activation, use_residual, stream);
+}
+
+extern "C" int sconv_fused_insert_conv_qsl(
+    const void* x, int64_t x_row_stride, const void* weight, int64_t w_stride_c,
+    int64_t w_stride_k, void* cache, int64_t num_blocks, int32_t H, int32_t N, int32_t D,
+    int64_t cs0, int64_t cs1, int64_t cs2, const int64_t* positions,
+    const int32_t* block_table, int64_t bt_row_stride, int32_t max_blocks,
+    const int32_t* query_start_loc, int32_t num_reqs, const int64_t* slot_mapping, void* out,
+    int64_t out_row_stride, int64_t T, int32_t off_s, int32_t ws, int32_t W, int32_t dtype,
+    int32_t activation, int32_t use_residual, hipStream_t stream) {
+  sconv::clear_error();
+  if (T > 0 && !query_start_loc)
+    return sconv::fail(SCONV_ERR_INVALID, "sconv_fused_insert_conv_qsl: NULL query_start_loc");
+  return sconv::fused_launch("sconv_fused_insert_conv_qsl", x, x_row_stride, weight, w_stride_c,
+                             w_stride_k, cache, num_blocks, H, N, D, cs0, cs1, cs2, positions,
+                             block_table, bt_row_stride, max_blocks, nullptr, nullptr,
+                             query_start_loc, num_reqs, slot_mapping, out, out_row_stride, T,
+                             off_s, ws, W, dtype, activation, use_residual, stream);
 }

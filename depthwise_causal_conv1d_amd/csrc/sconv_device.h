@@ -125,11 +125,12 @@ __device__ __forceinline__ T pick(const T (&a)[N], int idx) {
 // g % 8), and each XCD has its own L2.  Renumber so that each XCD walks one
 // contiguous run of logical workgroups, in order: neighbouring tiles, which
 // share halo rows, then meet in the same L2.  A bijection on [0, G).
+// Branch-free: XCD x owns the run starting at x*per + min(x, rem).
 __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t g, uint32_t G) {
   constexpr uint32_t kXcd = 8;
   const uint32_t per = G / kXcd, rem = G % kXcd;
   const uint32_t xcd = g % kXcd, idx = g / kXcd;
-  return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
 // Make a value the compiler cannot prove wave-uniform live in a scalar

@@ -70,27 +70,12 @@ def sconv_seq_metadata(query_start_loc: torch.Tensor, num_reqs: int, num_actual_
     _lib.check(rc, "sconv_seq_metadata")
 
 
-def sconv_fused_insert_conv(x: torch.Tensor, weight: torch.Tensor, cache: torch.Tensor,
-                            positions: torch.Tensor, block_table: torch.Tensor,
-                            seq_idx: torch.Tensor, slot_mapping: torch.Tensor,
-                            query_start: torch.Tensor, off_s: int, ws: int, block_size: int,
-                            activation: Optional[str] = None, use_residual: bool = True,
-                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Single-launch insert + depthwise causal conv1d over the paged cache.
-
-    x [T, H*ws], weight [H*ws, W], cache [num_blocks, H, N, D] (modified),
-    positions int64 [T], block_table int32 [num_reqs, max_blocks],
-    seq_idx / query_start int32 [T], slot_mapping int64 [T] (-1 = PAD).
-    Returns ``out`` (new [T, H*ws] tensor unless given; PAD rows untouched).
-    """
+def _fused_checks(x, weight, cache, positions, block_table, slot_mapping, off_s, ws,
+                  block_size, out):
     T = x.shape[0]
-    if out is None:
-        out = torch.empty_like(x)
     if x.dim() != 2 or weight.dim() != 2 or cache.dim() != 4 or block_table.dim() != 2:
         raise ValueError("x [T, C], weight [C, W], cache [nb, H, N, D], block_table [R, M]")
-    if T == 0:
-        return out
-    _dev(x, weight, cache, positions, block_table, seq_idx, slot_mapping, query_start, out)
+    _dev(x, weight, cache, positions, block_table, slot_mapping, out)
     dt = _dtype(x)
     if weight.dtype != x.dtype or cache.dtype != x.dtype or out.dtype != x.dtype:
         raise TypeError("x, weight, cache and out must share one element type")
@@ -107,8 +92,33 @@ def sconv_fused_insert_conv(x: torch.Tensor, weight: torch.Tensor, cache: torch.
         raise TypeError("block_table must be int32")
     _vec(positions, torch.int64, "positions", T)
     _vec(slot_mapping, torch.int64, "slot_mapping", T)
+    return dt
+
+
+def sconv_fused_insert_conv(x: torch.Tensor, weight: torch.Tensor, cache: torch.Tensor,
+                            positions: torch.Tensor, block_table: torch.Tensor,
+                            seq_idx: torch.Tensor, slot_mapping: torch.Tensor,
+                            query_start: torch.Tensor, off_s: int, ws: int, block_size: int,
+                            activation: Optional[str] = None, use_residual: bool = True,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Single-launch insert + depthwise causal conv1d over the paged cache.
+
+    x [T, H*ws], weight [H*ws, W], cache [num_blocks, H, N, D] (modified),
+    positions int64 [T], block_table int32 [num_reqs, max_blocks],
+    seq_idx / query_start int32 [T], slot_mapping int64 [T] (-1 = PAD).
+    Returns ``out`` (new [T, H*ws] tensor unless given; PAD rows untouched).
+    """
+    if out is None:
+        out = torch.empty_like(x)
+    if x.shape[0] == 0:
+        return out
+    dt = _fused_checks(x, weight, cache, positions, block_table, slot_mapping, off_s, ws,
+                       block_size, out)
+    T = x.shape[0]
+    _dev(seq_idx, query_start)
     _vec(seq_idx, torch.int32, "seq_idx", T)
     _vec(query_start, torch.int32, "query_start", T)
+    nb, H, N, D = cache.shape
     rc = _lib.load().sconv_fused_insert_conv(
         _ptr(x), x.stride(0), _ptr(weight), weight.stride(0), weight.stride(1),
         _ptr(cache), nb, H, N, D, cache.stride(0), cache.stride(1), cache.stride(2),
@@ -117,6 +127,36 @@ def sconv_fused_insert_conv(x: torch.Tensor, weight: torch.Tensor, cache: torch.
         T, int(off_s), int(ws), weight.shape[1], dt, _act(activation), int(bool(use_residual)),
         _stream(x))
     _lib.check(rc, "sconv_fused_insert_conv")
+    return out
+
+
+def sconv_fused_insert_conv_qsl(x: torch.Tensor, weight: torch.Tensor, cache: torch.Tensor,
+                                positions: torch.Tensor, block_table: torch.Tensor,
+                                query_start_loc: torch.Tensor, num_reqs: int,
+                                slot_mapping: torch.Tensor, off_s: int, ws: int,
+                                block_size: int, activation: Optional[str] = None,
+                                use_residual: bool = True,
+                                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sconv_seq_metadata + sconv_fused_insert_conv in one launch: rows find
+    their request in query_start_loc [num_reqs + 1] inside the kernel."""
+    if out is None:
+        out = torch.empty_like(x)
+    if x.shape[0] == 0:
+        return out
+    dt = _fused_checks(x, weight, cache, positions, block_table, slot_mapping, off_s, ws,
+                       block_size, out)
+    T = x.shape[0]
+    _dev(query_start_loc)
+    _vec(query_start_loc, torch.int32, "query_start_loc", num_reqs + 1)
+    nb, H, N, D = cache.shape
+    rc = _lib.load().sconv_fused_insert_conv_qsl(
+        _ptr(x), x.stride(0), _ptr(weight), weight.stride(0), weight.stride(1),
+        _ptr(cache), nb, H, N, D, cache.stride(0), cache.stride(1), cache.stride(2),
+        _ptr(positions), _ptr(block_table), block_table.stride(0), block_table.shape[1],
+        _ptr(query_start_loc), int(num_reqs), _ptr(slot_mapping), _ptr(out), out.stride(0),
+        T, int(off_s), int(ws), weight.shape[1], dt, _act(activation), int(bool(use_residual)),
+        _stream(x))
+    _lib.check(rc, "sconv_fused_insert_conv_qsl")
     return out
 
 

@@ -133,6 +133,39 @@ int sconv_fused_insert_conv(const void* x, int64_t x_row_stride,
                             int32_t use_residual, hipStream_t stream);
 
 /*
+ * sconv_fused_insert_conv_qsl -- the same insert + conv, with the per-row
+ * request search folded into the launch.
+ *
+ * Source: vLLM page "vllm.models.inkling.nvidia.ops.sconv", fused_sconv and
+ * sconv_seq_metadata: it computes exactly what sconv_seq_metadata followed
+ * by sconv_fused_insert_conv computes, in one launch.  Every argument is as
+ * in sconv_fused_insert_conv except that seq_idx / query_start are replaced
+ * by the request row offsets:
+ *
+ *   query_start_loc  int32 [num_reqs + 1], non-decreasing, qsl[0] == 0 (device)
+ *
+ * Each non-PAD row t belongs to the last request r with qsl[r] <= t (rows
+ * past qsl[num_reqs] clamp to the last request), and query_start = qsl[r].
+ * Each workgroup stages the offsets in LDS when num_reqs <= 4096; larger
+ * batches search them in device memory, where one sconv_seq_metadata launch
+ * plus sconv_fused_insert_conv is faster.
+ *
+ * Errors: as sconv_fused_insert_conv, plus SCONV_ERR_INVALID for
+ * num_reqs < 1 (or a NULL query_start_loc) with T > 0.
+ */
+int sconv_fused_insert_conv_qsl(const void* x, int64_t x_row_stride,
+                                const void* weight, int64_t w_stride_c, int64_t w_stride_k,
+                                void* cache, int64_t num_blocks, int32_t H, int32_t N,
+                                int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
+                                const int64_t* positions, const int32_t* block_table,
+                                int64_t bt_row_stride, int32_t max_blocks,
+                                const int32_t* query_start_loc, int32_t num_reqs,
+                                const int64_t* slot_mapping, void* out,
+                                int64_t out_row_stride, int64_t T, int32_t off_s,
+                                int32_t ws, int32_t W, int32_t dtype, int32_t activation,
+                                int32_t use_residual, hipStream_t stream);
+
+/*
  * causal_conv1d_varlen_fwd -- causal depthwise conv over packed
  * variable-length sequences, with a slot-indexed state pool.
  *

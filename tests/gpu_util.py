@@ -11,9 +11,11 @@ from tests.helpers import to_np
 SENTINEL = -777.0
 
 
-def gpu_fused(case, dev="cuda", out_init=None, metadata=True):
-    """Run metadata + fused insert/conv on the GPU.  Returns device tensors
-    (out, cache, seq_idx, query_start); the case's cache is not modified."""
+def gpu_fused(case, dev="cuda", out_init=None, fold=False):
+    """Run metadata + fused insert/conv on the GPU (or, with fold=True, the
+    single launch that searches query_start_loc itself).  Returns device
+    tensors (out, cache, seq_idx, query_start) -- the last two None when
+    folded; the case's cache is not modified."""
     import depthwise_causal_conv1d_amd as lib
     T = case.T
     x = case.x.to(dev)
@@ -23,10 +25,15 @@ def gpu_fused(case, dev="cuda", out_init=None, metadata=True):
     bt = case.block_table.to(dev)
     sm = case.slot_mapping.to(dev)
     qsl = case.query_start_loc.to(dev)
+    out = (torch.full_like(x, SENTINEL) if out_init is None else out_init.to(dev).clone())
+    if fold:
+        lib.sconv_fused_insert_conv_qsl(x, w, cache, pos, bt, qsl, case.num_reqs, sm, case.off_s,
+                                        case.ws, case.block_size, case.activation,
+                                        case.use_residual, out=out)
+        return out, cache, None, None
     seq_idx = torch.full((T,), -5, dtype=torch.int32, device=dev)
     qs = torch.full((T,), -5, dtype=torch.int32, device=dev)
     lib.sconv_seq_metadata(qsl, case.num_reqs, case.num_actual, seq_idx, qs, T)
-    out = (torch.full_like(x, SENTINEL) if out_init is None else out_init.to(dev).clone())
     lib.sconv_fused_insert_conv(x, w, cache, pos, bt, seq_idx, sm, qs, case.off_s, case.ws,
                                 case.block_size, case.activation, case.use_residual, out=out)
     return out, cache, seq_idx, qs

@@ -70,11 +70,11 @@ def test_seq_metadata_errors():
 
 # ------------------------------------------------------------------ fused insert + conv
 
-def check_fused(case, what, cache_compare="full"):
+def check_fused(case, what, cache_compare="full", fold=False):
     """Run both sides on one case and compare out, metadata and cache."""
     say(f"fused {what}: T={case.T} C={case.C} W={case.W} N={case.block_size} "
-        f"dtype={case.x.dtype} off_s={case.off_s}")
-    out_g, cache_g, si_g, qs_g = gpu_fused(case)
+        f"dtype={case.x.dtype} off_s={case.off_s} folded={fold}")
+    out_g, cache_g, si_g, qs_g = gpu_fused(case, fold=fold)
     if cache_compare == "full":
         out_r, cache_r, si_r, qs_r = oracle_fused(case)
         cache_gh = to_np(cache_g)
@@ -88,8 +88,9 @@ def check_fused(case, what, cache_compare="full"):
         untouched[ids] = False
         if untouched.any():
             assert torch.isnan(cache_g[untouched].float()).all(), "write outside referenced blocks"
-    np.testing.assert_array_equal(to_np(si_g), si_r)
-    np.testing.assert_array_equal(to_np(qs_g), qs_r)
+    if si_g is not None:
+        np.testing.assert_array_equal(to_np(si_g), si_r)
+        np.testing.assert_array_equal(to_np(qs_g), qs_r)
     live = live_rows(case)
     out_gh = to_np(out_g)
     assert_close(out_gh, out_r, dtype_name(case.x.dtype), f"{what} out", mask=live)
@@ -112,17 +113,19 @@ SWEEP = [
 ]
 
 
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
 @pytest.mark.parametrize("spec", SWEEP, ids=[s[0] for s in SWEEP])
-def test_fused_sweep(spec):
+def test_fused_sweep(spec, fold):
     name, dt, W, H, ws, D, off, N, new, ctx, pad, tail, act, res = spec
     case = workloads.fused_case(zlib.crc32(name.encode()) % 1000, new, ctx, H=H, D=D, ws=ws, off_s=off,
                                 block_size=N, W=W, dtype=dt, pad_count=pad, tail_pad=tail,
                                 activation=act, use_residual=res)
-    check_fused(case, name)
+    check_fused(case, name, fold=fold)
 
 
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
 @pytest.mark.parametrize("T_total,C_heads", [(4507, 32), (2000, 32), (500, 32)])
-def test_fused_tile_shapes(T_total, C_heads):
+def test_fused_tile_shapes(T_total, C_heads, fold):
     """Token counts that select each rows-per-wave tile (16, 4, 1) with a
     ragged tail, several requests per tile and requests straddling tiles."""
     rng = np.random.default_rng(T_total)
@@ -133,17 +136,32 @@ def test_fused_tile_shapes(T_total, C_heads):
     case = workloads.fused_case(7, new, ctx, H=C_heads, D=256, ws=128, off_s=128,
                                 block_size=16, W=4, dtype=torch.bfloat16,
                                 pad_count=T_total // 10, tail_pad=5)
-    check_fused(case, f"tiles T={T_total}")
+    check_fused(case, f"tiles T={T_total}", fold=fold)
 
 
-def test_config_tiny_prefill():
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
+def test_config_tiny_prefill(fold):
     case = workloads.tiny_prefill()
-    check_fused(case, "tiny prefill (fp32)")
+    check_fused(case, "tiny prefill (fp32)", fold=fold)
 
 
-def test_config_batched_decode():
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
+def test_config_batched_decode(fold):
     case = workloads.batched_decode()
-    check_fused(case, "batched decode", cache_compare="compact")
+    check_fused(case, "batched decode", cache_compare="compact", fold=fold)
+
+
+def test_folded_search_beyond_lds():
+    """More requests than the in-LDS limit: the folded launch searches the
+    offsets in device memory; empty requests included."""
+    g = torch.Generator().manual_seed(23)
+    R = 5000
+    new = [int(v) for v in torch.randint(0, 3, (R,), generator=g)]
+    new[-1] = max(new[-1], 1)
+    ctx = [int(v) for v in torch.randint(0, 40, (R,), generator=g)]
+    case = workloads.fused_case(23, new, ctx, H=2, D=16, ws=8, off_s=8, block_size=16, W=4,
+                                dtype=torch.bfloat16, pad_count=7, tail_pad=3)
+    check_fused(case, "5000 requests, in-memory search", fold=True)
 
 
 def test_config_batched_decode_large_pool():
@@ -185,14 +203,16 @@ def test_config_mixed_prefill_four_streams():
     assert_bits_equal(to_np(cache_g), cache_r, "shared cache after four streams")
 
 
-def test_config_spec_decode():
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
+def test_config_spec_decode(fold):
     case = workloads.spec_decode()
-    check_fused(case, "spec decode", cache_compare="compact")
+    check_fused(case, "spec decode", cache_compare="compact", fold=fold)
 
 
 # ------------------------------------------------------------------ hipGraph replay
 
-def test_graph_replay_decode_steps():
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
+def test_graph_replay_decode_steps(fold):
     """Capture metadata + fused conv once for a decode batch; replay it for
     successive steps with new inputs written into the captured buffers.
     Each replay must equal the oracle; each step reads the previous steps'
@@ -218,6 +238,10 @@ def test_graph_replay_decode_steps():
     bt = case.block_table.to(DEV)
 
     def step():
+        if fold:
+            lib.sconv_fused_insert_conv_qsl(x_b, w, cache, pos_b, bt, qsl_b, R, sm_b, case.off_s,
+                                            case.ws, case.block_size, "silu", True, out=out_b)
+            return
         lib.sconv_seq_metadata(qsl_b, R, R, si_b, qs_b, R)
         lib.sconv_fused_insert_conv(x_b, w, cache, pos_b, bt, si_b, sm_b, qs_b, case.off_s,
                                     case.ws, case.block_size, "silu", True, out=out_b)
