@@ -510,9 +510,11 @@ def main():
     ap.add_argument("--workload", default="batched_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the CPU baseline (0: skip)")
-    ap.add_argument("--metadata", choices=("separate", "folded"), default="separate",
+    ap.add_argument("--metadata", choices=("auto", "separate", "folded"), default="auto",
                     help="per-row request search: its own sconv_seq_metadata launch per step, "
-                         "or inside the fused launch (sconv_fused_insert_conv_qsl)")
+                         "or inside the fused launch (sconv_fused_insert_conv_qsl); auto picks "
+                         "the faster per step: folded for decode and spec decode, separate for "
+                         "the 4-stream prefill (one metadata launch serves four streams)")
     ap.add_argument("--requests", type=int, default=256,
                     help="batched_decode only: requests per decode batch (batch-size sweep)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -538,7 +540,8 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: {n} bytes read, {n} bytes written")
         del src, dst, evict
-    fold = args.metadata == "folded"
+    fold = (args.metadata == "folded" or
+            (args.metadata == "auto" and args.workload in ("batched_decode", "spec_decode")))
     if args.workload == "batched_decode":
         wl = DecodeBench(requests=args.requests, fold=fold)
     elif args.workload in ("mixed_prefill", "spec_decode"):
