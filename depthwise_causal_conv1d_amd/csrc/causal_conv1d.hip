@@ -229,6 +229,9 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(const VarlenParams p) {
 // ---------------------------------------------------------------- decode update
 
 struct UpdateParams {
+  // Small fields first (they come in with the first scalar load).
+  int32_t batch, dim, silu, pad_slot_id;
+  int32_t has_bias, has_idx, threads, nvec;  // nvec: lane vectors per row
   const void* x;
   void* states;
   const void* w;
@@ -236,13 +239,29 @@ struct UpdateParams {
   const int32_t* idx;
   void* out;
   int64_t x_rs, ss_slot, ss_c, ss_k, w_sc, w_sk, out_rs;
-  int64_t nvec;  // lane vectors per row
-  int32_t batch, dim, silu, pad_slot_id, state_packed;
 };
 
+// Element `flat` of a run of lane vectors (compile-time index).
+template <typename D, int VEC, int N>
+__device__ __forceinline__ typename D::storage elem_at(const Pack<D, VEC> (&a)[N], int flat) {
+  return __builtin_bit_cast(typename Pack<D, VEC>::Elems, a[flat / VEC].raw).e[flat % VEC];
+}
+
+// Keep a loaded value's load ahead of this point: without it the compiler
+// sinks loads whose only use is under the store branch behind that branch.
+template <typename T>
+__device__ __forceinline__ void loaded_here(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+
 // One thread per (row, VEC channels): window = state ++ x, one dot product,
-// state shifted by one.  The VEC*(W-1) state elements of a thread are
-// contiguous in the usual [slot, dim, W-1] layout and move as 16-byte chunks.
+// state shifted by one.  Loads are unconditional from valid addresses (a
+// PAD row reads slot 0 and stores nothing; a missing bias reads the weights
+// and is replaced by zero), so the only dependent step is index -> state.
+// The 16-byte-lane kernels take packed [dim, W] weights and the packed
+// [slot, dim, W-1] state layout and move each as W (W-1) lane vectors: the
+// VEC channels' taps are contiguous, flat index e*W + k (e*(W-1) + m).  The
+// one-channel kernels read any strides, one element per vector.
 template <typename D, int VEC, int W>
 __global__ __launch_bounds__(256) void update_kernel(const UpdateParams p) {
   using S = typename D::storage;
@@ -253,86 +272,88 @@ __global__ __launch_bounds__(256) void update_kernel(const UpdateParams p) {
   S* out = static_cast<S*>(p.out);
   S* st = static_cast<S*>(p.states);
   const S* __restrict__ wt = static_cast<const S*>(p.w);
-  const S* __restrict__ bias = static_cast<const S*>(p.bias);
+  // Bias, or the stand-in: each channel's first weight.
+  const S* bbase = p.has_bias ? static_cast<const S*>(p.bias) : wt;
+  const int64_t bstride = p.has_bias ? 1 : (VEC > 1 ? W : p.w_sc);
+  // Fetch every kernel argument in the first batch of scalar loads.
+  asm volatile("" ::"s"(p.idx), "s"(p.x), "s"(p.w), "s"(bbase), "s"(p.states), "s"(p.x_rs),
+               "s"(p.ss_slot), "s"(p.out), "s"(p.out_rs));
 
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t b = gid / p.nvec;
-  if (b >= p.batch) return;
-  const int c0 = (int)(gid - b * p.nvec) * VEC;
-  const int64_t slot = p.idx ? (int64_t)p.idx[b] : b;
-  if (slot == p.pad_slot_id) return;
+  // The host bounds batch * nvec below 2^31, so 32-bit index math suffices.
+  const uint32_t gid = blockIdx.x * (uint32_t)p.threads + threadIdx.x;
+  uint32_t b = gid / (uint32_t)p.nvec;
+  const bool live = b < (uint32_t)p.batch;
+  int c0 = (int)(gid - b * (uint32_t)p.nvec) * VEC;
+  if (!live) {
+    b = p.batch - 1;
+    c0 = 0;
+  }
 
-  P xv;
-  xv.load(x + b * p.x_rs + c0);
-  typename P::Elems xe = __builtin_bit_cast(typename P::Elems, xv.raw);
-  float xf[VEC];
+  // Independent loads: state index first, then input, weights, bias.
+  int32_t slot_in = (int32_t)b;
+  if (p.has_idx) slot_in = p.idx[b];
+  P xv, bv, wv[W], sv[SA];
+  xv.load(x + (int64_t)b * p.x_rs + c0);
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    if constexpr (VEC > 1)
+      wv[k].load(wt + (int64_t)c0 * W + k * VEC);
+    else
+      wv[k].load(wt + (int64_t)c0 * p.w_sc + (int64_t)k * p.w_sk);
+  }
+  bv.load(bbase + (int64_t)c0 * bstride);
+
+  // Dependent: the state of this thread's channels.
+  const bool pad = slot_in == p.pad_slot_id;
+  S* srow = st + (int64_t)(pad ? 0 : slot_in) * p.ss_slot;
+#pragma unroll
+  for (int m = 0; m < SL; ++m) {
+    if constexpr (VEC > 1)
+      sv[m].load(srow + (int64_t)c0 * SL + m * VEC);
+    else
+      sv[m].load(srow + (int64_t)c0 * p.ss_c + (int64_t)m * p.ss_k);
+  }
+  loaded_here(xv.raw);
+  loaded_here(bv.raw);
+#pragma unroll
+  for (int k = 0; k < W; ++k) loaded_here(wv[k].raw);
+#pragma unroll
+  for (int m = 0; m < SL; ++m) loaded_here(sv[m].raw);
+
+  float xf[VEC], bf[VEC], y[VEC];
   xv.to_float(xf);
-
-  S* srow = st + slot * p.ss_slot;
-  struct StateElems { S e[VEC * SA]; } sr;  // [e][m] flattened, m fastest
-  constexpr int kChunkE = 16 / (int)sizeof(S);
-  constexpr bool kChunked = VEC > 1 && SL > 0 && (VEC * SL) % kChunkE == 0;
-  if constexpr (kChunked) {
-    if (p.state_packed) {
-#pragma unroll
-      for (int ch = 0; ch < VEC * SL / kChunkE; ++ch) {
-        Pack<D, kChunkE> pk;
-        pk.load(srow + (int64_t)c0 * SL + ch * kChunkE);
-        typename Pack<D, kChunkE>::Elems v = __builtin_bit_cast(typename Pack<D, kChunkE>::Elems, pk.raw);
-#pragma unroll
-        for (int q = 0; q < kChunkE; ++q) sr.e[ch * kChunkE + q] = v.e[q];
-      }
-    }
-  }
-  if (!kChunked || !p.state_packed) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-#pragma unroll
-      for (int m = 0; m < SL; ++m)
-        sr.e[e * SA + m] = srow[(int64_t)(c0 + e) * p.ss_c + m * p.ss_k];
-  }
-
-  float y[VEC];
+  bv.to_float(bf);
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    float acc = bias ? load_as_float<D>(bias + c0 + e) : 0.f;
+    float acc = p.has_bias ? bf[e] : 0.f;
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-      const float v = k < SL ? to_float<D>(sr.e[e * SA + (k < SL ? k : 0)]) : xf[e];
-      acc = __builtin_fmaf(load_as_float<D>(wt + (int64_t)(c0 + e) * p.w_sc + k * p.w_sk), v, acc);
+      const float v = k < SL ? to_float<D>(elem_at(sv, e * SL + (k < SL ? k : 0))) : xf[e];
+      acc = __builtin_fmaf(to_float<D>(elem_at(wv, e * W + k)), v, acc);
     }
     y[e] = p.silu ? silu(acc) : acc;
   }
+  if (!live || pad) return;
   P o;
   o.from_float(y);
-  o.store(out + b * p.out_rs + c0);
+  o.store(out + (int64_t)b * p.out_rs + c0);
 
   // Shifted state: window entries 1 .. W-1.
-  StateElems ns;
+  const typename P::Elems xe = __builtin_bit_cast(typename P::Elems, xv.raw);
 #pragma unroll
-  for (int e = 0; e < VEC; ++e)
+  for (int m = 0; m < SL; ++m) {
+    typename P::Elems v;
 #pragma unroll
-    for (int m = 0; m < SL; ++m)
-      ns.e[e * SA + m] = (m + 1 < SL) ? sr.e[e * SA + m + 1] : xe.e[e];
-  if constexpr (kChunked) {
-    if (p.state_packed) {
-#pragma unroll
-      for (int ch = 0; ch < VEC * SL / kChunkE; ++ch) {
-        typename Pack<D, kChunkE>::Elems v;
-#pragma unroll
-        for (int q = 0; q < kChunkE; ++q) v.e[q] = ns.e[ch * kChunkE + q];
-        Pack<D, kChunkE> pk;
-        pk.raw = __builtin_bit_cast(typename Pack<D, kChunkE>::raw_t, v);
-        pk.store(srow + (int64_t)c0 * SL + ch * kChunkE);
-      }
+    for (int q = 0; q < VEC; ++q) {
+      const int flat = m * VEC + q, e = flat / SL, j = flat % SL;
+      v.e[q] = j + 1 < SL ? elem_at(sv, e * SL + j + 1) : xe.e[e];
     }
-  }
-  if (!kChunked || !p.state_packed) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-#pragma unroll
-      for (int m = 0; m < SL; ++m)
-        srow[(int64_t)(c0 + e) * p.ss_c + m * p.ss_k] = ns.e[e * SA + m];
+    P pk;
+    pk.raw = __builtin_bit_cast(typename P::raw_t, v);
+    if constexpr (VEC > 1)
+      pk.store(srow + (int64_t)c0 * SL + m * VEC);
+    else
+      pk.store(srow + (int64_t)c0 * p.ss_c + (int64_t)m * p.ss_k);
   }
 }
 
@@ -458,22 +479,27 @@ extern "C" int causal_conv1d_update(const void* x, int64_t x_stride_b, void* con
       return fail(SCONV_ERR_INVALID, "%s: out partially overlaps x", fn);
   }
   const int vec16 = (int)(16 / es);
+  // 16-byte lanes need packed weights and states, aligned rows and bias.
   const bool vec = dim % vec16 == 0 && x_stride_b % vec16 == 0 && out_stride_b % vec16 == 0 &&
-                   aligned16(x) && aligned16(out);
+                   aligned16(x) && aligned16(out) && w_stride_c == W && w_stride_k == 1 &&
+                   aligned16(weight) && (!bias || aligned16(bias)) &&
+                   (W == 1 || (st_stride_k == 1 && st_stride_c == W - 1 &&
+                               st_stride_slot % vec16 == 0 && aligned16(conv_states)));
   const int VEC = vec ? vec16 : 1;
-  UpdateParams p;
+  UpdateParams p = {};
   p.x = x; p.states = conv_states; p.w = weight; p.bias = bias; p.idx = conv_state_indices;
   p.out = out; p.x_rs = x_stride_b; p.ss_slot = st_stride_slot; p.ss_c = st_stride_c;
   p.ss_k = st_stride_k; p.w_sc = w_stride_c; p.w_sk = w_stride_k; p.out_rs = out_stride_b;
-  p.nvec = cdiv(dim, VEC);
+  p.nvec = (int32_t)cdiv(dim, VEC);
   p.batch = batch; p.dim = dim; p.silu = activation == SCONV_ACT_SILU;
   p.pad_slot_id = pad_slot_id;
-  p.state_packed = st_stride_k == 1 && st_stride_c == W - 1 && aligned16(conv_states) &&
-                   st_stride_slot % vec16 == 0;
-  const int64_t threads_total = p.nvec * batch;
+  p.has_bias = bias != nullptr;
+  p.has_idx = conv_state_indices != nullptr;
+  const int64_t threads_total = (int64_t)p.nvec * batch;
+  if (threads_total + 256 > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: batch * dim too large", fn);
   const uint32_t th = threads_total >= 256 * 512 ? 256 : 64;
+  p.threads = (int32_t)th;
   const int64_t grid = cdiv(threads_total, th);
-  if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
   if (dtype == SCONV_BF16) {
     if (vec) launch_update<Bf16, 8>(W, p, (uint32_t)grid, th, stream);
     else launch_update<Bf16, 1>(W, p, (uint32_t)grid, th, stream);
