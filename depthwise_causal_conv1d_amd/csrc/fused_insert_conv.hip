@@ -99,9 +99,18 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_ENOUGH_WAVES 4096
 #endif
 
-// QSL: rows find their request in the offsets p.qsl inside the kernel
-// (otherwise they read the per-row seq_idx / query_start buffers).
-template <typename D, int VEC, int W, int BT, bool QSL>
+// Where a row's request and request start come from (template QM).
+constexpr int kQslOff = 0;   // the per-row seq_idx / query_start buffers
+constexpr int kQslRegs = 1;  // the offsets qsl, read whole into registers
+constexpr int kQslLds = 2;   // the offsets qsl, staged in LDS or searched in memory
+#ifndef SCONV_FUSED_QSL_REG_MAX
+#define SCONV_FUSED_QSL_REG_MAX 512
+#endif
+// Requests that take kQslRegs (at most 512: 8 offsets per lane).
+constexpr int kQslRegMax = SCONV_FUSED_QSL_REG_MAX;
+static_assert(kQslRegMax <= 512, "8 offsets per lane");
+
+template <typename D, int VEC, int W, int BT, int QM>
 __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParams p) {
   using S = typename D::storage;
   using P = Pack<D, VEC>;
@@ -141,6 +150,7 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   // buffers (rows past T, lanes past C): a conditional load would join its
   // value with a default and force an immediate wait for it.
   const int64_t t_last = p.T - 1;
+  constexpr int QSL = QM != kQslOff;
   constexpr int F = QSL ? 3 : 5;
   constexpr int NM = F * BT;
   constexpr int NI = (NM + 63) / 64;
@@ -155,6 +165,17 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
         f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
               : (f == 3 ? seq_idx : qstart) + t;
     mv[g] = *src;
+  }
+  // Up to 512 request offsets: ov[j] of lane L is offset 64*j + L, so each
+  // load reads 256 contiguous bytes (indices clamped into the array; the
+  // copies past the end are masked below).
+  int32_t ov[8];
+  if constexpr (QM == kQslRegs) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = j * 64 + lane;
+      ov[j] = p.qsl[r < p.num_reqs ? r : p.num_reqs - 1];
+    }
   }
 
   // The tile's input rows (16 bytes per lane).
@@ -221,33 +242,100 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
       qs[i] = 0;
     }
   }
-  if constexpr (QSL) {
-    // Request of each row from the offsets: the workgroup stages them in LDS
-    // once (after the loads above are issued), then each wave searches.
-    extern __shared__ int32_t s_qsl[];
-    if (p.qsl_in_lds) {
-      for (int r = threadIdx.x; r < p.num_reqs; r += p.waves_per_group * 64) s_qsl[r] = p.qsl[r];
-      __syncthreads();
-    }
+  if constexpr (QM == kQslRegs) {
+    // Offsets in registers: the count of offsets <= t is t's request plus
+    // one (offsets are non-decreasing; those past the end are masked to
+    // INT32_MAX), summed over the eight 64-offset runs by ballot and
+    // popcount.  A tile whose first and last rows count the same lies in
+    // one request.
 #pragma unroll
-    for (int i = 0; i < BT; ++i) {
-      if (slot[i] < 0) continue;
-      const int64_t t = t0 + i;
-      if (p.qsl_in_lds) {
-        req[i] = find_request(s_qsl, p.num_reqs, t, lane);
-        qs[i] = uniform(s_qsl[req[i]]);
-      } else {
-        req[i] = find_request(p.qsl, p.num_reqs, t, lane);
-        qs[i] = uniform(p.qsl[req[i]]);
+    for (int j = 0; j < 8; ++j)
+      if (j * 64 + lane >= p.num_reqs) ov[j] = INT32_MAX;
+    auto count_le = [&](int32_t t) -> int32_t {
+      int32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c += (int32_t)__popcll(__ballot(ov[j] <= t));
+      return c;
+    };
+    auto offset_of = [&](int32_t r) -> int32_t {
+      const int32_t l = r & 63, j = r >> 6;
+      int32_t v = __builtin_amdgcn_readlane(ov[0], l);
+#pragma unroll
+      for (int q = 1; q < 8; ++q) {
+        const int32_t vq = __builtin_amdgcn_readlane(ov[q], l);
+        v = j == q ? vq : v;
+      }
+      return v;
+    };
+    const int32_t tl = (int32_t)t_last;
+    const int32_t ta = t0 < tl ? (int32_t)t0 : tl;
+    const int32_t ca = count_le(ta);
+    int32_t cb = ca;
+    if constexpr (BT > 1) {
+      const int32_t tb = t0 + BT - 1 < tl ? (int32_t)(t0 + BT - 1) : tl;
+      cb = count_le(tb);
+    }
+    if (ca == cb) {
+      const int32_t r = ca > 0 ? ca - 1 : 0;  // rows before the first offset: request 0
+      const int32_t q = offset_of(r);
+#pragma unroll
+      for (int i = 0; i < BT; ++i) {
+        req[i] = r;
+        qs[i] = q;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < BT; ++i) {
+        const int32_t t = t0 + i < tl ? (int32_t)(t0 + i) : tl;
+        const int32_t c = count_le(t);
+        req[i] = c > 0 ? c - 1 : 0;
+        qs[i] = offset_of(req[i]);
       }
     }
   }
-
-  float wk[W][VEC];
+  if constexpr (QM == kQslLds) {
+    // Request of each row from the offsets: the workgroup stages them in LDS
+    // once (after the loads above are issued).  Each wave searches for the
+    // request r0 of its first row, reads the 64 offsets from r0 on in one
+    // access, and every row's request is r0 plus the count of those offsets
+    // <= row, less one.  Only when 64 request starts fall inside one tile
+    // (empty requests) can a row lie past that window; such a row searches
+    // on its own.
+    extern __shared__ int32_t s_qsl[];
+    const int32_t n = p.num_reqs;
+    if (p.qsl_in_lds) {
+      for (int r = threadIdx.x; r < n; r += p.waves_per_group * 64) s_qsl[r] = p.qsl[r];
+      __syncthreads();
+    }
+    const int64_t tf = t0 < t_last ? t0 : t_last;
+    int32_t r0, wnd;
+    if (p.qsl_in_lds) {
+      r0 = find_request(s_qsl, n, tf, lane);
+      wnd = s_qsl[r0 + lane < n ? r0 + lane : n - 1];
+    } else {
+      r0 = find_request(p.qsl, n, tf, lane);
+      wnd = p.qsl[r0 + lane < n ? r0 + lane : n - 1];
+    }
+    const bool in_window = lane < n - r0;
+    const bool beyond = r0 + 64 < n;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e)
-#pragma unroll
-    for (int k = 0; k < W; ++k) wk[k][e] = to_float<D>(wr.e[e * W + k]);
+    for (int i = 0; i < BT; ++i) {
+      const int64_t t = t0 + i;
+      int32_t k = (int32_t)__popcll(__ballot(in_window && (int64_t)wnd <= t)) - 1;
+      k = k < 0 ? 0 : k;  // rows before the first offset belong to request 0
+      req[i] = r0 + k;
+      qs[i] = __builtin_amdgcn_readlane(wnd, k);
+      if (k == 63 && beyond && slot[i] >= 0) {
+        if (p.qsl_in_lds) {
+          req[i] = find_request(s_qsl, n, t, lane);
+          qs[i] = uniform(s_qsl[req[i]]);
+        } else {
+          req[i] = find_request(p.qsl, n, t, lane);
+          qs[i] = uniform(p.qsl[req[i]]);
+        }
+      }
+    }
+  }
 
   // Halo: input rows t0-m (m = 1..W-1) that a row of this tile reads as a
   // same-forward tap.
@@ -261,8 +349,13 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
       for (int i = 0; i < BT && i <= W - 1 - m; ++i)
         need |= slot[i] >= 0 && pos[i] - (i + m) >= 0 && t0 - m >= (int64_t)qs[i] && t0 - m >= 0;
     }
-    if (need && on) halo[m - 1].load(x + (t0 - m) * p.x_rs + c0); else halo[m - 1].zero();
+    // Loaded only where read (the tap choice below reads halo m exactly
+    // for the rows counted in `need`), and left unset otherwise: merging
+    // with a default value would make the wave wait for the load right
+    // here, in front of the history lookups.
+    if (need && on) halo[m - 1].load(x + (t0 - m) * p.x_rs + c0);
   }
+
 
   // History rows 1..W-1 of the current request, in named registers (an
   // array indexed by a run-time value would be demoted to LDS).
@@ -271,9 +364,9 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   hist2.zero();
   hist3.zero();
   int32_t hist_req = -1;  // request whose history rows are held
+  float wk[W][VEC];        // filter taps in fp32, widened after row 0's history fetch
 #pragma unroll
   for (int i = 0; i < BT; ++i) {
-    if (slot[i] < 0) continue;  // PAD (or past T): no output, no insert
     const int64_t t = t0 + i;
 
     // Pre-forward taps of a row are its request's history: the cache rows
@@ -282,7 +375,7 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     // fetched once, by the request's first row in the tile (the one that
     // needs the most of them), and kept in registers for the others.
     const int32_t d = (int32_t)(t - qs[i]);  // row offset inside its request
-    if (d < W - 1 && req[i] != hist_req && pos[i] - d > 0) {
+    if (slot[i] >= 0 && d < W - 1 && req[i] != hist_req && pos[i] - d > 0) {
       // first > 0, so history row 1 (position first-1) is read by this row
       // and its block-table entry is valid.  Every lookup and load below is
       // unconditional (a load inside a branch would wait for its value at
@@ -312,6 +405,16 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
       if constexpr (W > 3) fetch(3, hist3);
       hist_req = req[i];
     }
+    // Widening here rather than before the loop keeps the wait for the
+    // weights (which, counted in order, also waits for the halo loads)
+    // behind the issue of the history lookups.
+    if (i == 0) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int k = 0; k < W; ++k) wk[k][e] = to_float<D>(wr.e[e * W + k]);
+    }
+    if (slot[i] < 0) continue;  // PAD (or past T): no output, no insert
 
     // Taps, oldest first: pick the raw 16 bytes (uniform choice), widen,
     // accumulate in fp32.
@@ -375,12 +478,15 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 
 template <typename D, int VEC, int W, int BT>
 static void launch(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
-  if (p.qsl) {
+  if (p.qsl && p.num_reqs <= kQslRegMax) {
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs>), dim3(grid),
+                       dim3(threads), 0, s, p);
+  } else if (p.qsl) {
     const size_t lds = p.qsl_in_lds ? (size_t)p.num_reqs * sizeof(int32_t) : 0;
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, true>), dim3(grid),
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslLds>), dim3(grid),
                        dim3(threads), lds, s, p);
   } else {
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, false>), dim3(grid),
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslOff>), dim3(grid),
                        dim3(threads), 0, s, p);
   }
 }

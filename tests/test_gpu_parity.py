@@ -164,6 +164,30 @@ def test_folded_search_beyond_lds():
     check_fused(case, "5000 requests, in-memory search", fold=True)
 
 
+@pytest.mark.parametrize("run_len,runs", [(100, 8), (600, 7)], ids=["lds", "memory"])
+def test_folded_empty_request_runs(run_len, runs):
+    """Runs of >= 64 empty requests between two rows of one 8-row tile: a
+    row past such a run lies beyond the 64 offsets a wave reads after its
+    first row's request and must be found on its own.  About 4100 rows
+    over 4096 channels (8 slabs) select 8-row tiles; 2300 requests keep the
+    offsets in LDS, 5700 push the search into device memory."""
+    rng = np.random.default_rng(run_len)
+    new = [int(v) for v in rng.integers(1, 6, 1500)]
+    T = sum(new)
+    assert T >= 4100
+    starts = np.cumsum([0] + new[:-1])
+    # Insert each run before a request whose first row is not a tile's first.
+    cand = [r for r in range(1, 1500) if starts[r] % 8 != 0]
+    where = sorted(rng.choice(cand, runs, replace=False).tolist(), reverse=True)
+    for r in where:
+        new[r:r] = [0] * run_len
+    ctx = [int(v) for v in rng.integers(0, 40, len(new))]
+    case = workloads.fused_case(31 + run_len, new, ctx, H=32, D=128, ws=128, off_s=0,
+                                block_size=16, W=4, dtype=torch.bfloat16, pad_count=9,
+                                tail_pad=2)
+    check_fused(case, f"{len(new)} requests, runs of {run_len} empty", fold=True)
+
+
 def test_config_batched_decode_large_pool():
     """Same decode batch with its blocks scattered over a 16k-block pool."""
     case = workloads.batched_decode(pool_blocks=16384, device=DEV)
