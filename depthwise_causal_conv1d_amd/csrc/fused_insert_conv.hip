@@ -90,10 +90,19 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 
 // Build-time tuning knobs (defaults chosen by measurement on MI355X).
 #ifndef SCONV_FUSED_BT_MAX
-#define SCONV_FUSED_BT_MAX 8       // largest rows-per-wave tile
+#define SCONV_FUSED_BT_MAX 4       // largest rows-per-wave tile (4, 8 or 16)
 #endif
 #ifndef SCONV_FUSED_NT_STORES
 #define SCONV_FUSED_NT_STORES 1    // streaming (non-temporal) out / cache stores
+#endif
+#ifndef SCONV_FUSED_SLAB_MAJOR
+#define SCONV_FUSED_SLAB_MAJOR 1
+#endif
+#ifndef SCONV_FUSED_XCD_ORDER
+#define SCONV_FUSED_XCD_ORDER 1
+#endif
+#ifndef SCONV_FUSED_WG_THREADS
+#define SCONV_FUSED_WG_THREADS 256
 #endif
 #ifndef SCONV_FUSED_ENOUGH_WAVES
 #define SCONV_FUSED_ENOUGH_WAVES 4096
@@ -129,7 +138,11 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   // batch) rather than from the implicit arguments, which would cost a
   // second dependent round trip before any data load could start.
   // Wave counts are below 2^31 (checked on the host): 32-bit arithmetic.
+#if SCONV_FUSED_XCD_ORDER
   uint32_t wave = xcd_contiguous(blockIdx.x, p.num_groups) * (uint32_t)p.waves_per_group +
+#else
+  uint32_t wave = blockIdx.x * (uint32_t)p.waves_per_group +
+#endif
                   (uint32_t)uniform(threadIdx.x >> 6);
   // A wave past the end works on the last tile and writes nothing (no early
   // return: it would also split the parameter loads around the branch, and
@@ -137,8 +150,14 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   const uint32_t total_waves = (uint32_t)p.num_tiles * (uint32_t)p.num_slabs;
   const bool live_wave = wave < total_waves;
   if (!live_wave) wave = total_waves - 1;
+#if SCONV_FUSED_SLAB_MAJOR
+  const uint32_t slab_u = wave / (uint32_t)p.num_tiles;
+  const uint32_t tile = wave - slab_u * (uint32_t)p.num_tiles;
+  const int slab = (int)slab_u;
+#else
   const uint32_t tile = wave / (uint32_t)p.num_slabs;
   const int slab = (int)(wave - tile * (uint32_t)p.num_slabs);
+#endif
   const int64_t t0 = (int64_t)tile * BT;
 
   // Row metadata of the whole tile in one gather: lane L loads field L % F
@@ -494,8 +513,12 @@ static void launch(const FusedParams& p, uint32_t grid, uint32_t threads, hipStr
 template <typename D, int VEC, int W>
 static void launch_bt(int bt, const FusedParams& p, uint32_t g, uint32_t th, hipStream_t s) {
   switch (bt) {
+#if SCONV_FUSED_BT_MAX >= 16
     case 16: launch<D, VEC, W, 16>(p, g, th, s); break;
+#endif
+#if SCONV_FUSED_BT_MAX >= 8
     case 8: launch<D, VEC, W, 8>(p, g, th, s); break;
+#endif
     case 4: launch<D, VEC, W, 4>(p, g, th, s); break;
     default: launch<D, VEC, W, 1>(p, g, th, s); break;
   }
@@ -609,7 +632,7 @@ static int fused_launch(
 
   const int64_t waves = p.num_tiles * p.num_slabs;
   if (waves > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
-  const uint32_t threads = waves >= 4096 ? 256 : 64;
+  const uint32_t threads = waves >= 4096 ? SCONV_FUSED_WG_THREADS : 64;
   const int64_t grid = cdiv(waves, threads / 64);
   if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
   p.num_groups = (uint32_t)grid;
