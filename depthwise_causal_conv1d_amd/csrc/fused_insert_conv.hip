@@ -46,7 +46,7 @@ struct FusedParams {
   int32_t silu, residual;
   int32_t num_reqs;         // with qsl
   int32_t qsl_in_lds;       // offsets staged in dynamic LDS (else searched in memory)
-  int32_t pad0;
+  int32_t nt_x;             // host choice: streaming input loads (one wave generation)
   const void* x;
   const void* w;
   void* cache;
@@ -95,6 +95,18 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #ifndef SCONV_FUSED_NT_STORES
 #define SCONV_FUSED_NT_STORES 1    // streaming (non-temporal) out / cache stores
 #endif
+#ifndef SCONV_FUSED_NT_OUT
+#define SCONV_FUSED_NT_OUT SCONV_FUSED_NT_STORES
+#endif
+#ifndef SCONV_FUSED_NT_CACHE
+#define SCONV_FUSED_NT_CACHE SCONV_FUSED_NT_STORES
+#endif
+#ifndef SCONV_FUSED_NT_LOADS_MAX_WAVES
+#define SCONV_FUSED_NT_LOADS_MAX_WAVES 5120  // streaming x loads up to this many waves
+#endif
+#ifndef SCONV_FUSED_GROUP_STORES
+#define SCONV_FUSED_GROUP_STORES 0
+#endif
 #ifndef SCONV_FUSED_SLAB_MAJOR
 #define SCONV_FUSED_SLAB_MAJOR 1
 #endif
@@ -119,7 +131,8 @@ constexpr int kQslLds = 2;   // the offsets qsl, staged in LDS or searched in me
 constexpr int kQslRegMax = SCONV_FUSED_QSL_REG_MAX;
 static_assert(kQslRegMax <= 512, "8 offsets per lane");
 
-template <typename D, int VEC, int W, int BT, int QM>
+// NTX: input rows loaded as streaming (non-temporal) reads.
+template <typename D, int VEC, int W, int BT, int QM, bool NTX>
 __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParams p) {
   using S = typename D::storage;
   using P = Pack<D, VEC>;
@@ -205,7 +218,8 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 #pragma unroll
   for (int i = 0; i < BT; ++i) {
     const int64_t t = t0 + i < t_last ? t0 + i : t_last;
-    xr[i].load(x + t * p.x_rs + cl);
+    if constexpr (NTX) xr[i].load_nt(x + t * p.x_rs + cl);
+    else xr[i].load(x + t * p.x_rs + cl);
   }
   const int h = on ? c0 / p.ws : 0;
   const int j = c0 - h * p.ws;
@@ -217,17 +231,14 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   // chunks); the one-channel kernels read any strides.
   constexpr int kChunk = 16 / (int)sizeof(S);
   constexpr int kN = VEC * W;
+  constexpr int kNChunks = kN / kChunk > 0 ? kN / kChunk : 1;
+  Pack<D, kChunk> wpk[kNChunks];
   struct WRaw { S e[kN]; } wr;
   if constexpr (VEC > 1) {
     static_assert(kN % kChunk == 0, "packed weights come in whole 16-byte chunks");
 #pragma unroll
     for (int ch = 0; ch < kN / kChunk; ++ch) {
-      Pack<D, kChunk> pk;
-      pk.load(wt + (int64_t)cl * W + ch * kChunk);
-      typename Pack<D, kChunk>::Elems v =
-          __builtin_bit_cast(typename Pack<D, kChunk>::Elems, pk.raw);
-#pragma unroll
-      for (int q = 0; q < kChunk; ++q) wr.e[ch * kChunk + q] = v.e[q];
+      wpk[ch].load(wt + (int64_t)cl * W + ch * kChunk);
     }
   } else {
 #pragma unroll
@@ -376,6 +387,47 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   }
 
 
+  // Stores of row i (lanes past C store nothing): its output and its input
+  // row into the cache slot.
+  P outv[BT];
+  auto store_row = [&](int i) {
+    if (on) {
+      const int64_t t = t0 + i;
+#if SCONV_FUSED_NT_OUT
+      outv[i].store_nt(out + t * p.out_rs + c0);
+#else
+      outv[i].store(out + t * p.out_rs + c0);
+#endif
+      const uint32_t blk = div_n((uint32_t)slot[i], p);
+      const int32_t off = slot[i] - (int32_t)blk * p.N;
+#if SCONV_FUSED_NT_CACHE
+      xr[i].store_nt(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
+#else
+      xr[i].store(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
+#endif
+    }
+  };
+  // Output of row i from its fp32 accumulators: SiLU, residual, round.
+  auto finish = [&](int i, const float (&acc)[VEC]) {
+    float y[VEC];
+    {
+      float cur[VEC];
+      xr[i].to_float(cur);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float v = acc[e];
+        if (p.silu) v = silu(v);
+        if (p.residual) v += cur[e];
+        y[e] = v;
+      }
+    }
+    outv[i].from_float(y);
+#if !SCONV_FUSED_GROUP_STORES
+    store_row(i);
+#endif
+  };
+
+
   // History rows 1..W-1 of the current request, in named registers (an
   // array indexed by a run-time value would be demoted to LDS).
   P hist1, hist2, hist3;
@@ -431,7 +483,15 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
 #pragma unroll
-        for (int k = 0; k < W; ++k) wk[k][e] = to_float<D>(wr.e[e * W + k]);
+        for (int k = 0; k < W; ++k) {
+          if constexpr (VEC > 1) {
+            const int flat = e * W + k;
+            wk[k][e] = to_float<D>(__builtin_bit_cast(typename Pack<D, kChunk>::Elems,
+                                                      wpk[flat / kChunk].raw).e[flat % kChunk]);
+          } else {
+            wk[k][e] = to_float<D>(wr.e[k]);
+          }
+        }
     }
     if (slot[i] < 0) continue;  // PAD (or past T): no output, no insert
 
@@ -462,52 +522,43 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(wk[k][e], f[e], acc[e]);
     }
-    float y[VEC];
-    {
-      float cur[VEC];
-      xr[i].to_float(cur);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        float v = acc[e];
-        if (p.silu) v = silu(v);
-        if (p.residual) v += cur[e];
-        y[e] = v;
-      }
-    }
-    if (on) {
-      P o;
-      o.from_float(y);
-#if SCONV_FUSED_NT_STORES
-      o.store_nt(out + t * p.out_rs + c0);
-#else
-      o.store(out + t * p.out_rs + c0);
-#endif
-      const uint32_t blk = div_n((uint32_t)slot[i], p);
-      const int32_t off = slot[i] - (int32_t)blk * p.N;
-#if SCONV_FUSED_NT_STORES
-      xr[i].store_nt(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
-#else
-      xr[i].store(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
-#endif
-    }
+    finish(i, acc);
   }
+#if SCONV_FUSED_GROUP_STORES
+#pragma unroll
+  for (int i = 0; i < BT; ++i)
+    if (slot[i] >= 0) store_row(i);
+#endif
 }
 
 // ---------------------------------------------------------------- dispatch
 
-template <typename D, int VEC, int W, int BT>
-static void launch(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
+template <typename D, int VEC, int W, int BT, bool NTX>
+static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
   if (p.qsl && p.num_reqs <= kQslRegMax) {
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs>), dim3(grid),
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs, NTX>), dim3(grid),
                        dim3(threads), 0, s, p);
   } else if (p.qsl) {
     const size_t lds = p.qsl_in_lds ? (size_t)p.num_reqs * sizeof(int32_t) : 0;
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslLds>), dim3(grid),
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslLds, NTX>), dim3(grid),
                        dim3(threads), lds, s, p);
   } else {
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslOff>), dim3(grid),
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslOff, NTX>), dim3(grid),
                        dim3(threads), 0, s, p);
   }
+}
+
+// Streaming input loads are built only for the 16-byte-lane 4-row tiles,
+// the shape of launches large enough to fill the chip once.
+template <typename D, int VEC, int W, int BT>
+static void launch(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
+  if constexpr (VEC > 1 && BT == 4) {
+    if (p.nt_x) {
+      launch_q<D, VEC, W, BT, true>(p, grid, threads, s);
+      return;
+    }
+  }
+  launch_q<D, VEC, W, BT, false>(p, grid, threads, s);
 }
 
 template <typename D, int VEC, int W>
@@ -636,6 +687,11 @@ static int fused_launch(
   const int64_t grid = cdiv(waves, threads / 64);
   if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
   p.num_groups = (uint32_t)grid;
+  // Input rows are read once, except the last W-1 rows of a tile, which the
+  // next tile of the same slab reads again as its halo.  When all waves are
+  // resident at once the launch is latency-bound and streaming loads win;
+  // over several generations the halo re-reads must find the rows in L2.
+  p.nt_x = waves <= SCONV_FUSED_NT_LOADS_MAX_WAVES;
   p.waves_per_group = (int32_t)(threads / 64);
 
   if (dtype == SCONV_BF16) {

@@ -14,6 +14,14 @@
 #include "sconv_device.h"
 #include "sconv_host.h"
 
+#ifndef SCONV_GATHER_LDS_STORES
+#define SCONV_GATHER_LDS_STORES 1  // stores staged through LDS as 1 KB runs
+#endif
+#ifndef SCONV_GATHER_NT_STORES_LDS
+#define SCONV_GATHER_NT_STORES_LDS 1  // streaming stores for the 1 KB runs
+#endif
+
+
 namespace sconv {
 
 struct GatherParams {
@@ -22,7 +30,7 @@ struct GatherParams {
   const int32_t* real_count;
   void* out;
   int64_t seq_len, src_ss, src_sc, out_ss;
-  int32_t conv_dim, max_count, cblocks, out_chunked;
+  int32_t conv_dim, max_count, cblocks, out_chunked, threads;
 };
 
 template <typename D, int VEC, int DC>
@@ -30,14 +38,33 @@ __global__ __launch_bounds__(256) void gather_window_kernel(const GatherParams p
   using S = typename D::storage;
   const S* __restrict__ src = static_cast<const S*>(p.src);
   S* __restrict__ out = static_cast<S*>(p.out);
-  const int slot = (int)(blockIdx.x / (uint32_t)p.cblocks);
-  const int cb = (int)(blockIdx.x - (uint32_t)slot * p.cblocks);
+  const int slot = (int)blockIdx.y;  // grid: (channel blocks, max_count)
+  const int cb = (int)blockIdx.x;
+  // The live count and this slot's position are fetched together (slot <
+  // max_count, so its entry is always readable): one round trip, not two.
+  // Every kernel argument comes in the first scalar batch, and both values
+  // are in registers before the early exit (else the position load would be
+  // sunk below it).
+  asm volatile("" ::"s"(p.src), "s"(p.out), "s"(p.seq_len), "s"(p.src_ss), "s"(p.out_ss),
+               "s"(p.conv_dim), "s"(p.threads), "s"(p.max_count));
   int n = *p.real_count;
-  n = n < 0 ? 0 : (n > p.max_count ? p.max_count : n);
-  if (slot >= n) return;  // dead slot: no traffic
-  const int c0 = (cb * (int)blockDim.x + (int)threadIdx.x) * VEC;
-  if (c0 >= p.conv_dim) return;
   const int64_t pend = p.pos[slot];
+  asm volatile("" ::"v"(n), "v"(pend));
+  n = n < 0 ? 0 : (n > p.max_count ? p.max_count : n);
+  if (slot >= n) return;  // dead slot: no input or output traffic
+  int c0 = (cb * p.threads + (int)threadIdx.x) * VEC;
+  const bool lane_live = c0 < p.conv_dim;
+#if SCONV_GATHER_LDS_STORES
+  constexpr int kChunkE0 = 16 / (int)sizeof(S);
+  constexpr bool kLdsPath = VEC > 1 && (VEC * DC) % kChunkE0 == 0;
+#else
+  constexpr bool kLdsPath = false;
+#endif
+  if constexpr (!kLdsPath) {
+    if (!lane_live) return;
+  } else {
+    if (!lane_live) c0 = 0;  // loads a valid row; stores nothing
+  }
 
   struct OutElems { S e[VEC * DC]; } oe;  // [c][k], k fastest
 #pragma unroll
@@ -55,8 +82,56 @@ __global__ __launch_bounds__(256) void gather_window_kernel(const GatherParams p
     for (int e = 0; e < VEC; ++e) oe.e[e * DC + k] = v.e[e];
   }
 
-  S* dst = out + (int64_t)slot * p.out_ss + (int64_t)c0 * DC;
   constexpr int kChunkE = 16 / (int)sizeof(S);
+#if SCONV_GATHER_LDS_STORES
+  if constexpr (kLdsPath) {
+    if (p.out_chunked) {
+      // The wave's output is one contiguous run of 64 * VEC * DC elements
+      // (the lanes' channels are consecutive).  Each lane parks its VEC*DC
+      // elements in LDS and reads back the 16-byte chunks it stores, so
+      // every store instruction writes 1 KB of consecutive bytes.
+      constexpr int kPer = VEC * DC / kChunkE;  // chunks per lane
+      using Chunk = typename Pack<D, kChunkE>::raw_t;
+      __shared__ Chunk lds[256 / 64][64 * kPer];
+      Chunk* wl = lds[threadIdx.x >> 6];
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int ch = 0; ch < kPer; ++ch) {
+        typename Pack<D, kChunkE>::Elems v;
+#pragma unroll
+        for (int q = 0; q < kChunkE; ++q) v.e[q] = oe.e[ch * kChunkE + q];
+        wl[lane * kPer + ch] = __builtin_bit_cast(Chunk, v);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Live lanes are a prefix of the wave; so are their chunks.
+      const int wave_c0 = (cb * p.threads + (int)(threadIdx.x & ~63)) * VEC;
+      const int live = (p.conv_dim - wave_c0) / VEC;  // live lanes (may exceed 64)
+      const int nchunks = (live < 64 ? live : 64) * kPer;
+      S* wdst = out + (int64_t)slot * p.out_ss + (int64_t)wave_c0 * DC;
+      Chunk back[kPer];  // read every chunk first (always in the LDS array), then store
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) back[r] = wl[r * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int idx = r * 64 + lane;
+        if (idx < nchunks) {
+          Pack<D, kChunkE> pk;
+          pk.raw = back[r];
+#if SCONV_GATHER_NT_STORES_LDS
+          pk.store_nt(wdst + (int64_t)idx * kChunkE);
+#else
+          pk.store(wdst + (int64_t)idx * kChunkE);
+#endif
+        }
+      }
+      return;
+    }
+    if (!lane_live) return;
+  }
+#endif
+  S* dst = out + (int64_t)slot * p.out_ss + (int64_t)c0 * DC;
   constexpr bool kChunked = (VEC * DC) % kChunkE == 0;
   if constexpr (kChunked) {
     if (p.out_chunked) {
@@ -77,12 +152,12 @@ __global__ __launch_bounds__(256) void gather_window_kernel(const GatherParams p
 }
 
 template <typename D, int VEC>
-static void launch_gather(int dc, const GatherParams& p, uint32_t g, uint32_t th, hipStream_t s) {
+static void launch_gather(int dc, const GatherParams& p, dim3 g, uint32_t th, hipStream_t s) {
   switch (dc) {
-    case 1: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 1>), dim3(g), dim3(th), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 2>), dim3(g), dim3(th), 0, s, p); break;
-    case 3: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 3>), dim3(g), dim3(th), 0, s, p); break;
-    default: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 4>), dim3(g), dim3(th), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 1>), g, dim3(th), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 2>), g, dim3(th), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 3>), g, dim3(th), 0, s, p); break;
+    default: hipLaunchKernelGGL((gather_window_kernel<D, VEC, 4>), g, dim3(th), 0, s, p); break;
   }
 }
 
@@ -105,6 +180,8 @@ extern "C" int gather_intermediate_conv_window(const void* src, int64_t seq_len,
     return fail(SCONV_ERR_INVALID, "%s: conv_dim and max_count must be >= 0", fn);
   if (d_conv < 1 || d_conv > 4)
     return fail(SCONV_ERR_UNSUPPORTED, "%s: d_conv=%d outside [1, 4]", fn, d_conv);
+  if (max_count > 65535)
+    return fail(SCONV_ERR_UNSUPPORTED, "%s: max_count above 65535 (one grid row per slot)", fn);
   if (conv_dim == 0 || max_count == 0) return SCONV_OK;
   if (!src || !abs_positions || !real_count_dev || !out)
     return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
@@ -122,14 +199,14 @@ extern "C" int gather_intermediate_conv_window(const void* src, int64_t seq_len,
   p.out_chunked = aligned16(out) && out_slot_stride % vec16 == 0 && vec;
   const uint32_t th = (int64_t)conv_dim >= 256 * VEC ? 256 : 64;
   p.cblocks = (int32_t)cdiv(conv_dim, (int64_t)th * VEC);
-  const int64_t grid = (int64_t)max_count * p.cblocks;
-  if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  p.threads = (int32_t)th;
+  const dim3 grid((uint32_t)p.cblocks, (uint32_t)max_count);
   if (dtype == SCONV_BF16) {
-    if (vec) launch_gather<Bf16, 8>(d_conv, p, (uint32_t)grid, th, stream);
-    else launch_gather<Bf16, 1>(d_conv, p, (uint32_t)grid, th, stream);
+    if (vec) launch_gather<Bf16, 8>(d_conv, p, grid, th, stream);
+    else launch_gather<Bf16, 1>(d_conv, p, grid, th, stream);
   } else {
-    if (vec) launch_gather<F32, 4>(d_conv, p, (uint32_t)grid, th, stream);
-    else launch_gather<F32, 1>(d_conv, p, (uint32_t)grid, th, stream);
+    if (vec) launch_gather<F32, 4>(d_conv, p, grid, th, stream);
+    else launch_gather<F32, 1>(d_conv, p, grid, th, stream);
   }
   return check_launch(fn);
 }

@@ -48,6 +48,10 @@ struct Pack {
   __device__ __forceinline__ void store(S* p) const {
     *reinterpret_cast<raw_t*>(p) = raw;
   }
+  // Streaming load: these bytes are read once.
+  __device__ __forceinline__ void load_nt(const S* p) {
+    raw = __builtin_nontemporal_load(reinterpret_cast<const raw_t*>(p));
+  }
   // Streaming store: nothing will read these bytes again in this kernel.
   __device__ __forceinline__ void store_nt(S* p) const {
     __builtin_nontemporal_store(raw, reinterpret_cast<raw_t*>(p));

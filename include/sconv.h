@@ -256,7 +256,8 @@ int causal_conv1d_update(const void* x, int64_t x_stride_b, void* conv_states,
  * 0, seq_len - 1), c]  (bit copies).  Slots i >= n are not written.
  *
  * Host errors (SCONV_ERR_INVALID): seq_len < 1, conv_dim < 0, max_count < 0,
- * NULL pointer, unknown dtype.  d_conv outside [1, 4]: SCONV_ERR_UNSUPPORTED.
+ * NULL pointer, unknown dtype.  SCONV_ERR_UNSUPPORTED: d_conv outside [1, 4],
+ * max_count above 65535 (each slot is one row of the launch grid).
  */
 int gather_intermediate_conv_window(const void* src, int64_t seq_len, int32_t conv_dim,
                                     int64_t src_stride_s, int64_t src_stride_c,

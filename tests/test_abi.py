@@ -106,6 +106,8 @@ def test_ssm_ops_reject_bad_scalars(lib):
     assert g(NULL, 10, 8, 8, 1, NULL, NULL, 4, NULL, 24, 5, 1, NULL) == 2   # d_conv 5
     assert g(NULL, 0, 8, 8, 1, NULL, NULL, 4, NULL, 24, 3, 1, NULL) == 1    # seq_len 0
     assert g(NULL, 10, 8, 8, 1, NULL, NULL, 0, NULL, 24, 3, 1, NULL) == 0   # no slots
+    assert g(NULL, 10, 8, 8, 1, NULL, NULL, 65536, NULL, 24, 3, 1, NULL) == 2  # grid rows
+    assert b"65535" in lib.sconv_last_error()
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
