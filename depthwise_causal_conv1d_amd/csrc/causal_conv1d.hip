@@ -25,6 +25,9 @@ namespace sconv {
 #ifndef SCONV_VARLEN_GROUP
 #define SCONV_VARLEN_GROUP 4       // chunks loaded together per wave
 #endif
+#ifndef SCONV_VARLEN_NT_LOADS
+#define SCONV_VARLEN_NT_LOADS 1    // streaming loads of the inputs (read once)
+#endif
 #ifndef SCONV_VARLEN_NT_STORES
 #define SCONV_VARLEN_NT_STORES 1   // streaming stores of the outputs
 #endif
@@ -58,7 +61,11 @@ __device__ __forceinline__ Pack<D, VEC> load_span(const typename D::storage* row
   Pack<D, VEC> pk;
   if (tk >= lo && tk + VEC <= hi) {
     if constexpr (VEC > 1) {
+#if SCONV_VARLEN_NT_LOADS
+      pk.load_nt(row + tk);
+#else
       pk.load(row + tk);
+#endif
     } else {
       pk.load(row + tk * stride);
     }

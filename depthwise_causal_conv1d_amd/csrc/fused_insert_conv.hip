@@ -45,7 +45,6 @@ struct FusedParams {
   uint32_t n_magic, n_s1, n_s2;
   int32_t silu, residual;
   int32_t num_reqs;         // with qsl
-  int32_t qsl_in_lds;       // offsets staged in dynamic LDS (else searched in memory)
   int32_t nt_x;             // host choice: streaming input loads (one wave generation)
   const void* x;
   const void* w;
@@ -67,9 +66,9 @@ struct FusedParams {
 // spaced offsets of the remaining span, and since the offsets are
 // non-decreasing the lanes that see off <= t form a prefix whose length
 // (ballot + popcount) names the sub-span to keep.  Two rounds cover 4096
-// requests.  `off` is LDS or global memory; the result is wave-uniform.
-template <typename Ptr>
-__device__ __forceinline__ int32_t find_request(Ptr off, int32_t n, int64_t t, int lane) {
+// requests, three cover 262144.  The result is wave-uniform.
+__device__ __forceinline__ int32_t find_request(const int32_t* off, int32_t n, int64_t t,
+                                                int lane) {
   int32_t base = 0, span = n;
   while (span > 1) {
     const int32_t stride = (span + 63) >> 6;
@@ -123,7 +122,7 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 // Where a row's request and request start come from (template QM).
 constexpr int kQslOff = 0;   // the per-row seq_idx / query_start buffers
 constexpr int kQslRegs = 1;  // the offsets qsl, read whole into registers
-constexpr int kQslLds = 2;   // the offsets qsl, staged in LDS or searched in memory
+constexpr int kQslSearch = 2;  // the offsets qsl, searched in device memory
 #ifndef SCONV_FUSED_QSL_REG_MAX
 #define SCONV_FUSED_QSL_REG_MAX 512
 #endif
@@ -158,8 +157,7 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 #endif
                   (uint32_t)uniform(threadIdx.x >> 6);
   // A wave past the end works on the last tile and writes nothing (no early
-  // return: it would also split the parameter loads around the branch, and
-  // with offsets staged in LDS every wave must reach the barrier).
+  // return: it would split the parameter loads around the branch).
   const uint32_t total_waves = (uint32_t)p.num_tiles * (uint32_t)p.num_slabs;
   const bool live_wave = wave < total_waves;
   if (!live_wave) wave = total_waves - 1;
@@ -323,29 +321,18 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
       }
     }
   }
-  if constexpr (QM == kQslLds) {
-    // Request of each row from the offsets: the workgroup stages them in LDS
-    // once (after the loads above are issued).  Each wave searches for the
-    // request r0 of its first row, reads the 64 offsets from r0 on in one
-    // access, and every row's request is r0 plus the count of those offsets
-    // <= row, less one.  Only when 64 request starts fall inside one tile
-    // (empty requests) can a row lie past that window; such a row searches
-    // on its own.
-    extern __shared__ int32_t s_qsl[];
+  if constexpr (QM == kQslSearch) {
+    // More requests than fit in registers: each wave searches device memory
+    // for the request r0 of its first row, reads the 64 offsets from r0 on
+    // in one access, and every row's request is r0 plus the count of those
+    // offsets <= row, less one.  Only when 64 request starts fall inside one
+    // tile (empty requests) can a row lie past that window; such a row
+    // searches on its own.  (Staging the offsets in LDS per workgroup was
+    // measured slower: it moves every offset to every workgroup.)
     const int32_t n = p.num_reqs;
-    if (p.qsl_in_lds) {
-      for (int r = threadIdx.x; r < n; r += p.waves_per_group * 64) s_qsl[r] = p.qsl[r];
-      __syncthreads();
-    }
     const int64_t tf = t0 < t_last ? t0 : t_last;
-    int32_t r0, wnd;
-    if (p.qsl_in_lds) {
-      r0 = find_request(s_qsl, n, tf, lane);
-      wnd = s_qsl[r0 + lane < n ? r0 + lane : n - 1];
-    } else {
-      r0 = find_request(p.qsl, n, tf, lane);
-      wnd = p.qsl[r0 + lane < n ? r0 + lane : n - 1];
-    }
+    const int32_t r0 = find_request(p.qsl, n, tf, lane);
+    const int32_t wnd = p.qsl[r0 + lane < n ? r0 + lane : n - 1];
     const bool in_window = lane < n - r0;
     const bool beyond = r0 + 64 < n;
 #pragma unroll
@@ -356,13 +343,8 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
       req[i] = r0 + k;
       qs[i] = __builtin_amdgcn_readlane(wnd, k);
       if (k == 63 && beyond && slot[i] >= 0) {
-        if (p.qsl_in_lds) {
-          req[i] = find_request(s_qsl, n, t, lane);
-          qs[i] = uniform(s_qsl[req[i]]);
-        } else {
-          req[i] = find_request(p.qsl, n, t, lane);
-          qs[i] = uniform(p.qsl[req[i]]);
-        }
+        req[i] = find_request(p.qsl, n, t, lane);
+        qs[i] = uniform(p.qsl[req[i]]);
       }
     }
   }
@@ -539,9 +521,8 @@ static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipS
     hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs, NTX>), dim3(grid),
                        dim3(threads), 0, s, p);
   } else if (p.qsl) {
-    const size_t lds = p.qsl_in_lds ? (size_t)p.num_reqs * sizeof(int32_t) : 0;
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslLds, NTX>), dim3(grid),
-                       dim3(threads), lds, s, p);
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslSearch, NTX>), dim3(grid),
+                       dim3(threads), 0, s, p);
   } else {
     hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslOff, NTX>), dim3(grid),
                        dim3(threads), 0, s, p);
@@ -657,10 +638,6 @@ static int fused_launch(
   p.seq_idx = seq_idx; p.slot = slot_mapping; p.qs = query_start; p.out = out;
   p.qsl = qsl;
   p.num_reqs = qsl ? num_reqs : 0;
-  // Offsets of up to 4096 requests (16 KB) are staged in LDS; beyond that
-  // each wave searches them in memory (the separate metadata launch is then
-  // the faster choice for the caller).
-  p.qsl_in_lds = qsl && num_reqs <= 4096;
   p.x_rs = x_row_stride; p.w_sc = w_stride_c; p.w_sk = w_stride_k;
   p.cs0 = cs0; p.cs1 = cs1; p.cs2 = cs2; p.bt_rs = bt_row_stride; p.out_rs = out_row_stride;
   p.T = T;

@@ -146,9 +146,9 @@ int sconv_fused_insert_conv(const void* x, int64_t x_row_stride,
  *
  * Each non-PAD row t belongs to the last request r with qsl[r] <= t (rows
  * past qsl[num_reqs] clamp to the last request), and query_start = qsl[r].
- * Each workgroup stages the offsets in LDS when num_reqs <= 4096; larger
- * batches search them in device memory, where one sconv_seq_metadata launch
- * plus sconv_fused_insert_conv is faster.
+ * Up to 512 requests the offsets are read whole into registers; larger
+ * batches are searched in device memory once per row tile.  The launch
+ * allocates nothing and needs no LDS.
  *
  * Errors: as sconv_fused_insert_conv, plus SCONV_ERR_INVALID for
  * num_reqs < 1 (or a NULL query_start_loc) with T > 0.

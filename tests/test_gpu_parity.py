@@ -152,8 +152,8 @@ def test_config_batched_decode(fold):
 
 
 def test_folded_search_beyond_lds():
-    """More requests than the in-LDS limit: the folded launch searches the
-    offsets in device memory; empty requests included."""
+    """5000 requests (past the 512 held in registers): the folded launch
+    searches the offsets in device memory; empty requests included."""
     g = torch.Generator().manual_seed(23)
     R = 5000
     new = [int(v) for v in torch.randint(0, 3, (R,), generator=g)]
@@ -164,27 +164,30 @@ def test_folded_search_beyond_lds():
     check_fused(case, "5000 requests, in-memory search", fold=True)
 
 
-@pytest.mark.parametrize("run_len,runs", [(100, 8), (600, 7)], ids=["lds", "memory"])
-def test_folded_empty_request_runs(run_len, runs):
-    """Runs of >= 64 empty requests between two rows of one 8-row tile: a
-    row past such a run lies beyond the 64 offsets a wave reads after its
-    first row's request and must be found on its own.  About 4100 rows
-    over 4096 channels (8 slabs) select 8-row tiles; 2300 requests keep the
-    offsets in LDS, 5700 push the search into device memory."""
-    rng = np.random.default_rng(run_len)
-    new = [int(v) for v in rng.integers(1, 6, 1500)]
+@pytest.mark.parametrize("run_len,runs,live,lens", [(100, 2, 300, (5, 11)),
+                                                    (100, 8, 1500, (1, 6)),
+                                                    (600, 7, 1500, (1, 6))],
+                         ids=["registers-500", "search-2300", "search-5700"])
+def test_folded_empty_request_runs(run_len, runs, live, lens):
+    """Runs of >= 64 empty requests between two rows of one 4-row tile.  With
+    up to 512 requests the folded launch counts offsets held in registers;
+    above that a wave searches device memory once and reads 64 offsets from
+    its first row's request on, so a row past such a run lies beyond that
+    window and must be found on its own.  Over 4096 channels (8 slabs) and
+    more than 2048 rows the launch uses 4-row tiles; each run is inserted
+    before a request whose first row is not a tile's first."""
+    rng = np.random.default_rng(run_len + runs)
+    new = [int(v) for v in rng.integers(lens[0], lens[1], live)]
     T = sum(new)
-    assert T >= 4100
+    assert T > 2048
     starts = np.cumsum([0] + new[:-1])
-    # Insert each run before a request whose first row is not a tile's first.
-    cand = [r for r in range(1, 1500) if starts[r] % 8 != 0]
+    cand = [r for r in range(1, live) if starts[r] % 4 != 0]
     where = sorted(rng.choice(cand, runs, replace=False).tolist(), reverse=True)
     for r in where:
         new[r:r] = [0] * run_len
     ctx = [int(v) for v in rng.integers(0, 40, len(new))]
     case = workloads.fused_case(31 + run_len, new, ctx, H=32, D=128, ws=128, off_s=0,
-                                block_size=16, W=4, dtype=torch.bfloat16, pad_count=9,
-                                tail_pad=2)
+                                block_size=16, W=4, dtype=torch.bfloat16)
     check_fused(case, f"{len(new)} requests, runs of {run_len} empty", fold=True)
 
 
