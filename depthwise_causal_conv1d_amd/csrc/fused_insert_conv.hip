@@ -106,6 +106,9 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #ifndef SCONV_FUSED_GROUP_STORES
 #define SCONV_FUSED_GROUP_STORES 0
 #endif
+#ifndef SCONV_FUSED_LDS_HALO
+#define SCONV_FUSED_LDS_HALO 1  // halo rows passed between the waves of a workgroup
+#endif
 #ifndef SCONV_FUSED_SLAB_MAJOR
 #define SCONV_FUSED_SLAB_MAJOR 1
 #endif
@@ -353,19 +356,47 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   // same-forward tap.
   constexpr int kHalo = W > 1 ? W - 1 : 1;
   P halo[kHalo];
+  // In slab-major order the waves of a workgroup hold consecutive tiles of
+  // one slab, so a wave's halo rows are the previous wave's last rows:
+  // each wave leaves its last W-1 rows in LDS and, after one barrier, the
+  // next wave takes them from there instead of reading them again through
+  // L2.  The first wave of a workgroup, and a wave whose tile is the first
+  // of its slab, still load their halo.  Only launches of several wave
+  // generations do this: when all waves are resident at once, the barrier
+  // would hold back the history lookups that bound such launches.
+#if SCONV_FUSED_LDS_HALO && SCONV_FUSED_SLAB_MAJOR
+  constexpr bool kLdsHalo = !NTX && W > 1 && BT >= W - 1;
+#else
+  constexpr bool kLdsHalo = false;
+#endif
+  constexpr int kWavesMax = 256 / 64;
+  __shared__ typename P::raw_t s_halo[kLdsHalo ? kWavesMax : 1][kHalo][64];
+  const int wig = (int)(threadIdx.x >> 6);  // wave in workgroup
+  bool halo_from_lds = false;
+  if constexpr (kLdsHalo) {
 #pragma unroll
-  for (int m = 1; m <= kHalo; ++m) {
-    bool need = false;
-    if (m <= W - 1) {
+    for (int m = 1; m <= W - 1; ++m) s_halo[wig][m - 1][lane] = xr[BT - m].raw;
+    __syncthreads();
+    halo_from_lds = wig > 0 && tile > 0;
+  }
+  if (halo_from_lds) {
 #pragma unroll
-      for (int i = 0; i < BT && i <= W - 1 - m; ++i)
-        need |= slot[i] >= 0 && pos[i] - (i + m) >= 0 && t0 - m >= (int64_t)qs[i] && t0 - m >= 0;
+    for (int m = 1; m <= W - 1; ++m) halo[m - 1].raw = s_halo[kLdsHalo ? wig - 1 : 0][m - 1][lane];
+  } else {
+#pragma unroll
+    for (int m = 1; m <= kHalo; ++m) {
+      bool need = false;
+      if (m <= W - 1) {
+#pragma unroll
+        for (int i = 0; i < BT && i <= W - 1 - m; ++i)
+          need |= slot[i] >= 0 && pos[i] - (i + m) >= 0 && t0 - m >= (int64_t)qs[i] && t0 - m >= 0;
+      }
+      // Loaded only where read (the tap choice below reads halo m exactly
+      // for the rows counted in `need`), and left unset otherwise: merging
+      // with a default value would make the wave wait for the load right
+      // here, in front of the history lookups.
+      if (need && on) halo[m - 1].load(x + (t0 - m) * p.x_rs + c0);
     }
-    // Loaded only where read (the tap choice below reads halo m exactly
-    // for the rows counted in `need`), and left unset otherwise: merging
-    // with a default value would make the wave wait for the load right
-    // here, in front of the history lookups.
-    if (need && on) halo[m - 1].load(x + (t0 - m) * p.x_rs + c0);
   }
 
 
