@@ -116,6 +116,42 @@ def fused_algorithmic_bytes(case, rows=None) -> int:
     return (x_rows + taps + 2 * n_live) * C * e + C * W * e + 24 * (hi - lo) + 4 * bt_entries
 
 
+def fused_streams_algorithmic_bytes(cases, rows=None) -> int:
+    """Bytes one multi-stream launch must move: every stream's own bytes
+    (fused_algorithmic_bytes), with the per-row metadata and the block-table
+    entries, which the streams share, counted once."""
+    c0 = cases[0]
+    lo, hi = rows if rows is not None else (0, c0.T)
+    shared = 24 * (hi - lo) + _bt_bytes(c0, rows)
+    return sum(fused_algorithmic_bytes(c, rows) for c in cases) - (len(cases) - 1) * shared
+
+
+def _bt_bytes(case, rows=None) -> int:
+    """4 bytes per block-table entry the taps follow (as in
+    fused_algorithmic_bytes)."""
+    W, N = case.W, case.block_size
+    pos = case.positions.numpy()
+    sm = case.slot_mapping.numpy()
+    qsl = case.query_start_loc.numpy()
+    lo, hi = rows if rows is not None else (0, case.T)
+    n = 0
+    for r in range(case.num_reqs):
+        a, b = max(int(qsl[r]), lo), min(int(qsl[r + 1]), hi)
+        if a >= b:
+            continue
+        first = int(pos[int(qsl[r])])
+        tapped = set()
+        for t in range(a, b):
+            if sm[t] < 0:
+                continue
+            for lag in range(1, W):
+                src = int(pos[t]) - lag
+                if src >= 0 and t - lag < int(qsl[r]) and src < first:
+                    tapped.add(src)
+        n += len({p // N for p in tapped})
+    return 4 * n
+
+
 def sub_case(case, rows, reqs, poison):
     """The requests `reqs` (rows `rows`) of a multi-batch case as a case of
     their own, for the oracle."""
@@ -233,21 +269,104 @@ class DecodeBench(Workload):
         return done / spent, f"{i} decode sub-batches of 256 requests ({done} tokens)", spent
 
 
+class DecodeLayerBench(Workload):
+    """Batched decode of all four conv streams of one layer (ws = 32 each,
+    D = 128): one launch per step for the four streams, or one per stream."""
+
+    STREAMS = [(0, 32), (32, 32), (64, 32), (96, 32)]
+
+    def __init__(self, dev="cuda", requests: int = 256, one_launch: bool = True):
+        import torch
+
+        import depthwise_causal_conv1d_amd as lib
+        import workloads
+        self.lib = lib
+        self.one_launch = one_launch
+        self.B = B = requests
+        per_batch = 4 * B * 12_350
+        self.R = max(2, -(-FLUSH_BYTES // per_batch) + 4 * (B <= 256))
+        t = time.time()
+        g = torch.Generator().manual_seed(6)
+        ctx = [int(v) for v in torch.randint(1, 4097, (B * self.R,), generator=g)]
+        self.cases = workloads.fused_streams_case(
+            6, [1] * (B * self.R), ctx, H=32, D=128, streams=self.STREAMS, block_size=16, W=4,
+            dtype="bf16", pool_blocks=int(B * self.R * 2 * 1.25) + 1, device=dev)
+        c = self.cases[0]
+        log(f"decode_layer: {self.R} batches of {B} requests x 4 streams in "
+            f"{time.time() - t:.1f}s, cache {c.cache.numel() * c.cache.element_size() / 2**30:.1f} GiB")
+        self.xs = [k.x.to(dev) for k in self.cases]
+        self.ws_ = [k.weight.to(dev) for k in self.cases]
+        self.cache = c.cache
+        self.pos, self.sm, self.bt = c.positions.to(dev), c.slot_mapping.to(dev), c.block_table.to(dev)
+        self.outs = [torch.empty_like(x) for x in self.xs]
+        self.qsl = torch.arange(B + 1, dtype=torch.int32, device=dev)
+        self.bytes_per_launch = (fused_streams_algorithmic_bytes(self.cases, (0, B))
+                                 if one_launch else fused_algorithmic_bytes(c, (0, B)))
+        self.tokens_per_step = B
+
+    def rows(self, i):
+        return slice(i * self.B, (i + 1) * self.B)
+
+    def kernel(self, i):
+        s, c = self.rows(i), self.cases[0]
+        if self.one_launch:
+            self.lib.sconv_fused_insert_conv_streams(
+                [x[s] for x in self.xs], self.ws_, self.cache, self.pos[s], self.bt[s],
+                self.sm[s], [o for o, _ in self.STREAMS], [w for _, w in self.STREAMS],
+                c.block_size, "silu", True, query_start_loc=self.qsl, num_reqs=self.B,
+                outs=[o[s] for o in self.outs])
+            return
+        for k, (off, ws) in enumerate(self.STREAMS):
+            self.lib.sconv_fused_insert_conv_qsl(self.xs[k][s], self.ws_[k], self.cache,
+                                                 self.pos[s], self.bt[s], self.qsl, self.B,
+                                                 self.sm[s], off, ws, c.block_size, "silu", True,
+                                                 out=self.outs[k][s])
+
+    def kernels_per_call(self):
+        return 1 if self.one_launch else 4
+
+    def step(self, i):
+        self.kernel(i)
+
+    def config(self):
+        return {"workload": "decode_layer", "requests": self.B, "tokens_per_step": self.B,
+                "streams": 4, "stream_launches": "one launch for all 4 streams"
+                if self.one_launch else "one launch per stream",
+                "metadata": "folded into the fused launch", "history": "uniform[1,4096]",
+                "H": 32, "D": 128, "ws": 32, "C_per_stream": 1024, "W": 4, "block_size": 16,
+                "activation": "silu", "residual": True, "graph": "hipGraph", "replicas": self.R}
+
+    def oracle_sample(self, budget):
+        # Whole sub-batches of 256 requests x 4 streams, until the budget is spent.
+        done, spent, i = 0, 0.0, 0
+        n_sub = self.R * self.B // 256
+        while i < n_sub and (spent < budget or done == 0):
+            rows = slice(256 * i, 256 * (i + 1))
+            for k in self.cases:
+                sub = sub_case(k, rows, rows, k.poison_block)
+                spent += time_oracle_fused(sub)
+            done += 256
+            i += 1
+        return done / spent, f"{i} decode sub-batches of 256 requests x 4 streams ({done} tokens)", spent
+
+
 class MixedPrefillBench(Workload):
     """Four streams of one layer convolved in turn over one shared cache."""
 
-    def __init__(self, dev="cuda", fold: bool = False):
+    def __init__(self, dev="cuda", fold: bool = False, one_launch: bool = False):
         import torch
 
         import depthwise_causal_conv1d_amd as lib
         import workloads
         self.lib = lib
         self.fold = fold
+        self.one_launch = one_launch
         t = time.time()
         self.streams = workloads.mixed_prefill_streams()
         b = self.streams[0]
         log(f"mixed_prefill: T={b.T} generated in {time.time() - t:.1f}s")
-        self.bytes_per_launch = fused_algorithmic_bytes(b)
+        self.bytes_per_launch = (fused_streams_algorithmic_bytes(self.streams) if one_launch
+                                 else fused_algorithmic_bytes(b))
         self.R = 1   # one step moves ~4 x bytes_per_launch >> MALL
         self.cache = b.cache.to(dev)
         self.xs = [s.x.to(dev) for s in self.streams]
@@ -262,6 +381,14 @@ class MixedPrefillBench(Workload):
 
     def kernel(self, i):
         b = self.streams[0]
+        if self.one_launch:
+            meta = (dict(query_start_loc=self.qsl, num_reqs=b.num_reqs) if self.fold
+                    else dict(seq_idx=self.si, query_start=self.qs))
+            self.lib.sconv_fused_insert_conv_streams(
+                self.xs, self.ws_, self.cache, self.pos, self.bt, self.sm,
+                [st.off_s for st in self.streams], [st.ws for st in self.streams],
+                b.block_size, "silu", True, outs=self.outs, **meta)
+            return
         for s, st in enumerate(self.streams):
             if self.fold:
                 self.lib.sconv_fused_insert_conv_qsl(self.xs[s], self.ws_[s], self.cache, self.pos,
@@ -274,7 +401,7 @@ class MixedPrefillBench(Workload):
                                              b.block_size, "silu", True, out=self.outs[s])
 
     def kernels_per_call(self):
-        return 4
+        return 1 if self.one_launch else 4
 
     def step(self, i):
         b = self.streams[0]
@@ -286,6 +413,8 @@ class MixedPrefillBench(Workload):
         b = self.streams[0]
         return {"workload": "mixed_prefill", "requests": 16, "rows": b.T,
                 "metadata": "folded into the fused launches" if self.fold else "separate launch",
+                "stream_launches": "one launch for all 4 streams" if self.one_launch
+                else "one launch per stream",
                 "non_pad_tokens": self.live, "streams": 4, "H": 32, "D": 512, "ws": 128,
                 "C": 4096, "W": 4, "block_size": 16, "pad_fraction": 0.1,
                 "activation": "silu", "residual": True}
@@ -481,14 +610,15 @@ def torch_where(mask):
 
 WORKLOADS = {
     "batched_decode": DecodeBench,
+    "decode_layer": DecodeLayerBench,
     "mixed_prefill": MixedPrefillBench,
     "spec_decode": SpecDecodeBench,
     "ssm_prefill": SsmPrefillBench,
     "ssm_decode": SsmDecodeBench,
 }
 
-DEFAULT_STEPS = {"batched_decode": 19200, "mixed_prefill": 200, "spec_decode": 2000,
-                 "ssm_prefill": 200, "ssm_decode": 6400}
+DEFAULT_STEPS = {"batched_decode": 19200, "decode_layer": 9600, "mixed_prefill": 200,
+                 "spec_decode": 2000, "ssm_prefill": 200, "ssm_decode": 6400}
 
 
 # ---------------------------------------------------------------- timing
@@ -516,7 +646,12 @@ def main():
                          "the faster per step: folded for decode and spec decode, separate for "
                          "the 4-stream prefill (one metadata launch serves four streams)")
     ap.add_argument("--requests", type=int, default=256,
-                    help="batched_decode only: requests per decode batch (batch-size sweep)")
+                    help="batched_decode and decode_layer: requests per decode batch")
+    ap.add_argument("--stream-launches", choices=("auto", "one", "separate"), default="auto",
+                    help="decode_layer and mixed_prefill: all four streams of the layer in one "
+                         "sconv_fused_insert_conv_streams launch, or one launch per stream; "
+                         "auto: one for decode_layer, separate (the configured four calls) "
+                         "for mixed_prefill")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "reference for hardware byte counters)")
@@ -542,9 +677,15 @@ def main():
         del src, dst, evict
     fold = (args.metadata == "folded" or
             (args.metadata == "auto" and args.workload in ("batched_decode", "spec_decode")))
+    one = (args.stream_launches == "one" or
+           (args.stream_launches == "auto" and args.workload == "decode_layer"))
     if args.workload == "batched_decode":
         wl = DecodeBench(requests=args.requests, fold=fold)
-    elif args.workload in ("mixed_prefill", "spec_decode"):
+    elif args.workload == "decode_layer":
+        wl = DecodeLayerBench(requests=args.requests, one_launch=one)
+    elif args.workload == "mixed_prefill":
+        wl = MixedPrefillBench(fold=fold, one_launch=one)
+    elif args.workload == "spec_decode":
         wl = WORKLOADS[args.workload](fold=fold)
     else:
         wl = WORKLOADS[args.workload]()

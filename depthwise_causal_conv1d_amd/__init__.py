@@ -12,6 +12,7 @@ from .ops import (
     gather_intermediate_conv_window,
     sconv_fused_insert_conv,
     sconv_fused_insert_conv_qsl,
+    sconv_fused_insert_conv_streams,
     sconv_seq_metadata,
 )
 
@@ -24,5 +25,6 @@ __all__ = [
     "gather_intermediate_conv_window",
     "sconv_fused_insert_conv",
     "sconv_fused_insert_conv_qsl",
+    "sconv_fused_insert_conv_streams",
     "sconv_seq_metadata",
 ]

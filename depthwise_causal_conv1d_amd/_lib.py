@@ -25,6 +25,7 @@ EXPORTS = (
     "sconv_seq_metadata",
     "sconv_fused_insert_conv",
     "sconv_fused_insert_conv_qsl",
+    "sconv_fused_insert_conv_streams",
     "causal_conv1d_varlen_fwd",
     "causal_conv1d_update",
     "gather_intermediate_conv_window",
@@ -34,6 +35,14 @@ P = ctypes.c_void_p
 I32 = ctypes.c_int32
 I64 = ctypes.c_int64
 
+
+class StreamT(ctypes.Structure):
+    """sconv_stream_t of include/sconv.h (one conv stream of a layer)."""
+    _fields_ = [("x", P), ("x_row_stride", I64), ("weight", P), ("w_stride_c", I64),
+                ("w_stride_k", I64), ("out", P), ("out_row_stride", I64), ("off_s", I32),
+                ("ws", I32), ("activation", I32), ("use_residual", I32)]
+
+
 _SIGS = {
     "sconv_seq_metadata": [P, I32, I64, I64, P, I64, P, I64, P],
     "sconv_fused_insert_conv": [P, I64, P, I64, I64, P, I64, I32, I32, I32, I64, I64, I64,
@@ -42,6 +51,9 @@ _SIGS = {
     "sconv_fused_insert_conv_qsl": [P, I64, P, I64, I64, P, I64, I32, I32, I32, I64, I64, I64,
                                     P, P, I64, I32, P, I32, P, P, I64, I64, I32, I32, I32,
                                     I32, I32, I32, P],
+    "sconv_fused_insert_conv_streams": [ctypes.POINTER(StreamT), I32, P, I64, I32, I32, I32,
+                                        I64, I64, I64, P, P, I64, I32, P, P, P, I32, P, I64,
+                                        I32, I32, P],
     "causal_conv1d_varlen_fwd": [P, I64, I64, P, I64, I64, P, P, I64, I64, I64, I64, P, I32,
                                  P, P, P, I64, I64, I32, I64, I32, I32, I32, I32, P],
     "causal_conv1d_update": [P, I64, P, I64, I64, I64, I64, P, I64, I64, P, P, P, P, I64,

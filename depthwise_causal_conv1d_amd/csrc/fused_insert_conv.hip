@@ -31,23 +31,34 @@
 
 namespace sconv {
 
+// One conv stream of a layer: its own input, weights and output, and the
+// sub-range [off_s, off_s + ws) of every head's D columns in the shared
+// cache.  Its slabs are global slabs [slab0, slab0 + ceil(C / lane width)).
+constexpr int kMaxStreams = 4;
+struct FusedStream {
+  const void* x;
+  const void* w;
+  void* out;
+  int64_t x_rs, out_rs, w_sc, w_sk;
+  int32_t C, ws, off_s, slab0;
+  int32_t silu, residual;
+};
+
 struct FusedParams {
   // Small fields first: they are needed before anything else and then come
   // in with the first scalar load of the parameters.
   uint32_t num_groups;      // grid size in workgroups
   int32_t waves_per_group;  // workgroup size / 64
-  int32_t num_slabs;
-  int32_t C, ws, off_s, N;
+  int32_t num_slabs;        // over all streams
+  int32_t num_streams;
+  int32_t N;
   // Division by N of non-negative 32-bit positions and slots, branch-free:
   // q = (t + ((v - t) >> n_s1)) >> n_s2 with t = mulhi(v, n_magic)
   // (Granlund & Montgomery, round-up variant; exact for every uint32 v).
   // N = 1: (0, 0, 0); N = 2^k: (1, 1, k-1); otherwise the magic number.
   uint32_t n_magic, n_s1, n_s2;
-  int32_t silu, residual;
   int32_t num_reqs;         // with qsl
   int32_t nt_x;             // host choice: streaming input loads (one wave generation)
-  const void* x;
-  const void* w;
   void* cache;
   const int64_t* positions;
   const int32_t* bt;
@@ -55,9 +66,9 @@ struct FusedParams {
   const int64_t* slot;
   const int32_t* qs;        // per-row request start (NULL: search qsl)
   const int32_t* qsl;       // request row offsets [num_reqs + 1] (or NULL)
-  void* out;
-  int64_t x_rs, w_sc, w_sk, cs0, cs1, cs2, bt_rs, out_rs, T;
+  int64_t cs0, cs1, cs2, bt_rs, T;
   int64_t num_tiles;
+  FusedStream st[kMaxStreams];
 };
 
 // Request of row t: the last r in [0, n) with off[r] <= t (rows past the
@@ -133,21 +144,28 @@ constexpr int kQslSearch = 2;  // the offsets qsl, searched in device memory
 constexpr int kQslRegMax = SCONV_FUSED_QSL_REG_MAX;
 static_assert(kQslRegMax <= 512, "8 offsets per lane");
 
-// NTX: input rows loaded as streaming (non-temporal) reads.
-template <typename D, int VEC, int W, int BT, int QM, bool NTX>
+// NTX: input rows loaded as streaming (non-temporal) reads.  MS: several
+// streams, each wave finding its own (one-stream launches read entry 0).
+template <typename D, int VEC, int W, int BT, int QM, bool NTX, bool MS>
 __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParams p) {
   using S = typename D::storage;
   using P = Pack<D, VEC>;
-  const S* __restrict__ x = static_cast<const S*>(p.x);
-  const S* __restrict__ wt = static_cast<const S*>(p.w);
   S* __restrict__ cache = static_cast<S*>(p.cache);
-  S* __restrict__ out = static_cast<S*>(p.out);
   const int64_t* __restrict__ positions = p.positions;
   const int64_t* __restrict__ slots = p.slot;
   const int32_t* __restrict__ seq_idx = p.seq_idx;
   const int32_t* __restrict__ qstart = p.qs;
   const int32_t* __restrict__ btab = p.bt;
 
+  // Fields needed to place this wave and to issue its metadata loads (the
+  // geometry, the streams' first slabs, the metadata pointers) all come in
+  // the first batch of parameter loads.
+  asm volatile("" ::"s"(p.num_groups), "s"(p.waves_per_group), "s"(p.num_tiles),
+               "s"(p.positions), "s"(p.slot), "s"(p.qsl), "s"(p.seq_idx), "s"(p.qs),
+               "s"(p.num_reqs), "s"(p.T));
+  if constexpr (MS)
+    asm volatile("" ::"s"(p.num_streams), "s"(p.st[1].slab0), "s"(p.st[2].slab0),
+                 "s"(p.st[3].slab0));
   const int lane = threadIdx.x & 63;
   // The launch geometry comes in the parameters (loaded with them in one
   // batch) rather than from the implicit arguments, which would cost a
@@ -173,6 +191,7 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   const int slab = (int)(wave - tile * (uint32_t)p.num_slabs);
 #endif
   const int64_t t0 = (int64_t)tile * BT;
+
 
   // Row metadata of the whole tile in one gather: lane L loads field L % F
   // of row t0 + L / F (position, slot low and high words, and without QSL
@@ -211,20 +230,51 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     }
   }
 
+  // The stream owning this slab (its first slab is the last one <= slab).
+  // With several streams its fields come with one more scalar load from the
+  // parameter segment; the scheduling barrier keeps the metadata loads above
+  // issued ahead of it, since their chain (metadata, block table, history)
+  // bounds small launches while the stream's fields are needed only for the
+  // input rows.  A one-stream launch reads entry 0 at fixed offsets, with
+  // the first parameter loads.
+  int sid = 0;
+  if constexpr (MS) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 1; k < kMaxStreams; ++k)
+      sid = (k < p.num_streams && slab >= p.st[k].slab0) ? k : sid;
+  }
+  const S* x;
+  const S* wt;
+  S* out;
+  int64_t x_rs, out_rs, w_sc, w_sk;
+  int32_t s_C, s_ws, s_off, s_silu, s_res, s_slab0;
+  auto take = [&](const FusedStream& fs) {
+    x = static_cast<const S*>(fs.x);
+    wt = static_cast<const S*>(fs.w);
+    out = static_cast<S*>(fs.out);
+    x_rs = fs.x_rs; out_rs = fs.out_rs; w_sc = fs.w_sc; w_sk = fs.w_sk;
+    s_C = fs.C; s_ws = fs.ws; s_off = fs.off_s; s_silu = fs.silu; s_res = fs.residual;
+    s_slab0 = fs.slab0;
+  };
+  if constexpr (MS) take(p.st[uniform(sid)]);
+  else take(p.st[0]);
+  const int lslab = slab - s_slab0;  // slab within the stream
+
   // The tile's input rows (16 bytes per lane).
-  const int c0 = (slab * 64 + lane) * VEC;  // lane's channels lie in one head
-  const bool on = c0 < p.C;
+  const int c0 = (lslab * 64 + lane) * VEC;  // lane's channels lie in one head
+  const bool on = c0 < s_C;
   const int cl = on ? c0 : 0;               // clamped for the loads
   P xr[BT];
 #pragma unroll
   for (int i = 0; i < BT; ++i) {
     const int64_t t = t0 + i < t_last ? t0 + i : t_last;
-    if constexpr (NTX) xr[i].load_nt(x + t * p.x_rs + cl);
-    else xr[i].load(x + t * p.x_rs + cl);
+    if constexpr (NTX) xr[i].load_nt(x + t * x_rs + cl);
+    else xr[i].load(x + t * x_rs + cl);
   }
-  const int h = on ? c0 / p.ws : 0;
-  const int j = c0 - h * p.ws;
-  const int64_t lane_off = (int64_t)h * p.cs1 + p.off_s + j;
+  const int h = on ? c0 / s_ws : 0;
+  const int j = c0 - h * s_ws;
+  const int64_t lane_off = (int64_t)h * p.cs1 + s_off + j;
 
   // Filter taps of this lane's channels, as raw elements [e][k]; widened to
   // fp32 after the metadata is in.  The 16-byte-lane kernels take packed
@@ -243,7 +293,7 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < W; ++k) wr.e[k] = wt[(int64_t)cl * p.w_sc + (int64_t)k * p.w_sk];
+    for (int k = 0; k < W; ++k) wr.e[k] = wt[(int64_t)cl * w_sc + (int64_t)k * w_sk];
   }
 
   // The parameters needed from here on (addressing, epilogue flags) must
@@ -251,8 +301,8 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   // would add a dependent round trip after the metadata returns.  An empty
   // statement taking them as scalar inputs pins their loads here.
   asm volatile("" ::"s"(p.n_magic), "s"(p.n_s1), "s"(p.n_s2), "s"(p.N),
-               "s"(p.silu), "s"(p.residual), "s"(p.cs0), "s"(p.cs2), "s"(p.bt_rs),
-               "s"(p.out_rs));
+               "s"(s_silu), "s"(s_res), "s"(p.cs0), "s"(p.cs2), "s"(p.bt_rs),
+               "s"(out_rs));
 
   // Broadcast the metadata.  Positions and slots are below max_blocks*N and
   // num_blocks*N, both checked on the host to fit in 31 bits; a negative
@@ -395,7 +445,7 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
       // for the rows counted in `need`), and left unset otherwise: merging
       // with a default value would make the wave wait for the load right
       // here, in front of the history lookups.
-      if (need && on) halo[m - 1].load(x + (t0 - m) * p.x_rs + c0);
+      if (need && on) halo[m - 1].load(x + (t0 - m) * x_rs + c0);
     }
   }
 
@@ -407,9 +457,9 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     if (on) {
       const int64_t t = t0 + i;
 #if SCONV_FUSED_NT_OUT
-      outv[i].store_nt(out + t * p.out_rs + c0);
+      outv[i].store_nt(out + t * out_rs + c0);
 #else
-      outv[i].store(out + t * p.out_rs + c0);
+      outv[i].store(out + t * out_rs + c0);
 #endif
       const uint32_t blk = div_n((uint32_t)slot[i], p);
       const int32_t off = slot[i] - (int32_t)blk * p.N;
@@ -429,8 +479,8 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         float v = acc[e];
-        if (p.silu) v = silu(v);
-        if (p.residual) v += cur[e];
+        if (s_silu) v = silu(v);
+        if (s_res) v += cur[e];
         y[e] = v;
       }
     }
@@ -546,31 +596,37 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 
 // ---------------------------------------------------------------- dispatch
 
-template <typename D, int VEC, int W, int BT, bool NTX>
+template <typename D, int VEC, int W, int BT, bool NTX, bool MS>
 static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
   if (p.qsl && p.num_reqs <= kQslRegMax) {
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs, NTX>), dim3(grid),
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs, NTX, MS>), dim3(grid),
                        dim3(threads), 0, s, p);
   } else if (p.qsl) {
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslSearch, NTX>), dim3(grid),
-                       dim3(threads), 0, s, p);
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslSearch, NTX, MS>),
+                       dim3(grid), dim3(threads), 0, s, p);
   } else {
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslOff, NTX>), dim3(grid),
+    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslOff, NTX, MS>), dim3(grid),
                        dim3(threads), 0, s, p);
   }
 }
 
-// Streaming input loads are built only for the 16-byte-lane 4-row tiles,
-// the shape of launches large enough to fill the chip once.
-template <typename D, int VEC, int W, int BT>
-static void launch(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
+template <typename D, int VEC, int W, int BT, bool MS>
+static void launch_n(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
+  // Streaming input loads are built only for the 16-byte-lane 4-row tiles,
+  // the shape of launches large enough to fill the chip once.
   if constexpr (VEC > 1 && BT == 4) {
     if (p.nt_x) {
-      launch_q<D, VEC, W, BT, true>(p, grid, threads, s);
+      launch_q<D, VEC, W, BT, true, MS>(p, grid, threads, s);
       return;
     }
   }
-  launch_q<D, VEC, W, BT, false>(p, grid, threads, s);
+  launch_q<D, VEC, W, BT, false, MS>(p, grid, threads, s);
+}
+
+template <typename D, int VEC, int W, int BT>
+static void launch(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
+  if (p.num_streams > 1) launch_n<D, VEC, W, BT, true>(p, grid, threads, s);
+  else launch_n<D, VEC, W, BT, false>(p, grid, threads, s);
 }
 
 template <typename D, int VEC, int W>
@@ -615,64 +671,86 @@ namespace sconv {
 // Shared launcher of both entry points: per-row metadata (seq_idx,
 // query_start) or request offsets (qsl, num_reqs) searched in the kernel.
 static int fused_launch(
-    const char* fn, const void* x, int64_t x_row_stride, const void* weight,
-    int64_t w_stride_c, int64_t w_stride_k, void* cache, int64_t num_blocks, int32_t H,
-    int32_t N, int32_t D, int64_t cs0, int64_t cs1, int64_t cs2, const int64_t* positions,
-    const int32_t* block_table, int64_t bt_row_stride, int32_t max_blocks,
-    const int32_t* seq_idx, const int32_t* query_start, const int32_t* qsl, int32_t num_reqs,
-    const int64_t* slot_mapping, void* out, int64_t out_row_stride, int64_t T, int32_t off_s,
-    int32_t ws, int32_t W, int32_t dtype, int32_t activation, int32_t use_residual,
+    const char* fn, const sconv_stream_t* streams, int32_t num_streams, void* cache,
+    int64_t num_blocks, int32_t H, int32_t N, int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
+    const int64_t* positions, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t max_blocks, const int32_t* seq_idx, const int32_t* query_start, const int32_t* qsl,
+    int32_t num_reqs, const int64_t* slot_mapping, int64_t T, int32_t W, int32_t dtype,
     hipStream_t stream) {
   if (T < 0) return fail(SCONV_ERR_INVALID, "%s: T < 0", fn);
   if (!valid_dtype(dtype)) return fail(SCONV_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
-  if (!valid_act(activation))
-    return fail(SCONV_ERR_INVALID, "%s: unknown activation %d", fn, activation);
   if (W < 1 || W > 4) return fail(SCONV_ERR_INVALID, "%s: W=%d outside [1, 4]", fn, W);
-  if (H < 1 || N < 1 || ws < 1 || D < 1 || num_blocks < 1 || max_blocks < 1)
-    return fail(SCONV_ERR_INVALID, "%s: H, N, ws, D, num_blocks and max_blocks must be >= 1", fn);
-  if (off_s < 0 || (int64_t)off_s + ws > D)
-    return fail(SCONV_ERR_INVALID, "%s: stream range [%d, %d) outside D=%d", fn, off_s,
-                off_s + ws, D);
-  const int64_t C = (int64_t)H * ws;
-  if (C > INT32_MAX / 2) return fail(SCONV_ERR_UNSUPPORTED, "%s: C too large", fn);
-  if (x_row_stride < C || out_row_stride < C)
-    return fail(SCONV_ERR_INVALID, "%s: row strides must be >= C=%lld", fn, (long long)C);
+  if (num_streams < 1 || num_streams > kMaxStreams || !streams)
+    return fail(SCONV_ERR_INVALID, "%s: num_streams=%d outside [1, %d]", fn, num_streams,
+                kMaxStreams);
+  if (H < 1 || N < 1 || D < 1 || num_blocks < 1 || max_blocks < 1)
+    return fail(SCONV_ERR_INVALID, "%s: H, N, D, num_blocks and max_blocks must be >= 1", fn);
   if ((int64_t)num_blocks * N > INT32_MAX || (int64_t)max_blocks * N > INT32_MAX)
     return fail(SCONV_ERR_UNSUPPORTED, "%s: more than 2^31 cache slots or positions", fn);
   if (T > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: T above 2^31", fn);
-  if (cs2 < D || cs1 < 1 || cs0 < 1 || bt_row_stride < max_blocks || w_stride_c < 1 ||
-      w_stride_k < 1)
-    return fail(SCONV_ERR_INVALID, "%s: cache / block-table / weight strides too small", fn);
+  if (cs2 < D || cs1 < 1 || cs0 < 1 || bt_row_stride < max_blocks)
+    return fail(SCONV_ERR_INVALID, "%s: cache / block-table strides too small", fn);
+  const int64_t es = elem_size(dtype);
+  const int vec16 = (int)(16 / es);
+  bool vec = cs0 % vec16 == 0 && cs1 % vec16 == 0 && cs2 % vec16 == 0 && aligned16(cache);
+  int64_t C[kMaxStreams];
+  for (int s = 0; s < num_streams; ++s) {
+    const sconv_stream_t& q = streams[s];
+    if (!valid_act(q.activation))
+      return fail(SCONV_ERR_INVALID, "%s: stream %d: unknown activation %d", fn, s, q.activation);
+    if (q.ws < 1) return fail(SCONV_ERR_INVALID, "%s: stream %d: ws must be >= 1", fn, s);
+    if (q.off_s < 0 || (int64_t)q.off_s + q.ws > D)
+      return fail(SCONV_ERR_INVALID, "%s: stream %d: range [%d, %d) outside D=%d", fn, s,
+                  q.off_s, q.off_s + q.ws, D);
+    for (int r = 0; r < s; ++r)
+      if (q.off_s < streams[r].off_s + streams[r].ws && streams[r].off_s < q.off_s + q.ws)
+        return fail(SCONV_ERR_INVALID, "%s: streams %d and %d share cache columns", fn, r, s);
+    C[s] = (int64_t)H * q.ws;
+    if (C[s] > INT32_MAX / 2) return fail(SCONV_ERR_UNSUPPORTED, "%s: C too large", fn);
+    if (q.x_row_stride < C[s] || q.out_row_stride < C[s])
+      return fail(SCONV_ERR_INVALID, "%s: stream %d: row strides must be >= C=%lld", fn, s,
+                  (long long)C[s]);
+    if (q.w_stride_c < 1 || q.w_stride_k < 1)
+      return fail(SCONV_ERR_INVALID, "%s: stream %d: weight strides too small", fn, s);
+    const bool w_packed = q.w_stride_c == W && q.w_stride_k == 1 && aligned16(q.weight);
+    vec = vec && w_packed && C[s] % vec16 == 0 && q.ws % vec16 == 0 && q.off_s % vec16 == 0 &&
+          q.x_row_stride % vec16 == 0 && q.out_row_stride % vec16 == 0 && aligned16(q.x) &&
+          aligned16(q.out);
+  }
   if (T == 0) return SCONV_OK;
-  if (!x || !weight || !cache || !positions || !block_table || !slot_mapping || !out ||
+  if (!cache || !positions || !block_table || !slot_mapping ||
       (qsl ? false : (!seq_idx || !query_start)))
     return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
   if (qsl && num_reqs < 1)
     return fail(SCONV_ERR_INVALID, "%s: num_reqs < 1 with %lld rows", fn, (long long)T);
-  const int64_t es = elem_size(dtype);
-  const int64_t x_bytes = ((T - 1) * x_row_stride + C) * es;
-  const int64_t o_bytes = ((T - 1) * out_row_stride + C) * es;
   const int64_t c_bytes = ((num_blocks - 1) * cs0 + (H - 1) * cs1 + (N - 1) * cs2 + D) * es;
-  if (overlap(out, o_bytes, x, x_bytes) || overlap(out, o_bytes, cache, c_bytes))
-    return fail(SCONV_ERR_INVALID, "%s: out overlaps x or the cache", fn);
-
-  const int vec16 = (int)(16 / es);
-  const bool w_packed = w_stride_c == W && w_stride_k == 1 && aligned16(weight);
-  const bool vec = w_packed && C % vec16 == 0 && ws % vec16 == 0 && off_s % vec16 == 0 &&
-                   x_row_stride % vec16 == 0 && out_row_stride % vec16 == 0 &&
-                   cs0 % vec16 == 0 && cs1 % vec16 == 0 && cs2 % vec16 == 0 && aligned16(x) &&
-                   aligned16(out) && aligned16(cache);
+  for (int s = 0; s < num_streams; ++s) {
+    const sconv_stream_t& q = streams[s];
+    if (!q.x || !q.weight || !q.out) return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
+    const int64_t o_bytes = ((T - 1) * q.out_row_stride + C[s]) * es;
+    if (overlap(q.out, o_bytes, cache, c_bytes))
+      return fail(SCONV_ERR_INVALID, "%s: out overlaps x or the cache", fn);
+    for (int r = 0; r < num_streams; ++r) {
+      const int64_t x_bytes = ((T - 1) * streams[r].x_row_stride + C[r]) * es;
+      if (overlap(q.out, o_bytes, streams[r].x, x_bytes))
+        return fail(SCONV_ERR_INVALID, "%s: out overlaps x or the cache", fn);
+      if (r != s) {
+        const int64_t o2 = ((T - 1) * streams[r].out_row_stride + C[r]) * es;
+        if (overlap(q.out, o_bytes, streams[r].out, o2))
+          return fail(SCONV_ERR_INVALID, "%s: outputs of streams %d and %d overlap", fn, r, s);
+      }
+    }
+  }
   const int VEC = vec ? vec16 : 1;
 
   FusedParams p = {};
-  p.x = x; p.w = weight; p.cache = cache; p.positions = positions; p.bt = block_table;
-  p.seq_idx = seq_idx; p.slot = slot_mapping; p.qs = query_start; p.out = out;
+  p.cache = cache; p.positions = positions; p.bt = block_table;
+  p.seq_idx = seq_idx; p.slot = slot_mapping; p.qs = query_start;
   p.qsl = qsl;
   p.num_reqs = qsl ? num_reqs : 0;
-  p.x_rs = x_row_stride; p.w_sc = w_stride_c; p.w_sk = w_stride_k;
-  p.cs0 = cs0; p.cs1 = cs1; p.cs2 = cs2; p.bt_rs = bt_row_stride; p.out_rs = out_row_stride;
+  p.cs0 = cs0; p.cs1 = cs1; p.cs2 = cs2; p.bt_rs = bt_row_stride;
   p.T = T;
-  p.C = (int32_t)C; p.ws = ws; p.off_s = off_s; p.N = N;
+  p.N = N;
   if (N == 1) {
     p.n_magic = 0; p.n_s1 = 0; p.n_s2 = 0;
   } else if ((N & (N - 1)) == 0) {
@@ -683,11 +761,23 @@ static int fused_launch(
     p.n_s1 = 1;
     p.n_s2 = l - 1;
   }
-  p.num_slabs = (int32_t)cdiv(C, 64 * VEC);
+  p.num_streams = num_streams;
+  int64_t slabs = 0;
+  for (int s = 0; s < num_streams; ++s) {
+    const sconv_stream_t& q = streams[s];
+    FusedStream& f = p.st[s];
+    f.x = q.x; f.w = q.weight; f.out = q.out;
+    f.x_rs = q.x_row_stride; f.out_rs = q.out_row_stride;
+    f.w_sc = q.w_stride_c; f.w_sk = q.w_stride_k;
+    f.C = (int32_t)C[s]; f.ws = q.ws; f.off_s = q.off_s;
+    f.silu = q.activation == SCONV_ACT_SILU;
+    f.residual = q.use_residual != 0;
+    f.slab0 = (int32_t)slabs;
+    slabs += cdiv(C[s], 64 * VEC);
+  }
+  p.num_slabs = (int32_t)slabs;
   const int bt = pick_bt(T, p.num_slabs);
   p.num_tiles = cdiv(T, bt);
-  p.silu = activation == SCONV_ACT_SILU;
-  p.residual = use_residual != 0;
 
   const int64_t waves = p.num_tiles * p.num_slabs;
   if (waves > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
@@ -714,6 +804,18 @@ static int fused_launch(
 
 }  // namespace sconv
 
+static sconv_stream_t one_stream(const void* x, int64_t x_row_stride, const void* weight,
+                                 int64_t w_stride_c, int64_t w_stride_k, void* out,
+                                 int64_t out_row_stride, int32_t off_s, int32_t ws,
+                                 int32_t activation, int32_t use_residual) {
+  sconv_stream_t q;
+  q.x = x; q.x_row_stride = x_row_stride; q.weight = weight;
+  q.w_stride_c = w_stride_c; q.w_stride_k = w_stride_k;
+  q.out = out; q.out_row_stride = out_row_stride;
+  q.off_s = off_s; q.ws = ws; q.activation = activation; q.use_residual = use_residual;
+  return q;
+}
+
 extern "C" int sconv_fused_insert_conv(
     const void* x, int64_t x_row_stride, const void* weight, int64_t w_stride_c,
     int64_t w_stride_k, void* cache, int64_t num_blocks, int32_t H, int32_t N, int32_t D,
@@ -723,11 +825,12 @@ extern "C" int sconv_fused_insert_conv(
     int64_t out_row_stride, int64_t T, int32_t off_s, int32_t ws, int32_t W, int32_t dtype,
     int32_t activation, int32_t use_residual, hipStream_t stream) {
   sconv::clear_error();
-  return sconv::fused_launch("sconv_fused_insert_conv", x, x_row_stride, weight, w_stride_c,
-                             w_stride_k, cache, num_blocks, H, N, D, cs0, cs1, cs2, positions,
-                             block_table, bt_row_stride, max_blocks, seq_idx, query_start,
-                             nullptr, 0, slot_mapping, out, out_row_stride, T, off_s, ws, W,
-                             dtype, activation, use_residual, stream);
+  const sconv_stream_t q = one_stream(x, x_row_stride, weight, w_stride_c, w_stride_k, out,
+                                      out_row_stride, off_s, ws, activation, use_residual);
+  return sconv::fused_launch("sconv_fused_insert_conv", &q, 1, cache, num_blocks, H, N, D, cs0,
+                             cs1, cs2, positions, block_table, bt_row_stride, max_blocks,
+                             seq_idx, query_start, nullptr, 0, slot_mapping, T, W, dtype,
+                             stream);
 }
 
 extern "C" int sconv_fused_insert_conv_qsl(
@@ -741,9 +844,29 @@ extern "C" int sconv_fused_insert_conv_qsl(
   sconv::clear_error();
   if (T > 0 && !query_start_loc)
     return sconv::fail(SCONV_ERR_INVALID, "sconv_fused_insert_conv_qsl: NULL query_start_loc");
-  return sconv::fused_launch("sconv_fused_insert_conv_qsl", x, x_row_stride, weight, w_stride_c,
-                             w_stride_k, cache, num_blocks, H, N, D, cs0, cs1, cs2, positions,
-                             block_table, bt_row_stride, max_blocks, nullptr, nullptr,
-                             query_start_loc, num_reqs, slot_mapping, out, out_row_stride, T,
-                             off_s, ws, W, dtype, activation, use_residual, stream);
+  const sconv_stream_t q = one_stream(x, x_row_stride, weight, w_stride_c, w_stride_k, out,
+                                      out_row_stride, off_s, ws, activation, use_residual);
+  return sconv::fused_launch("sconv_fused_insert_conv_qsl", &q, 1, cache, num_blocks, H, N, D,
+                             cs0, cs1, cs2, positions, block_table, bt_row_stride, max_blocks,
+                             nullptr, nullptr, query_start_loc, num_reqs, slot_mapping, T, W,
+                             dtype, stream);
+}
+
+extern "C" int sconv_fused_insert_conv_streams(
+    const sconv_stream_t* streams, int32_t num_streams, void* cache, int64_t num_blocks,
+    int32_t H, int32_t N, int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
+    const int64_t* positions, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t max_blocks, const int32_t* seq_idx, const int32_t* query_start,
+    const int32_t* query_start_loc, int32_t num_reqs, const int64_t* slot_mapping, int64_t T,
+    int32_t W, int32_t dtype, hipStream_t stream) {
+  const char* fn = "sconv_fused_insert_conv_streams";
+  sconv::clear_error();
+  const bool per_row = seq_idx || query_start;
+  if (per_row == (query_start_loc != nullptr))
+    return sconv::fail(SCONV_ERR_INVALID,
+                       "%s: give either seq_idx and query_start, or query_start_loc", fn);
+  return sconv::fused_launch(fn, streams, num_streams, cache, num_blocks, H, N, D, cs0, cs1,
+                             cs2, positions, block_table, bt_row_stride, max_blocks, seq_idx,
+                             query_start, query_start_loc, num_reqs, slot_mapping, T, W, dtype,
+                             stream);
 }

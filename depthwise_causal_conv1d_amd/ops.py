@@ -7,7 +7,7 @@ HIP kernels; there is no CPU path.  Argument names follow the source pages.
 """
 from __future__ import annotations
 
-from typing import Optional
+from typing import List, Optional, Sequence
 
 import torch
 
@@ -158,6 +158,74 @@ def sconv_fused_insert_conv_qsl(x: torch.Tensor, weight: torch.Tensor, cache: to
         _stream(x))
     _lib.check(rc, "sconv_fused_insert_conv_qsl")
     return out
+
+
+def sconv_fused_insert_conv_streams(xs: Sequence[torch.Tensor], weights: Sequence[torch.Tensor],
+                                    cache: torch.Tensor, positions: torch.Tensor,
+                                    block_table: torch.Tensor, slot_mapping: torch.Tensor,
+                                    off_s: Sequence[int], ws: Sequence[int], block_size: int,
+                                    activation=None, use_residual=True,
+                                    seq_idx: Optional[torch.Tensor] = None,
+                                    query_start: Optional[torch.Tensor] = None,
+                                    query_start_loc: Optional[torch.Tensor] = None,
+                                    num_reqs: Optional[int] = None,
+                                    outs: Optional[Sequence[torch.Tensor]] = None
+                                    ) -> List[torch.Tensor]:
+    """The insert + conv of up to four streams of one layer in one launch.
+
+    Stream s has x ``xs[s]`` [T, H*ws[s]], weight ``weights[s]`` [H*ws[s], W]
+    and cache columns [off_s[s], off_s[s] + ws[s]) of every head.
+    ``activation`` and ``use_residual`` are one value for all streams or a
+    sequence with one per stream.  Rows find their request either from
+    ``seq_idx`` / ``query_start`` or, inside the launch, from
+    ``query_start_loc`` with ``num_reqs``.  Returns the outputs.
+    """
+    n = len(xs)
+    if not (len(weights) == len(off_s) == len(ws) == n):
+        raise ValueError("xs, weights, off_s and ws need one entry per stream")
+    acts = list(activation) if isinstance(activation, (list, tuple)) else [activation] * n
+    ress = list(use_residual) if isinstance(use_residual, (list, tuple)) else [use_residual] * n
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    if len(acts) != n or len(ress) != n or len(outs) != n:
+        raise ValueError("activation, use_residual and outs need one entry per stream")
+    T = xs[0].shape[0] if n else 0
+    if n == 0 or T == 0:
+        return list(outs)
+    if any(x.shape[0] != T for x in xs):
+        raise ValueError("every stream needs the same rows T")
+    dt = None
+    for x, w, o, a, b in zip(xs, weights, outs, off_s, ws):
+        dt = _fused_checks(x, w, cache, positions, block_table, slot_mapping, a, b, block_size, o)
+    if any(w.shape[1] != weights[0].shape[1] for w in weights):
+        raise ValueError("every stream needs the same filter width W")
+    if any(x.dtype != xs[0].dtype for x in xs):
+        raise TypeError("every stream needs the same element type")
+    if query_start_loc is not None:
+        if seq_idx is not None or query_start is not None or num_reqs is None:
+            raise ValueError("give query_start_loc with num_reqs, or seq_idx and query_start")
+        _dev(query_start_loc)
+        _vec(query_start_loc, torch.int32, "query_start_loc", num_reqs + 1)
+    else:
+        if seq_idx is None or query_start is None:
+            raise ValueError("give query_start_loc with num_reqs, or seq_idx and query_start")
+        _dev(seq_idx, query_start)
+        _vec(seq_idx, torch.int32, "seq_idx", T)
+        _vec(query_start, torch.int32, "query_start", T)
+    arr = (_lib.StreamT * n)()
+    for i, (x, w, o) in enumerate(zip(xs, weights, outs)):
+        arr[i] = _lib.StreamT(_ptr(x), x.stride(0), _ptr(w), w.stride(0), w.stride(1), _ptr(o),
+                              o.stride(0), int(off_s[i]), int(ws[i]), _act(acts[i]),
+                              int(bool(ress[i])))
+    nb, H, N, D = cache.shape
+    rc = _lib.load().sconv_fused_insert_conv_streams(
+        arr, n, _ptr(cache), nb, H, N, D, cache.stride(0), cache.stride(1), cache.stride(2),
+        _ptr(positions), _ptr(block_table), block_table.stride(0), block_table.shape[1],
+        _ptr(seq_idx), _ptr(query_start), _ptr(query_start_loc),
+        int(num_reqs) if num_reqs is not None else 0, _ptr(slot_mapping), T,
+        weights[0].shape[1], dt, _stream(xs[0]))
+    _lib.check(rc, "sconv_fused_insert_conv_streams")
+    return list(outs)
 
 
 def causal_conv1d_varlen_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],

@@ -166,6 +166,66 @@ int sconv_fused_insert_conv_qsl(const void* x, int64_t x_row_stride,
                                 int32_t use_residual, hipStream_t stream);
 
 /*
+ * sconv_stream_t -- one conv stream of a layer, for
+ * sconv_fused_insert_conv_streams.  Fields as the same-named arguments of
+ * sconv_fused_insert_conv: x and out [T, H*ws] rows of their row strides,
+ * weight [H*ws, W], and the stream's columns [off_s, off_s + ws) of every
+ * head of the shared cache.  activation and use_residual are per stream.
+ * All pointers are device pointers owned by the caller; the array itself is
+ * host memory, read during the call only.
+ */
+typedef struct sconv_stream {
+  const void* x;
+  int64_t x_row_stride;
+  const void* weight;
+  int64_t w_stride_c, w_stride_k;
+  void* out;
+  int64_t out_row_stride;
+  int32_t off_s, ws;
+  int32_t activation, use_residual;
+} sconv_stream_t;
+
+/*
+ * sconv_fused_insert_conv_streams -- the insert + conv of up to four conv
+ * streams of one layer in a single launch.
+ *
+ * Source: vLLM page "vllm.models.inkling.nvidia.ops.sconv", module
+ * description (a layer's four conv streams -- K, V, attention output, MLP
+ * output -- share one paged cache, each in its own column sub-range of
+ * every head) and fused_sconv.  The result is exactly that of calling
+ * sconv_fused_insert_conv once per stream, in any order: streams touch
+ * disjoint cache columns, and each reads only its own pre-forward taps.
+ *
+ *   streams      host array [num_streams], 1 <= num_streams <= 4; their
+ *                column ranges must be pairwise disjoint
+ *   per-row request: either seq_idx and query_start (as filled by
+ *                sconv_seq_metadata; query_start_loc NULL), or
+ *                query_start_loc [num_reqs + 1] searched inside the launch
+ *                (seq_idx and query_start NULL), as in
+ *                sconv_fused_insert_conv_qsl
+ *   all other arguments as in sconv_fused_insert_conv, shared by the streams
+ *
+ * The 16-byte-lane kernels run when every stream meets their alignment
+ * (else all streams take the one-channel kernels).
+ *
+ * Device-data contract: as sconv_fused_insert_conv, for every stream.
+ *
+ * Host errors (SCONV_ERR_INVALID): num_streams outside [1, 4], overlapping
+ * column ranges, both or neither per-row request forms, any stream failing
+ * the checks of sconv_fused_insert_conv, any stream's out overlapping the
+ * cache or another stream's x or out.  T == 0 is a successful no-op.
+ */
+int sconv_fused_insert_conv_streams(const sconv_stream_t* streams, int32_t num_streams,
+                                    void* cache, int64_t num_blocks, int32_t H, int32_t N,
+                                    int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
+                                    const int64_t* positions, const int32_t* block_table,
+                                    int64_t bt_row_stride, int32_t max_blocks,
+                                    const int32_t* seq_idx, const int32_t* query_start,
+                                    const int32_t* query_start_loc, int32_t num_reqs,
+                                    const int64_t* slot_mapping, int64_t T, int32_t W,
+                                    int32_t dtype, hipStream_t stream);
+
+/*
  * causal_conv1d_varlen_fwd -- causal depthwise conv over packed
  * variable-length sequences, with a slot-indexed state pool.
  *

@@ -9,7 +9,8 @@ rounding to the output type).  This file only marshals numpy arrays into it.
 Arrays hold float32, float64 or bfloat16 *bit patterns* (numpy ``uint16``);
 the element type of a call is taken from ``x``.
 
-Every function cites the page passage it follows in ``sconv_oracle.c``.
+Every function cites the page passage it follows in ``sconv_oracle.c``;
+``fused_insert_conv_streams`` is the single-stream op applied per stream.
 """
 from __future__ import annotations
 
@@ -183,6 +184,29 @@ def fused_insert_conv(x, weight, cache, positions, block_table, seq_idx, slot_ma
         dt, _act(activation), int(bool(use_residual)))
     _check(rc, "fused_insert_conv")
     return out, cache_out
+
+
+def fused_insert_conv_streams(streams, cache, positions, block_table, seq_idx, slot_mapping,
+                              query_start, block_size: int):
+    """Insert + conv of several conv streams of one layer (vLLM sconv page,
+    module description: a layer's streams share one paged cache, each in its
+    own column sub-range of every head).  By definition this is the
+    single-stream op applied to each stream in turn, the cache carried from
+    one to the next.
+
+    ``streams``: one dict per stream with x, weight, off_s, ws, activation,
+    use_residual and optionally out_init.  Returns ([out per stream],
+    cache_after); ``cache`` itself is not modified.
+    """
+    outs = []
+    c = cache
+    for st in streams:
+        o, c = fused_insert_conv(st["x"], st["weight"], c, positions, block_table, seq_idx,
+                                 slot_mapping, query_start, st["off_s"], st["ws"], block_size,
+                                 st.get("activation"), st.get("use_residual", True),
+                                 out_init=st.get("out_init"))
+        outs.append(o)
+    return outs, c
 
 
 def causal_conv1d_varlen_fwd(x, weight, bias, conv_states, query_start_loc, cache_indices,

@@ -55,6 +55,50 @@ def oracle_fused(case, cache=None, block_table=None, slot_mapping=None, out_init
     return out, cache_after, si, qs
 
 
+def gpu_fused_streams(cases, dev="cuda", fold=True):
+    """All streams of ``cases`` (one layer, shared cache) in one
+    sconv_fused_insert_conv_streams launch; rows find their request inside
+    the launch (fold) or from sconv_seq_metadata buffers.  Returns (outs,
+    cache) as device tensors; the cases are not modified."""
+    import depthwise_causal_conv1d_amd as lib
+    c0 = cases[0]
+    xs = [c.x.to(dev) for c in cases]
+    ws_ = [c.weight.to(dev) for c in cases]
+    cache = c0.cache.to(dev).clone()
+    pos = c0.positions.to(dev)
+    bt = c0.block_table.to(dev)
+    sm = c0.slot_mapping.to(dev)
+    qsl = c0.query_start_loc.to(dev)
+    outs = [torch.full_like(x, SENTINEL) for x in xs]
+    kw = dict(activation=[c.activation for c in cases],
+              use_residual=[c.use_residual for c in cases], outs=outs)
+    if fold:
+        kw.update(query_start_loc=qsl, num_reqs=c0.num_reqs)
+    else:
+        si = torch.full((c0.T,), -5, dtype=torch.int32, device=dev)
+        qs = torch.full((c0.T,), -5, dtype=torch.int32, device=dev)
+        lib.sconv_seq_metadata(qsl, c0.num_reqs, c0.num_actual, si, qs, c0.T)
+        kw.update(seq_idx=si, query_start=qs)
+    lib.sconv_fused_insert_conv_streams(xs, ws_, cache, pos, bt, sm, [c.off_s for c in cases],
+                                        [c.ws for c in cases], c0.block_size, **kw)
+    return outs, cache
+
+
+def oracle_fused_streams(cases, cache=None, block_table=None, slot_mapping=None):
+    """The oracle's multi-stream op on the same inputs (optionally a
+    compacted cache).  Returns (outs, cache_after)."""
+    import oracle
+    c0 = cases[0]
+    si, qs = oracle.seq_metadata(to_np(c0.query_start_loc), c0.num_reqs, c0.num_actual, c0.T)
+    specs = [{"x": to_np(c.x), "weight": to_np(c.weight), "off_s": c.off_s, "ws": c.ws,
+              "activation": c.activation, "use_residual": c.use_residual,
+              "out_init": to_np(torch.full_like(c.x, SENTINEL))} for c in cases]
+    return oracle.fused_insert_conv_streams(
+        specs, to_np(c0.cache if cache is None else cache), to_np(c0.positions),
+        to_np(c0.block_table if block_table is None else block_table), si,
+        to_np(c0.slot_mapping if slot_mapping is None else slot_mapping), qs, c0.block_size)
+
+
 def dtype_name(t: torch.dtype) -> str:
     return {torch.float32: "f32", torch.bfloat16: "bf16"}[t]
 

@@ -110,6 +110,41 @@ def test_ssm_ops_reject_bad_scalars(lib):
     assert b"65535" in lib.sconv_last_error()
 
 
+def test_streams_entry_rejects_bad_host_arguments(lib):
+    """sconv_fused_insert_conv_streams: stream count, overlapping column
+    ranges and the two per-row request forms are checked on the host.  Every
+    call has T = 0 or fails validation, so none launches a kernel."""
+    from depthwise_causal_conv1d_amd._lib import StreamT
+    f = lib.sconv_fused_insert_conv_streams
+    one = ctypes.c_int32(0)
+
+    def streams(*ranges):
+        arr = (StreamT * max(1, len(ranges)))()
+        for i, (off, ws) in enumerate(ranges):
+            arr[i] = StreamT(None, 4 * ws, None, 4, 1, None, 4 * ws, off, ws, 1, 1)
+        return arr
+
+    # H=4, N=16, D=16, cs=(1024, 256, 16); T = 0 unless noted.
+    def call(arr, n, seq=NULL, qs=NULL, qsl=NULL, T=0):
+        return f(arr, n, NULL, 8, 4, 16, 16, 1024, 256, 16, NULL, NULL, 4, 4, seq, qs, qsl, 1,
+                 NULL, T, 4, 1, NULL)
+
+    ok = streams((0, 4), (4, 4), (8, 8))
+    assert call(ok, 3, qsl=ctypes.addressof(one)) == 0                  # valid, T = 0: no-op
+    assert call(ok, 0, qsl=ctypes.addressof(one)) == 1                  # no stream
+    assert call(streams((0, 4), (4, 4), (8, 4), (12, 2), (14, 2)), 5,
+                qsl=ctypes.addressof(one)) == 1                          # five streams
+    assert b"num_streams" in lib.sconv_last_error()
+    assert call(streams((0, 8), (4, 8)), 2, qsl=ctypes.addressof(one)) == 1   # overlap
+    assert b"share cache columns" in lib.sconv_last_error()
+    assert call(streams((12, 8)), 1, qsl=ctypes.addressof(one)) == 1     # past D
+    assert call(ok, 3) == 1                                              # no request form
+    assert b"either" in lib.sconv_last_error()
+    assert call(ok, 3, seq=ctypes.addressof(one), qs=ctypes.addressof(one),
+                qsl=ctypes.addressof(one)) == 1                          # both forms
+    assert call(ok, 3, seq=ctypes.addressof(one), qs=ctypes.addressof(one)) == 0
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     """The binding has no CPU fallback: a missing library is an import error."""
     from depthwise_causal_conv1d_amd import _lib

@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import workloads
-from tests.gpu_util import SENTINEL, dtype_name, gpu_fused, live_rows, oracle_fused
+from tests.gpu_util import (SENTINEL, dtype_name, gpu_fused, gpu_fused_streams, live_rows,
+                            oracle_fused, oracle_fused_streams)
 from tests.helpers import assert_bits_equal, assert_close, to_np
 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("oracle_lib")]
@@ -189,6 +190,84 @@ def test_folded_empty_request_runs(run_len, runs, live, lens):
     case = workloads.fused_case(31 + run_len, new, ctx, H=32, D=128, ws=128, off_s=0,
                                 block_size=16, W=4, dtype=torch.bfloat16)
     check_fused(case, f"{len(new)} requests, runs of {run_len} empty", fold=True)
+
+
+_STREAMS_ORACLE = {}
+
+
+def check_streams(cases, what, fold, cache_compare="full"):
+    """One multi-stream launch against the oracle's multi-stream op: every
+    stream's output (PAD rows untouched) and the shared cache, bit for bit."""
+    c0 = cases[0]
+    say(f"streams {what}: {len(cases)} streams T={c0.T} ws={[c.ws for c in cases]} "
+        f"off_s={[c.off_s for c in cases]} dtype={c0.x.dtype} folded={fold}")
+    outs_g, cache_g = gpu_fused_streams(cases, fold=fold)
+    if cache_compare == "full":
+        if what not in _STREAMS_ORACLE:  # the same inputs serve both metadata forms
+            _STREAMS_ORACLE[what] = oracle_fused_streams(cases)
+        outs_r, cache_r = _STREAMS_ORACLE[what]
+        cache_gh = to_np(cache_g)
+    else:
+        cc, bt, sm = c0.compact()
+        outs_r, cache_r = oracle_fused_streams(cases, cache=cc, block_table=bt, slot_mapping=sm)
+        cache_gh = to_np(cache_g[c0.used_blocks.to(cache_g.device)])
+    live = live_rows(c0)
+    for i, (og, orf) in enumerate(zip(outs_g, outs_r)):
+        ogh = to_np(og)
+        assert_close(ogh, orf, dtype_name(c0.x.dtype), f"{what} stream {i} out", mask=live)
+        assert_bits_equal(ogh[~live], orf[~live], f"{what} stream {i} PAD rows untouched")
+    assert_bits_equal(cache_gh, cache_r, f"{what} cache")
+
+
+STREAM_SPECS = [
+    # name, dtype, W, H, D, N, streams (off_s, ws), acts, residuals, new, ctx, pad, tail
+    ("bf16-vec", torch.bfloat16, 4, 4, 64, 16, [(0, 16), (16, 16), (32, 32)],
+     ["silu", None, "silu"], [True, False, True], [9, 1, 30, 4], [20, 3, 0, 50], 4, 2),
+    ("bf16-scalar", torch.bfloat16, 4, 3, 32, 8, [(0, 8), (8, 6), (20, 10)],
+     ["silu", "silu", None], [True, True, False], [12, 2, 7], [0, 9, 30], 3, 1),
+    ("f32-vec", torch.float32, 4, 2, 16, 16, [(0, 4), (4, 8), (12, 4)],
+     [None, "silu", "silu"], [True, True, True], [5, 17], [2, 40], 2, 0),
+    ("bf16-w3-two", torch.bfloat16, 3, 8, 64, 32, [(32, 32), (0, 16)],
+     ["silu", "silu"], [False, True], [3, 60, 1], [100, 7, 0], 5, 3),
+]
+
+
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
+@pytest.mark.parametrize("spec", STREAM_SPECS, ids=[s[0] for s in STREAM_SPECS])
+def test_streams_sweep(spec, fold):
+    name, dt, W, H, D, N, streams, acts, ress, new, ctx, pad, tail = spec
+    cases = workloads.fused_streams_case(zlib.crc32(name.encode()) % 1000, new, ctx, H=H, D=D,
+                                         streams=streams, block_size=N, W=W, dtype=dt,
+                                         pad_count=pad, tail_pad=tail, activations=acts,
+                                         residuals=ress)
+    check_streams(cases, name, fold)
+
+
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
+def test_streams_mixed_prefill_one_launch(fold):
+    """The four streams of the mixed prefill (ws 128 at off_s 0/128/256/384 of
+    D=512, 20 450 rows, 10% PAD) in one launch."""
+    check_streams(workloads.mixed_prefill_streams(), "mixed prefill", fold)
+
+
+def test_streams_decode_layer():
+    """A decode batch of 256 requests with all four streams of the layer
+    (ws=32 each, D=128) in one folded launch."""
+    g = torch.Generator().manual_seed(5)
+    ctx = [int(v) for v in torch.randint(1, 4097, (256,), generator=g)]
+    cases = workloads.fused_streams_case(5, [1] * 256, ctx, H=32, D=128,
+                                         streams=[(0, 32), (32, 32), (64, 32), (96, 32)],
+                                         block_size=16, W=4, dtype=torch.bfloat16)
+    check_streams(cases, "decode layer", True, cache_compare="compact")
+
+
+def test_streams_one_stream_equals_single_entry():
+    """A one-stream call gives the same bits as sconv_fused_insert_conv."""
+    case = workloads.batched_decode(seed=9)
+    a_out, a_cache, _, _ = gpu_fused(case, fold=True)
+    b_outs, b_cache = gpu_fused_streams([case], fold=True)
+    assert_bits_equal(to_np(b_outs[0]), to_np(a_out), "out")
+    assert torch.equal(b_cache.view(torch.int16), a_cache.view(torch.int16))
 
 
 def test_config_batched_decode_large_pool():

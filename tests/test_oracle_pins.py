@@ -306,6 +306,39 @@ def test_fused_streams_touch_only_their_subrange():
     assert_bits_equal(k[..., untouched], cache[..., untouched], "other sub-ranges")
 
 
+def test_fused_streams_order_free_and_each_stream_alone():
+    """Four streams of one layer (different widths, activations and residual
+    flags, PAD rows): any order of application gives the same bits, every
+    stream's output equals that stream run alone on the original cache, and
+    columns outside every stream's range keep their bits."""
+    cases = workloads.fused_streams_case(
+        43, [6, 1, 9], [5, 0, 12], H=3, D=24, streams=[(0, 4), (4, 8), (16, 2), (20, 4)],
+        block_size=4, W=4, dtype=torch.float64, pad_count=2,
+        activations=["silu", None, "silu", None], residuals=[True, True, False, False])
+    o = orc()
+    c0 = cases[0]
+    si, qs = o.seq_metadata(to_np(c0.query_start_loc), c0.num_reqs, c0.num_actual, c0.T)
+    common = (to_np(c0.positions), to_np(c0.block_table), si, to_np(c0.slot_mapping), qs,
+              c0.block_size)
+    spec = lambda c: {"x": to_np(c.x), "weight": to_np(c.weight), "off_s": c.off_s,
+                      "ws": c.ws, "activation": c.activation, "use_residual": c.use_residual}
+    cache = to_np(c0.cache)
+    outs, k = o.fused_insert_conv_streams([spec(c) for c in cases], cache, *common)
+    routs, rk = o.fused_insert_conv_streams([spec(c) for c in cases[::-1]], cache, *common)
+    assert_bits_equal(k, rk, "cache, reversed order")
+    for i, c in enumerate(cases):
+        assert_bits_equal(outs[i], routs[len(cases) - 1 - i], f"stream {i}, reversed order")
+        alone, _ = o.fused_insert_conv(spec(c)["x"], spec(c)["weight"], cache, *common[:5],
+                                       c.off_s, c.ws, c.block_size, c.activation,
+                                       c.use_residual)
+        assert_bits_equal(outs[i], alone, f"stream {i} alone")
+    untouched = np.ones(24, bool)
+    for c in cases:
+        untouched[c.off_s:c.off_s + c.ws] = False
+    assert untouched.sum() == 6
+    assert_bits_equal(k[..., untouched], cache[..., untouched], "columns of no stream")
+
+
 def test_fused_rejects_out_of_table_reads():
     case = workloads.fused_case(3, [2], [40], H=1, D=4, ws=4, block_size=4, W=4,
                                 dtype=torch.float64)

@@ -181,6 +181,35 @@ def fused_case(seed: int, new_lens: List[int], ctx_lens: List[int], *, H: int, D
                      used_blocks=used_blocks, poison_block=poison)
 
 
+def fused_streams_case(seed: int, new_lens: List[int], ctx_lens: List[int], *, H: int, D: int,
+                       streams, block_size: int = 16, W: int = 4, dtype="bf16",
+                       pad_count: int = 0, tail_pad: int = 0,
+                       pool_blocks: Optional[int] = None, activations=None, residuals=None,
+                       device="cpu") -> List[FusedCase]:
+    """Several conv streams of one layer over one shared cache: ``streams``
+    lists (off_s, ws) per stream.  Stream 0 is ``fused_case`` with these
+    arguments; each further stream draws its own x [T, H*ws] and weight
+    [H*ws, W] (N(0,1), N(0,0.5)) from a second generator seeded seed + 7919,
+    in stream order.  ``activations`` / ``residuals`` give one value per
+    stream (default SiLU and residual for all)."""
+    dt = _dt(dtype)
+    off0, ws0 = streams[0]
+    acts = activations if activations is not None else ["silu"] * len(streams)
+    ress = residuals if residuals is not None else [True] * len(streams)
+    base = fused_case(seed, new_lens, ctx_lens, H=H, D=D, ws=ws0, off_s=off0,
+                      block_size=block_size, W=W, dtype=dtype, pad_count=pad_count,
+                      tail_pad=tail_pad, pool_blocks=pool_blocks, activation=acts[0],
+                      use_residual=ress[0], device=device)
+    g = torch.Generator().manual_seed(seed + 7919)
+    cases = [base]
+    for k, (off, ws) in enumerate(streams[1:], start=1):
+        x = torch.randn(base.T, H * ws, generator=g).to(dt)
+        w = (torch.randn(H * ws, W, generator=g) * 0.5).to(dt)
+        cases.append(FusedCase(**{**base.__dict__, "x": x, "weight": w, "off_s": off, "ws": ws,
+                                  "activation": acts[k], "use_residual": ress[k]}))
+    return cases
+
+
 # ---------------------------------------------------------------- SSM-style ops
 
 @dataclass
