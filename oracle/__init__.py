@@ -34,6 +34,7 @@ _ERRORS = {
     -4: "physical block outside [0, num_blocks)",
     -5: "x row outside [0, T)",
     -6: "state slot outside [0, num_slots)",
+    -7: "state row outside [0, num_chunks)",
 }
 
 
@@ -282,4 +283,27 @@ def gather_conv_window(src, abs_positions, real_count: int, out, d_conv: int):
         _p(src), I64(seq_len), I32(conv_dim), I64(_es(src, 0)), I64(_es(src, 1)), _p(pos),
         I32(real_count), I32(out.shape[0]), _p(out), I64(_es(out, 0)), I32(d_conv), dt)
     _check(rc, "gather_conv_window")
+    return out
+
+
+def gather_ssm_state(states, chunk_indices, real_count: int, out):
+    """Returns a copy of ``out`` with slots < clamp(real_count) filled.
+
+    states [num_chunks, *state_shape], chunk_indices int64 [max_count],
+    out [max_count, *state_shape] (rows are flattened).
+    """
+    lib = _load()
+    st = _c(states)
+    dt = _dtype_code(st)
+    num_chunks = st.shape[0]
+    st2 = st.reshape(num_chunks, -1)
+    out = np.array(out, dtype=st.dtype, copy=True, order="C")
+    out2 = out.reshape(out.shape[0], -1)
+    if out2.shape[1] != st2.shape[1]:
+        raise ValueError("states and out rows differ in size")
+    idx = _c(chunk_indices, np.int64)
+    rc = lib.oracle_gather_ssm_state(
+        _p(st2), I64(num_chunks), I64(st2.shape[1]), I64(_es(st2, 0)), _p(idx), I32(real_count),
+        I32(out2.shape[0]), _p(out2), I64(_es(out2, 0)), dt)
+    _check(rc, "gather_ssm_state")
     return out

@@ -329,3 +329,28 @@ int oracle_gather_conv_window(const void* src, int64_t seq_len, int32_t conv_dim
   }
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* conditional gather of SSM-state rows                                */
+/* ------------------------------------------------------------------ */
+
+int oracle_gather_ssm_state(const void* states, int64_t num_chunks, int64_t state_flat,
+                            int64_t states_rs, const int64_t* chunk_indices,
+                            int32_t real_count, int32_t max_count, void* out, int64_t out_rs,
+                            int dtype) {
+  if (!valid_dtype(dtype) || num_chunks < 1 || state_flat < 0 || max_count < 0)
+    return ORC_ERR_ARGS;
+  /* Reading: as for the conv windows, a count outside [0, max_count] is
+     clamped into it. */
+  int64_t n = real_count;
+  if (n < 0) n = 0;
+  if (n > max_count) n = max_count;
+  for (int64_t i = 0; i < n; ++i) {
+    /* Slot i receives the whole state row chosen by its index. */
+    const int64_t r = chunk_indices[i];
+    if (r < 0 || r >= num_chunks) return ORC_ERR_CHUNK;
+    for (int64_t e = 0; e < state_flat; ++e)
+      copy_elem(out, i * out_rs + e, states, r * states_rs + e, dtype);
+  }
+  return ORC_OK;
+}

@@ -38,6 +38,7 @@ enum {
   ORC_ERR_BLOCK = -4,     /* physical block outside [0, num_blocks) */
   ORC_ERR_ROW = -5,       /* x row outside [0, T)                   */
   ORC_ERR_SLOT = -6,      /* state slot outside [0, num_slots)      */
+  ORC_ERR_CHUNK = -7,     /* state row outside [0, num_chunks)      */
 };
 
 /* bfloat16 helpers (bit patterns held in uint16_t). */
@@ -127,6 +128,20 @@ int oracle_gather_conv_window(const void* src, int64_t seq_len, int32_t conv_dim
                               int64_t src_ss, int64_t src_sc, const int32_t* abs_positions,
                               int32_t real_count, int32_t max_count, void* out,
                               int64_t out_ss, int32_t d_conv, int dtype);
+
+/*
+ * Conditional gather of whole SSM-state rows.  Page: Megatron-core
+ * "core.ssm.ops.intermediate_extraction", scatter_intermediate_ssm and the
+ * description of its kernel.
+ *   states [num_chunks, state_flat] row stride states_rs
+ *   chunk_indices int64 [max_count]: source row of each slot
+ *   out    [max_count, state_flat] row stride out_rs
+ *   real_count: host copy of the device count; slots >= it are untouched.
+ */
+int oracle_gather_ssm_state(const void* states, int64_t num_chunks, int64_t state_flat,
+                            int64_t states_rs, const int64_t* chunk_indices,
+                            int32_t real_count, int32_t max_count, void* out, int64_t out_rs,
+                            int dtype);
 
 #ifdef __cplusplus
 }

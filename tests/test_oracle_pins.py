@@ -507,6 +507,37 @@ def test_gather_window_equals_prefill_final_state():
         assert_bits_equal(g[0], st[0], f"p={p}")
 
 
+@pytest.mark.parametrize("real_count", [0, 1, 17, 40, 55, -3])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ssm_state_gather_matches_numpy_row_indexing(real_count, dt):
+    """Slots below the clamped count receive their state row bit for bit;
+    the others keep their bits."""
+    o = orc()
+    rng = np.random.default_rng(real_count + 77)
+    nc, shape, mc = 9, (3, 4, 5), 40
+    if dt == "f32":
+        states = rng.standard_normal((nc,) + shape).astype(np.float32)
+        out0 = np.full((mc,) + shape, -1.0, np.float32)
+    else:
+        states = rng.integers(0, 2**16, (nc,) + shape).astype(np.uint16)
+        out0 = np.full((mc,) + shape, 0xBEEF, np.uint16)
+    idx = rng.integers(0, nc, mc).astype(np.int64)
+    got = o.gather_ssm_state(states, idx, real_count, out0)
+    n = min(max(real_count, 0), mc)
+    want = out0.copy()
+    want[:n] = states[idx[:n]]
+    assert_bits_equal(got, want, "ssm gather")
+
+
+def test_ssm_state_gather_rejects_out_of_range_rows():
+    o = orc()
+    states = np.zeros((4, 6), np.float32)
+    idx = np.array([0, 4, 1], np.int64)
+    with pytest.raises(ValueError, match="num_chunks"):
+        o.gather_ssm_state(states, idx, 2, np.zeros((3, 6), np.float32))
+    o.gather_ssm_state(states, idx, 1, np.zeros((3, 6), np.float32))  # slot 1 is dead
+
+
 def test_named_workloads_are_well_formed():
     """The generators' layout obeys the preconditions the op relies on:
     slots point at the row's own position, no slot is written twice, and no
