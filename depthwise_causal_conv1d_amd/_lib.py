@@ -29,6 +29,7 @@ EXPORTS = (
     "causal_conv1d_varlen_fwd",
     "causal_conv1d_update",
     "gather_intermediate_conv_window",
+    "gather_intermediate_ssm_state",
 )
 
 P = ctypes.c_void_p
@@ -59,6 +60,7 @@ _SIGS = {
     "causal_conv1d_update": [P, I64, P, I64, I64, I64, I64, P, I64, I64, P, P, P, P, I64,
                              I32, I32, I32, I32, I32, I32, P],
     "gather_intermediate_conv_window": [P, I64, I32, I64, I64, P, P, I32, P, I64, I32, I32, P],
+    "gather_intermediate_ssm_state": [P, I64, I64, I64, P, P, I32, P, I64, I32, P],
 }
 
 
@@ -83,7 +85,12 @@ def load() -> ctypes.CDLL:
         lib.sconv_version.restype = ctypes.c_char_p
         lib.sconv_version.argtypes = []
         for name, args in _SIGS.items():
-            fn = getattr(lib, name)
+            try:
+                fn = getattr(lib, name)
+            except AttributeError:
+                raise ImportError(
+                    f"{LIB_PATH} lacks {name}: it is older than the sources; rebuild it with "
+                    "`python -m depthwise_causal_conv1d_amd.build`") from None
             fn.restype = ctypes.c_int
             fn.argtypes = args
         _lib = lib

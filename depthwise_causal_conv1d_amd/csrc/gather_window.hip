@@ -161,7 +161,105 @@ static void launch_gather(int dc, const GatherParams& p, dim3 g, uint32_t th, hi
   }
 }
 
+// ---------------------------------------------------------------- SSM-state rows
+
+struct SsmGatherParams {
+  const void* states;
+  const int64_t* idx;
+  const int32_t* real_count;
+  void* out;
+  int64_t states_rs, out_rs;  // row strides in units of T
+  int64_t nvec;               // units of T per row
+  int32_t max_count, threads;
+};
+
+#ifndef SCONV_SSM_GATHER_UNROLL
+#define SCONV_SSM_GATHER_UNROLL 4  // units of T per thread
+#endif
+
+// One workgroup per (column block, slot): the live count and the slot's
+// source row are fetched in one round trip, dead slots leave at once, and
+// live ones copy U units of T per thread (T = 16 bytes when the rows allow
+// it), with streaming stores.
+template <typename T, int U>
+__global__ __launch_bounds__(256) void gather_ssm_kernel(const SsmGatherParams p) {
+  const int slot = (int)blockIdx.y;  // grid: (column blocks, max_count)
+  asm volatile("" ::"s"(p.states), "s"(p.out), "s"(p.states_rs), "s"(p.out_rs), "s"(p.nvec),
+               "s"(p.threads), "s"(p.max_count));
+  int n = *p.real_count;
+  const int64_t r = p.idx[slot];
+  asm volatile("" ::"v"(n), "v"(r));
+  n = n < 0 ? 0 : (n > p.max_count ? p.max_count : n);
+  if (slot >= n) return;  // dead slot: no traffic
+  const T* __restrict__ src = static_cast<const T*>(p.states) + r * p.states_rs;
+  T* __restrict__ dst = static_cast<T*>(p.out) + (int64_t)slot * p.out_rs;
+  const int64_t base = (int64_t)blockIdx.x * p.threads * U + threadIdx.x;
+  T v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + (int64_t)u * p.threads;
+    if (i < p.nvec) v[u] = src[i];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + (int64_t)u * p.threads;
+    if (i < p.nvec) __builtin_nontemporal_store(v[u], dst + i);
+  }
+}
+
+template <typename T>
+static void launch_ssm(const SsmGatherParams& p, hipStream_t s) {
+  constexpr int U = SCONV_SSM_GATHER_UNROLL;
+  const dim3 grid((uint32_t)cdiv(p.nvec, (int64_t)p.threads * U), (uint32_t)p.max_count);
+  hipLaunchKernelGGL((gather_ssm_kernel<T, U>), grid, dim3(p.threads), 0, s, p);
+}
+
 }  // namespace sconv
+
+extern "C" int gather_intermediate_ssm_state(const void* states, int64_t num_chunks,
+                                             int64_t state_flat, int64_t states_row_stride,
+                                             const int64_t* chunk_indices,
+                                             const int32_t* real_count_dev, int32_t max_count,
+                                             void* out, int64_t out_row_stride, int32_t dtype,
+                                             hipStream_t stream) {
+  using namespace sconv;
+  clear_error();
+  const char* fn = "gather_intermediate_ssm_state";
+  if (!valid_dtype(dtype)) return fail(SCONV_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (num_chunks < 1) return fail(SCONV_ERR_INVALID, "%s: num_chunks < 1", fn);
+  if (state_flat < 0 || max_count < 0)
+    return fail(SCONV_ERR_INVALID, "%s: state_flat and max_count must be >= 0", fn);
+  if (max_count > 65535)
+    return fail(SCONV_ERR_UNSUPPORTED, "%s: max_count above 65535 (one grid row per slot)", fn);
+  if (states_row_stride < state_flat || out_row_stride < state_flat)
+    return fail(SCONV_ERR_INVALID, "%s: row strides smaller than state_flat", fn);
+  if (state_flat == 0 || max_count == 0) return SCONV_OK;
+  if (!states || !chunk_indices || !real_count_dev || !out)
+    return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
+  const int64_t es = elem_size(dtype);
+  const int64_t s_bytes = ((num_chunks - 1) * states_row_stride + state_flat) * es;
+  const int64_t o_bytes = ((int64_t)(max_count - 1) * out_row_stride + state_flat) * es;
+  if (overlap(out, o_bytes, states, s_bytes))
+    return fail(SCONV_ERR_INVALID, "%s: out overlaps states", fn);
+  SsmGatherParams p;
+  p.states = states; p.idx = chunk_indices; p.real_count = real_count_dev; p.out = out;
+  p.max_count = max_count;
+  p.threads = 256;
+  const bool vec = (state_flat * es) % 16 == 0 && (states_row_stride * es) % 16 == 0 &&
+                   (out_row_stride * es) % 16 == 0 && aligned16(states) && aligned16(out);
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  if (vec) {
+    const int64_t per = 16 / es;
+    p.nvec = state_flat / per; p.states_rs = states_row_stride / per;
+    p.out_rs = out_row_stride / per;
+    launch_ssm<u4>(p, stream);
+  } else {
+    p.nvec = state_flat; p.states_rs = states_row_stride; p.out_rs = out_row_stride;
+    if (es == 2) launch_ssm<uint16_t>(p, stream);
+    else launch_ssm<uint32_t>(p, stream);
+  }
+  return check_launch(fn);
+}
 
 extern "C" int gather_intermediate_conv_window(const void* src, int64_t seq_len,
                                                int32_t conv_dim, int64_t src_stride_s,

@@ -337,3 +337,30 @@ def gather_intermediate_conv_window(src: torch.Tensor, abs_positions: torch.Tens
         _ptr(src), src.shape[1], conv_dim, src.stride(1), src.stride(2), _ptr(abs_positions),
         _ptr(real_count_gpu), max_count, _ptr(out), out.stride(0), d_conv, dt, _stream(src))
     _lib.check(rc, "gather_intermediate_conv_window")
+
+
+def gather_intermediate_ssm_state(states: torch.Tensor, chunk_indices: torch.Tensor,
+                                  real_count_gpu: torch.Tensor, out: torch.Tensor) -> None:
+    """Copy states[chunk_indices[i]] into out[i] for the first real_count
+    slots (count read on the device).  states [num_chunks, *state_shape],
+    out [max_count, *state_shape]; each row must be dense."""
+    _dev(states, chunk_indices, real_count_gpu, out)
+    dt = _dtype(states)
+    if out.dtype != states.dtype:
+        raise TypeError("states and out must share one element type")
+    if states.shape[1:] != out.shape[1:]:
+        raise ValueError("states and out rows must have one shape")
+    flat = 1
+    for d in states.shape[1:]:
+        flat *= d
+    for t, name in ((states, "states"), (out, "out")):
+        if t.dim() > 1 and not t[0].is_contiguous():
+            raise ValueError(f"{name} rows must be dense")
+    max_count = out.shape[0]
+    _vec(chunk_indices, torch.int64, "chunk_indices", max_count)
+    _vec(real_count_gpu, torch.int32, "real_count_gpu", 1)
+    rc = _lib.load().gather_intermediate_ssm_state(
+        _ptr(states), states.shape[0], flat, states.stride(0) if states.dim() > 1 else 1,
+        _ptr(chunk_indices), _ptr(real_count_gpu), max_count, _ptr(out),
+        out.stride(0) if out.dim() > 1 else 1, dt, _stream(states))
+    _lib.check(rc, "gather_intermediate_ssm_state")

@@ -326,6 +326,38 @@ int gather_intermediate_conv_window(const void* src, int64_t seq_len, int32_t co
                                     void* out, int64_t out_slot_stride, int32_t d_conv,
                                     int32_t dtype, hipStream_t stream);
 
+/*
+ * gather_intermediate_ssm_state -- conditional gather of whole SSM-state
+ * rows, with the live slot count read on the device.
+ *
+ * Source: Megatron-core page "core.ssm.ops.intermediate_extraction", module
+ * description, _scatter_intermediate_ssm_kernel and scatter_intermediate_ssm.
+ *
+ *   states         [num_chunks, state_flat] row stride states_row_stride:
+ *                  one layer's chunk-scan states, each flattened (device)
+ *   chunk_indices  int64 [max_count] source row of each slot (device)
+ *   real_count_dev int32 [1] number of live slots, read ON THE DEVICE when
+ *                  the kernel runs (clamped into [0, max_count]); the grid is
+ *                  sized by max_count, so the call is graph-replay safe
+ *   out            [max_count, state_flat] row stride out_row_stride
+ *
+ * For slot i < n: out[i, :] = states[chunk_indices[i], :] (bit copies).
+ * Slots i >= n are not written and cost no memory traffic.
+ *
+ * Device-data contract: chunk_indices[i] lies in [0, num_chunks) for every
+ * live slot.
+ *
+ * Host errors (SCONV_ERR_INVALID): num_chunks < 1, state_flat < 0,
+ * max_count < 0, a row stride smaller than state_flat, NULL pointer, unknown
+ * dtype, out overlapping states.  SCONV_ERR_UNSUPPORTED: max_count above
+ * 65535 (each slot is one row of the launch grid).  state_flat == 0 or
+ * max_count == 0 is a successful no-op.
+ */
+int gather_intermediate_ssm_state(const void* states, int64_t num_chunks, int64_t state_flat,
+                                  int64_t states_row_stride, const int64_t* chunk_indices,
+                                  const int32_t* real_count_dev, int32_t max_count, void* out,
+                                  int64_t out_row_stride, int32_t dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -145,6 +145,17 @@ def test_streams_entry_rejects_bad_host_arguments(lib):
     assert call(ok, 3, seq=ctypes.addressof(one), qs=ctypes.addressof(one)) == 0
 
 
+def test_ssm_gather_rejects_bad_host_arguments(lib):
+    g = lib.gather_intermediate_ssm_state
+    assert g(NULL, 0, 8, 8, NULL, NULL, 4, NULL, 8, 0, NULL) == 1        # no rows
+    assert g(NULL, 4, 8, 7, NULL, NULL, 4, NULL, 8, 0, NULL) == 1        # stride < row
+    assert g(NULL, 4, 8, 8, NULL, NULL, 65536, NULL, 8, 0, NULL) == 2    # grid rows
+    assert b"65535" in lib.sconv_last_error()
+    assert g(NULL, 4, 8, 8, NULL, NULL, 4, NULL, 8, 7, NULL) == 1        # dtype
+    assert g(NULL, 4, 8, 8, NULL, NULL, 0, NULL, 8, 0, NULL) == 0        # no slots: no-op
+    assert g(NULL, 4, 8, 8, NULL, NULL, 4, NULL, 8, 0, NULL) == 1        # NULL pointers
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     """The binding has no CPU fallback: a missing library is an import error."""
     from depthwise_causal_conv1d_amd import _lib

@@ -602,3 +602,67 @@ def test_gather_graph_replay_with_device_count():
         out_r = oracle.gather_conv_window(to_np(gc.src), to_np(gc.abs_positions), n,
                                           to_np(gc.out_init), 3)
         assert_bits_equal(to_np(out), out_r, f"replay n={n}")
+
+
+# ------------------------------------------------------------------ SSM-state row gather
+
+SSM_GATHER = [
+    # name, dtype, num_chunks, state shape, max_count
+    ("f32-vec", torch.float32, 11, (3, 4, 8), 23),        # 384-byte rows: 16-byte path
+    ("bf16-vec", torch.bfloat16, 7, (2, 64, 16), 9),      # 4 KiB rows
+    ("bf16-elem", torch.bfloat16, 5, (3, 15), 13),        # 90-byte rows: element path
+    ("f32-big", torch.float32, 6, (16, 64, 256), 5),      # 1 MiB rows, many column blocks
+]
+
+
+@pytest.mark.parametrize("spec", SSM_GATHER, ids=[s[0] for s in SSM_GATHER])
+def test_ssm_state_gather_sweep(spec):
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    name, dt, nc, shape, mc = spec
+    g = torch.Generator().manual_seed(nc * 31 + mc)
+    states = torch.randn((nc,) + shape, generator=g).to(dt)
+    idx = torch.randint(0, nc, (mc,), generator=g)
+    out0 = torch.full((mc,) + shape, SENTINEL).to(dt)
+    say(f"ssm gather {name}: {nc} rows of {shape}, max_count {mc}")
+    st_d, idx_d = states.to(DEV), idx.to(DEV)
+    for n in (0, 1, mc // 2, mc, mc + 5, -2):
+        out_r = oracle.gather_ssm_state(to_np(states), to_np(idx), n, to_np(out0))
+        out_g = out0.to(DEV).clone()
+        lib.gather_intermediate_ssm_state(st_d, idx_d,
+                                          torch.tensor([n], dtype=torch.int32, device=DEV), out_g)
+        assert_bits_equal(to_np(out_g), out_r, f"{name} n={n}")
+
+
+def test_ssm_state_gather_graph_replay_with_device_count():
+    """Grid fixed at capture (max_count); the live count and the indices
+    change between replays through their fixed device buffers only."""
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    g = torch.Generator().manual_seed(5)
+    nc, shape, mc = 8, (4, 32, 16), 40
+    states = torch.randn((nc,) + shape, generator=g)
+    out0 = torch.full((mc,) + shape, SENTINEL)
+    st_d = states.to(DEV)
+    idx_d = torch.zeros(mc, dtype=torch.int64, device=DEV)
+    rc = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = out0.to(DEV).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lib.gather_intermediate_ssm_state(st_d, idx_d, rc, out)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lib.gather_intermediate_ssm_state(st_d, idx_d, rc, out)
+    torch.cuda.synchronize()
+    for n in (0, mc, 3, 17, 1):
+        idx = torch.randint(0, nc, (mc,), generator=g)
+        idx_d.copy_(idx.to(DEV))
+        out.copy_(out0.to(DEV))
+        rc.fill_(n)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        out_r = oracle.gather_ssm_state(to_np(states), to_np(idx), n, to_np(out0))
+        assert_bits_equal(to_np(out), out_r, f"replay n={n}")
