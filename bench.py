@@ -603,6 +603,56 @@ class SsmDecodeBench(Workload):
         return 8 / spent, "one decode step (8 rows)", spent
 
 
+class SsmStateGatherBench(Workload):
+    """Prefix-cache extraction of SSM states: 96 live of 128 slots, each a
+    whole state row (64 heads x 64 x 128 fp32 = 2 MiB) gathered from 128
+    chunk states at distinct indices; three replicas, so a step reads HBM,
+    not the MALL."""
+    kernel_name = "gather_ssm_kernel"
+    dtype = "f32"
+    SHAPE = (64, 64, 128)
+    CHUNKS, SLOTS, LIVE, R_ = 128, 128, 96, 3
+
+    def __init__(self, dev="cuda"):
+        import torch
+
+        import depthwise_causal_conv1d_amd as lib
+        self.lib = lib
+        g = torch.Generator().manual_seed(8)
+        self.R = self.R_
+        self.states = [torch.randn((self.CHUNKS,) + self.SHAPE, generator=g).to(dev)
+                       for _ in range(self.R)]
+        # Distinct source rows: a repeated row would be served from cache.
+        self.idx = [torch.randperm(self.CHUNKS, generator=g)[:self.SLOTS].to(dev)
+                    for _ in range(self.R)]
+        self.out = [torch.empty((self.SLOTS,) + self.SHAPE, device=dev) for _ in range(self.R)]
+        self.rc = torch.tensor([self.LIVE], dtype=torch.int32, device=dev)
+        row = 4 * self.SHAPE[0] * self.SHAPE[1] * self.SHAPE[2]
+        self.bytes_per_launch = 2 * self.LIVE * row + 8 * self.LIVE + 4
+        self.tokens_per_step = self.LIVE  # one unit per extracted slot
+
+    def kernel(self, i):
+        self.lib.gather_intermediate_ssm_state(self.states[i], self.idx[i], self.rc, self.out[i])
+
+    step = kernel
+
+    def config(self):
+        return {"workload": "ssm_state_gather", "unit_per_token": "one extracted slot",
+                "num_chunks": self.CHUNKS, "max_count": self.SLOTS, "real_count": self.LIVE,
+                "state_shape": list(self.SHAPE), "state_dtype": "f32", "graph": "hipGraph",
+                "replicas": self.R}
+
+    def oracle_sample(self, budget):
+        import oracle
+        st = self.states[0][:16].cpu().numpy()
+        idx = (self.idx[0].cpu() % 16).numpy()
+        out0 = self.out[0][:32].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.gather_ssm_state(st, idx, 32, out0)
+        spent = time.perf_counter() - t0
+        return 32 / spent, "32 slots from 16 chunk states", spent
+
+
 def torch_where(mask):
     import torch
     return torch.nonzero(mask).flatten()
@@ -615,10 +665,12 @@ WORKLOADS = {
     "spec_decode": SpecDecodeBench,
     "ssm_prefill": SsmPrefillBench,
     "ssm_decode": SsmDecodeBench,
+    "ssm_state_gather": SsmStateGatherBench,
 }
 
 DEFAULT_STEPS = {"batched_decode": 19200, "decode_layer": 9600, "mixed_prefill": 200,
-                 "spec_decode": 2000, "ssm_prefill": 200, "ssm_decode": 6400}
+                 "spec_decode": 2000, "ssm_prefill": 200, "ssm_decode": 6400,
+                 "ssm_state_gather": 600}
 
 
 # ---------------------------------------------------------------- timing
