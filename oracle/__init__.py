@@ -264,6 +264,32 @@ def causal_conv1d_update(x, conv_states, weight, bias, activation, conv_state_in
     return out, st_out
 
 
+def causal_conv1d_update_tokens(x, conv_states, weight, bias, activation, cache_seqlens=None,
+                                conv_state_indices=None, pad_slot_id: int = -1, out_init=None):
+    """Returns (out, conv_states_after).  x [batch, dim, seqlen];
+    conv_states [num_slots, dim, state_len]; cache_seqlens int32 [batch] or
+    None (see oracle_causal_conv1d_update_tokens for both state readings)."""
+    lib = _load()
+    x = _c(x)
+    dt = _dtype_code(x)
+    w = _c(weight, x.dtype)
+    b = _c(bias, x.dtype)
+    st_in = _c(conv_states, x.dtype)
+    st_out = st_in.copy()
+    cs = _c(cache_seqlens, np.int32)
+    ci = _c(conv_state_indices, np.int32)
+    batch, dim, seqlen = x.shape
+    out = np.zeros_like(x) if out_init is None else np.array(out_init, dtype=x.dtype, copy=True)
+    rc = lib.oracle_causal_conv1d_update_tokens(
+        _p(x), I64(_es(x, 0)), I64(_es(x, 1)), I64(_es(x, 2)), I32(seqlen), _p(st_in),
+        _p(st_out), I64(st_in.shape[0]), I32(st_in.shape[2]), I64(_es(st_in, 0)),
+        I64(_es(st_in, 1)), I64(_es(st_in, 2)), _p(w), I64(_es(w, 0)), I64(_es(w, 1)), _p(b),
+        _p(cs), _p(ci), _p(out), I64(_es(out, 0)), I64(_es(out, 1)), I64(_es(out, 2)),
+        I32(batch), I32(dim), I32(w.shape[1]), dt, _act(activation), I32(pad_slot_id))
+    _check(rc, "causal_conv1d_update_tokens")
+    return out, st_out
+
+
 def gather_conv_window(src, abs_positions, real_count: int, out, d_conv: int):
     """Returns a copy of ``out`` with slots < clamp(real_count) filled.
 

@@ -301,6 +301,74 @@ int oracle_causal_conv1d_update(const void* x, int64_t x_rs, const void* st_in,
 }
 
 /* ------------------------------------------------------------------ */
+/* multi-token update, shift or ring state                             */
+/* ------------------------------------------------------------------ */
+
+int oracle_causal_conv1d_update_tokens(
+    const void* x, int64_t x_sb, int64_t x_sc, int64_t x_st, int32_t seqlen, const void* st_in,
+    void* st_out, int64_t num_slots, int32_t state_len, int64_t ss_slot, int64_t ss_c,
+    int64_t ss_k, const void* w, int64_t w_sc, int64_t w_sk, const void* bias,
+    const int32_t* cache_seqlens, const int32_t* conv_state_indices, void* out, int64_t out_sb,
+    int64_t out_sc, int64_t out_st, int32_t batch, int32_t dim, int32_t W, int dtype, int act,
+    int32_t pad_slot_id) {
+  if (!valid_dtype(dtype) || batch < 0 || dim < 0 || W < 1 || seqlen < 0 ||
+      state_len < W - 1 || (cache_seqlens && state_len < 1))
+    return ORC_ERR_ARGS;
+  const int64_t L = state_len;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t slot = conv_state_indices ? conv_state_indices[b] : b;
+    if (slot == pad_slot_id) continue;
+    if (slot < 0 || slot >= num_slots) return ORC_ERR_SLOT;
+    const int64_t s = cache_seqlens ? cache_seqlens[b] : 0;
+    if (s < 0) return ORC_ERR_ARGS;
+    for (int32_t c = 0; c < dim; ++c) {
+      const int64_t sbase = slot * ss_slot + (int64_t)c * ss_c;
+      const int64_t xbase = (int64_t)b * x_sb + (int64_t)c * x_sc;
+      for (int32_t i = 0; i < seqlen; ++i) {
+        double acc = bias ? ld(bias, dtype, c) : 0.0;
+        for (int32_t k = 0; k < W; ++k) {
+          const int64_t lag = W - 1 - k;
+          double v;
+          if (!cache_seqlens) {
+            /* Shift state: index j of the sequence state ++ x. */
+            const int64_t j = L + i - lag;
+            v = j < L ? ld(st_in, dtype, sbase + j * ss_k)
+                      : ld(x, dtype, xbase + (j - L) * x_st);
+          } else {
+            /* Ring state: absolute positions. */
+            const int64_t pos = s + i - lag;
+            if (pos < 0)
+              v = 0.0;
+            else if (pos >= s)
+              v = ld(x, dtype, xbase + (pos - s) * x_st);
+            else
+              v = ld(st_in, dtype, sbase + (pos % L) * ss_k);
+          }
+          acc += ld(w, dtype, (int64_t)c * w_sc + (int64_t)k * w_sk) * v;
+        }
+        st(out, dtype, (int64_t)b * out_sb + (int64_t)c * out_sc + (int64_t)i * out_st,
+           activate(acc, act));
+      }
+      if (!cache_seqlens) {
+        /* Column m of the new state is entry seqlen + m of state ++ x. */
+        for (int64_t m = 0; m < L; ++m) {
+          const int64_t j = seqlen + m;
+          if (j < L)
+            copy_elem(st_out, sbase + m * ss_k, st_in, sbase + j * ss_k, dtype);
+          else
+            copy_elem(st_out, sbase + m * ss_k, x, xbase + (j - L) * x_st, dtype);
+        }
+      } else {
+        /* Each new input lands in its ring column, in order. */
+        for (int32_t i = 0; i < seqlen; ++i)
+          copy_elem(st_out, sbase + ((s + i) % L) * ss_k, x, xbase + (int64_t)i * x_st, dtype);
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
 /* conditional gather of conv windows                                  */
 /* ------------------------------------------------------------------ */
 

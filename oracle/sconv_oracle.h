@@ -116,6 +116,31 @@ int oracle_causal_conv1d_update(const void* x, int64_t x_rs, const void* st_in,
                                 int dtype, int act, int32_t pad_slot_id);
 
 /*
+ * Multi-token state update, with an optional ring-buffer state.  Page:
+ * sglang "Implementation:Sgl project Sglang Mamba Ops", Signature and I/O
+ * Contract of causal_conv1d_update (cache_seqlens is listed there without
+ * semantics; the reading below is ours).
+ *   x     [batch, dim, seqlen] strides (x_sb, x_sc, x_st)
+ *   state [num_slots, dim, state_len] strides (ss_slot, ss_c, ss_k),
+ *         state_len >= W-1; st_out must start as a copy of st_in
+ *   out   [batch, dim, seqlen] strides (out_sb, out_sc, out_st)
+ * Without cache_seqlens the state is the last state_len inputs, oldest
+ * first; token i convolves the W taps ending at it in state ++ x, and the
+ * state becomes the last state_len entries of state ++ x.  With
+ * cache_seqlens[b] = s (the position of x[b, :, 0]) the state is a ring:
+ * the input at position p sits in column p % state_len; taps before
+ * position 0 are zero, taps at positions >= s come from x, earlier ones
+ * from the ring; afterwards column (s + i) % state_len holds x[b, :, i].
+ */
+int oracle_causal_conv1d_update_tokens(
+    const void* x, int64_t x_sb, int64_t x_sc, int64_t x_st, int32_t seqlen, const void* st_in,
+    void* st_out, int64_t num_slots, int32_t state_len, int64_t ss_slot, int64_t ss_c,
+    int64_t ss_k, const void* w, int64_t w_sc, int64_t w_sk, const void* bias,
+    const int32_t* cache_seqlens, const int32_t* conv_state_indices, void* out, int64_t out_sb,
+    int64_t out_sc, int64_t out_st, int32_t batch, int32_t dim, int32_t W, int dtype, int act,
+    int32_t pad_slot_id);
+
+/*
  * Conditional gather of the length-d_conv window ending before each slot's
  * position, written transposed.  Page: Megatron-core
  * "core.ssm.ops.intermediate_extraction", scatter_intermediate_conv and its

@@ -507,6 +507,122 @@ def test_gather_window_equals_prefill_final_state():
         assert_bits_equal(g[0], st[0], f"p={p}")
 
 
+# ------------------------------------------------------------------ multi-token / ring update
+
+def _upd_inputs(seed, batch, dim, W, L, seqlen, slots):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, dim, seqlen))
+    w = rng.standard_normal((dim, W)) * 0.5
+    bias = rng.standard_normal(dim) * 0.1
+    st = rng.standard_normal((slots, dim, L))
+    idx = rng.permutation(slots)[:batch].astype(np.int32)
+    return x, w, bias, st, idx
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+def test_update_tokens_one_token_equals_single_update(W):
+    """seqlen 1 with a W-1 state is exactly causal_conv1d_update (f64 and
+    bf16 bits), PAD rows included."""
+    o = orc()
+    x, w, bias, st, idx = _upd_inputs(W, 6, 5, W, W - 1, 1, 9)
+    idx[2] = -1
+    for cast in (lambda a: a, lambda a: to_np(torch.from_numpy(a).to(torch.bfloat16))):
+        out_a, st_a = o.causal_conv1d_update(cast(np.ascontiguousarray(x[:, :, 0])), cast(st),
+                                             cast(w), cast(bias), "silu", idx, -1)
+        out_b, st_b = o.causal_conv1d_update_tokens(cast(x), cast(st), cast(w), cast(bias),
+                                                    "silu", None, idx, -1)
+        assert_bits_equal(out_b[:, :, 0], out_a, "out")
+        assert_bits_equal(st_b, st_a, "state")
+
+
+@pytest.mark.parametrize("L", [3, 5])
+def test_update_tokens_equals_one_token_steps(L):
+    """k tokens in one shift-state call equal k one-token calls, outputs and
+    final state bit for bit (a state longer than W-1 keeps more history)."""
+    o = orc()
+    x, w, bias, st, idx = _upd_inputs(L, 4, 6, 4, L, 7, 5)
+    out_m, st_m = o.causal_conv1d_update_tokens(x, st, w, bias, "silu", None, idx, -1)
+    cur = st
+    for i in range(7):
+        oi, cur = o.causal_conv1d_update_tokens(np.ascontiguousarray(x[:, :, i:i + 1]), cur, w,
+                                                bias, "silu", None, idx, -1)
+        assert_bits_equal(out_m[:, :, i], oi[:, :, 0], f"token {i}")
+    assert_bits_equal(st_m, cur, "state")
+
+
+def test_update_tokens_ring_fresh_sequence_equals_zero_padded_conv():
+    """A ring state fed from position 0 in calls of 3, 1, 5 and 2 tokens gives
+    the zero-padded causal conv of all 11 inputs (torch conv1d, f64)."""
+    o = orc()
+    W, L, dim = 4, 5, 3
+    rng = np.random.default_rng(12)
+    xs = rng.standard_normal((1, dim, 11))
+    w = rng.standard_normal((dim, W)) * 0.5
+    bias = rng.standard_normal(dim) * 0.1
+    st = np.zeros((1, dim, L))
+    outs, s = [], 0
+    for n in (3, 1, 5, 2):
+        oi, st = o.causal_conv1d_update_tokens(np.ascontiguousarray(xs[:, :, s:s + n]), st, w,
+                                               bias, "silu", np.array([s], np.int32), None, -1)
+        outs.append(oi)
+        s += n
+    got = np.concatenate(outs, axis=2)
+    ref = F.conv1d(F.pad(torch.from_numpy(xs), (W - 1, 0)), torch.from_numpy(w)[:, None, :],
+                   torch.from_numpy(bias), groups=dim).numpy()
+    np.testing.assert_allclose(got, silu_np(ref), rtol=1e-12, atol=1e-12)
+    # the ring holds the last L inputs at their position's column
+    for p in range(11 - L, 11):
+        np.testing.assert_array_equal(st[0, :, p % L], xs[0, :, p])
+
+
+def test_update_tokens_ring_equals_rotated_shift_state():
+    """With s >= state_len, a ring call equals a shift call on the ring
+    rotated into chronological order: same outputs, and the new ring is the
+    new shift state rotated back (bit for bit)."""
+    o = orc()
+    W, L, T = 4, 6, 4
+    x, w, bias, ring, idx = _upd_inputs(21, 3, 4, W, L, T, 3)
+    s = np.array([9, 14, 6], np.int32)
+    out_r, ring_new = o.causal_conv1d_update_tokens(x, ring, w, bias, None, s, idx, -1)
+    chrono = np.empty_like(ring)
+    for b in range(3):
+        sl = idx[b]
+        for m in range(L):
+            chrono[sl, :, m] = ring[sl, :, (s[b] - L + m) % L]
+    out_s, chrono_new = o.causal_conv1d_update_tokens(x, chrono, w, bias, None, None, idx, -1)
+    assert_bits_equal(out_r, out_s, "outputs")
+    for b in range(3):
+        sl = idx[b]
+        for m in range(L):
+            assert_bits_equal(ring_new[sl, :, (s[b] + T - L + m) % L], chrono_new[sl, :, m],
+                              f"row {b} column {m}")
+
+
+def test_update_tokens_ring_never_reads_before_position_zero():
+    """s = 2 < W-1: the ring column of position -1 holds NaN and is never
+    read; the outputs are the zero-padded conv of the stored positions 0, 1
+    and the new inputs.  A PAD row keeps its output and state bits."""
+    o = orc()
+    W, L, dim = 4, 3, 2
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, dim, 3))
+    w = rng.standard_normal((dim, W)) * 0.5
+    ring = np.full((2, dim, L), np.nan)
+    prev = rng.standard_normal((dim, 2))
+    ring[0, :, 0], ring[0, :, 1] = prev[:, 0], prev[:, 1]
+    idx = np.array([0, -1], np.int32)
+    out0 = np.full((2, dim, 3), 7.0)
+    got, ring_new = o.causal_conv1d_update_tokens(x, ring, w, None, None,
+                                                  np.array([2, 0], np.int32), idx, -1,
+                                                  out_init=out0)
+    seq = np.concatenate([prev, x[0]], axis=1)[None]
+    ref = F.conv1d(F.pad(torch.from_numpy(seq), (W - 1, 0)), torch.from_numpy(w)[:, None, :],
+                   groups=dim).numpy()[0, :, 2:]
+    np.testing.assert_allclose(got[0], ref, rtol=1e-12, atol=1e-12)
+    assert_bits_equal(got[1], out0[1], "PAD row output")
+    assert_bits_equal(ring_new[1], ring[1], "PAD row state")
+
+
 @pytest.mark.parametrize("real_count", [0, 1, 17, 40, 55, -3])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_ssm_state_gather_matches_numpy_row_indexing(real_count, dt):
