@@ -603,6 +603,63 @@ class SsmDecodeBench(Workload):
         return 8 / spent, "one decode step (8 rows)", spent
 
 
+class SsmSpecDecodeBench(Workload):
+    """Speculative decode on the SSM state pool: 8 rows x 4 draft tokens of
+    dim 8192 per step against ring states (W-1 columns, positions
+    uniform[0, 4096)), through causal_conv1d_update_tokens; 64 steps per
+    graph, each with its own inputs and outputs."""
+    kernel_name = "update_tokens_kernel"
+    B, T, DIM, W, STEPS = 8, 4, 8192, 4, 64
+
+    def __init__(self, dev="cuda"):
+        import torch
+
+        import depthwise_causal_conv1d_amd as lib
+        import workloads
+        self.lib = lib
+        c = workloads.ssm_varlen()
+        self.case = c
+        g = torch.Generator().manual_seed(11)
+        self.R = self.STEPS
+        # x [R, batch, T, dim] with channels contiguous, viewed [batch, dim, T]
+        self.x = torch.randn(self.R, self.B, self.T, self.DIM, generator=g).to(torch.bfloat16).to(dev)
+        self.out = torch.empty_like(self.x)
+        self.w, self.b = c.weight.to(dev), c.bias.to(dev)
+        self.st = c.conv_states.to(dev)
+        self.ci = c.cache_indices.to(dev)
+        self.seqlens = torch.randint(0, 4096, (self.R, self.B), generator=g).to(torch.int32).to(dev)
+        e = 2
+        self.bytes_per_launch = (2 * self.B * self.T * self.DIM * e        # x in, out
+                                 + 2 * self.B * self.DIM * (self.W - 1) * e  # state in, out
+                                 + self.DIM * (self.W + 1) * e + 8 * self.B)
+        self.tokens_per_step = self.B * self.T
+
+    def kernel(self, i):
+        self.lib.causal_conv1d_update_tokens(self.x[i].permute(0, 2, 1), self.st, self.w, self.b,
+                                             True, self.seqlens[i], self.ci, -1,
+                                             out=self.out[i].permute(0, 2, 1))
+
+    step = kernel
+
+    def config(self):
+        return {"workload": "ssm_spec_decode", "batch": self.B, "draft_tokens": self.T,
+                "dim": self.DIM, "W": self.W, "state": "ring, W-1 columns",
+                "positions": "uniform[0,4096)", "state_slots": 1024, "activation": "silu",
+                "bias": True, "graph": "hipGraph", "steps_per_graph": self.STEPS}
+
+    def oracle_sample(self, budget):
+        import oracle
+        from tests.helpers import to_np
+        c = self.case
+        x = to_np(self.x[0].permute(0, 2, 1).cpu())
+        t0 = time.perf_counter()
+        oracle.causal_conv1d_update_tokens(x, to_np(c.conv_states), to_np(c.weight),
+                                           to_np(c.bias), "silu", to_np(self.seqlens[0].cpu()),
+                                           to_np(c.cache_indices), -1)
+        spent = time.perf_counter() - t0
+        return self.B * self.T / spent, "one step (8 rows x 4 tokens)", spent
+
+
 class SsmStateGatherBench(Workload):
     """Prefix-cache extraction of SSM states: 96 live of 128 slots, each a
     whole state row (64 heads x 64 x 128 fp32 = 2 MiB) gathered from 128
@@ -665,12 +722,13 @@ WORKLOADS = {
     "spec_decode": SpecDecodeBench,
     "ssm_prefill": SsmPrefillBench,
     "ssm_decode": SsmDecodeBench,
+    "ssm_spec_decode": SsmSpecDecodeBench,
     "ssm_state_gather": SsmStateGatherBench,
 }
 
 DEFAULT_STEPS = {"batched_decode": 19200, "decode_layer": 9600, "mixed_prefill": 200,
                  "spec_decode": 2000, "ssm_prefill": 200, "ssm_decode": 6400,
-                 "ssm_state_gather": 600}
+                 "ssm_spec_decode": 6400, "ssm_state_gather": 600}
 
 
 # ---------------------------------------------------------------- timing

@@ -10,6 +10,7 @@ build module runs even where an older library lies next to it.
 from ._lib import LibsconvError, load
 from .ops import (
     causal_conv1d_update,
+    causal_conv1d_update_tokens,
     causal_conv1d_varlen_fwd,
     gather_intermediate_conv_window,
     gather_intermediate_ssm_state,
@@ -23,6 +24,7 @@ from .ops import (
 __all__ = [
     "LibsconvError",
     "causal_conv1d_update",
+    "causal_conv1d_update_tokens",
     "causal_conv1d_varlen_fwd",
     "gather_intermediate_conv_window",
     "gather_intermediate_ssm_state",

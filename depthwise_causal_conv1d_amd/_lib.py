@@ -28,6 +28,7 @@ EXPORTS = (
     "sconv_fused_insert_conv_streams",
     "causal_conv1d_varlen_fwd",
     "causal_conv1d_update",
+    "causal_conv1d_update_tokens",
     "gather_intermediate_conv_window",
     "gather_intermediate_ssm_state",
 )
@@ -59,6 +60,9 @@ _SIGS = {
                                  P, P, P, I64, I64, I32, I64, I32, I32, I32, I32, P],
     "causal_conv1d_update": [P, I64, P, I64, I64, I64, I64, P, I64, I64, P, P, P, P, I64,
                              I32, I32, I32, I32, I32, I32, P],
+    "causal_conv1d_update_tokens": [P, I64, I64, I64, I32, P, I64, I32, I64, I64, I64, P, I64,
+                                    I64, P, P, P, P, I64, I64, I64, I32, I32, I32, I32, I32,
+                                    I32, P],
     "gather_intermediate_conv_window": [P, I64, I32, I64, I64, P, P, I32, P, I64, I32, I32, P],
     "gather_intermediate_ssm_state": [P, I64, I64, I64, P, P, I32, P, I64, I32, P],
 }

@@ -364,6 +364,217 @@ __global__ __launch_bounds__(256) void update_kernel(const UpdateParams p) {
   }
 }
 
+// ---------------------------------------------------------------- multi-token update
+
+struct UpdTokParams {
+  const void* x;
+  void* out;
+  void* states;
+  const void* w;
+  const void* bias;  // or the weights as a stand-in (value unused)
+  const int32_t* idx;
+  const int32_t* seqlens;
+  int64_t x_sb, x_sc, x_st, out_sb, out_sc, out_st;
+  int64_t ss_slot, ss_c, ss_k, w_sc, w_sk;
+  int32_t batch, dim, seqlen, L;
+  int32_t silu, pad_slot_id, has_bias, has_idx, ring, threads;
+};
+
+// Non-negative p mod L for any p (L >= 1).
+__device__ __forceinline__ int64_t pmod(int64_t p, int64_t L) {
+  const int64_t r = p % L;
+  return r < 0 ? r + L : r;
+}
+
+// One thread per (row, channel).  win[LMAX - l] holds the input at lag l
+// (l = 1..LMAX) before the current token: loaded straight from the state
+// column that holds it (shift state: column L - l; ring state: the column
+// of position s - l), then shifted by one per token.  Taps are win slots
+// and state columns are addresses, so no register array is indexed at run
+// time.  The weights, the bias and the first tokens are loaded before the
+// state index, so only index -> state is a dependent step.  A thread reads
+// each x[i] before it writes out[i], so out may be x.
+template <typename D, int W, int LMAX>
+__global__ __launch_bounds__(256) void update_tokens_kernel(const UpdTokParams p) {
+  using S = typename D::storage;
+  static_assert(W - 1 <= LMAX, "the window holds every tap");
+  constexpr int kChunk = 8;  // tokens loaded together
+  asm volatile("" ::"s"(p.x), "s"(p.out), "s"(p.states), "s"(p.w), "s"(p.bias), "s"(p.idx),
+               "s"(p.seqlens), "s"(p.x_sb), "s"(p.x_st), "s"(p.ss_slot), "s"(p.ss_c),
+               "s"(p.ss_k));
+  const S* x = static_cast<const S*>(p.x);
+  S* out = static_cast<S*>(p.out);
+  S* st = static_cast<S*>(p.states);
+  const S* __restrict__ wt = static_cast<const S*>(p.w);
+  const S* __restrict__ bs = static_cast<const S*>(p.bias);
+
+  const uint32_t gid = blockIdx.x * (uint32_t)p.threads + threadIdx.x;
+  uint32_t b = gid / (uint32_t)p.dim;
+  const bool live = b < (uint32_t)p.batch;
+  int c = (int)(gid - b * (uint32_t)p.dim);
+  if (!live) {
+    b = p.batch - 1;
+    c = 0;
+  }
+  // Independent of the state: weights, bias, the first chunk of tokens.
+  S wr[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) wr[k] = wt[(int64_t)c * p.w_sc + (int64_t)k * p.w_sk];
+  const S br = bs[p.has_bias ? c : 0];
+  const S* xrow = x + (int64_t)b * p.x_sb + (int64_t)c * p.x_sc;
+  S* orow = out + (int64_t)b * p.out_sb + (int64_t)c * p.out_sc;
+  S xc[kChunk];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u) xc[u] = xrow[(int64_t)(u < p.seqlen ? u : p.seqlen - 1) * p.x_st];
+
+  // State index and ring position, then the state columns.
+  int32_t slot_in = (int32_t)b;
+  if (p.has_idx) slot_in = p.idx[b];
+  int32_t s0 = p.L;  // shift state: its columns are positions 0 .. L-1
+  if (p.ring) s0 = p.seqlens[b];
+  const bool pad = slot_in == p.pad_slot_id;
+  S* srow = st + (int64_t)(pad ? 0 : slot_in) * p.ss_slot + (int64_t)c * p.ss_c;
+  const int L = p.L;
+  // Ring column of position s0 - l, l = 1..L: (r - l) mod L, r = s0 mod L.
+  const int r0 = (p.ring && L > 0) ? (int)((uint32_t)s0 % (uint32_t)L) : 0;
+  S win[LMAX];
+#pragma unroll
+  for (int j = 0; j < LMAX; ++j) {
+    const int l = LMAX - j;  // lag of this slot; slots with l > L are never read
+    int col = p.ring ? r0 - l : L - l;
+    if (col < 0) col += L;
+    win[j] = srow[(int64_t)(l <= L && col >= 0 ? col : 0) * p.ss_k];
+  }
+  float wk[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) wk[k] = to_float<D>(wr[k]);
+  const float bias = p.has_bias ? to_float<D>(br) : 0.f;
+
+  for (int i0 = 0; i0 < p.seqlen; i0 += kChunk) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int i = i0 + u < p.seqlen ? i0 + u : p.seqlen - 1;  // clamped: a valid row
+        xc[u] = xrow[(int64_t)i * p.x_st];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int i = i0 + u;
+      if (i >= p.seqlen) break;
+      const S xi = xc[u];
+      float acc = bias;
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        const int l = W - 1 - k;
+        float v = to_float<D>(l == 0 ? xi : win[LMAX - (l > 0 ? l : 1)]);
+        if (p.ring && s0 + i - l < 0) v = 0.f;  // before position 0
+        acc = __builtin_fmaf(wk[k], v, acc);
+      }
+      const float y = p.silu ? silu(acc) : acc;
+      if (live && !pad) {
+        S o;
+        if constexpr (sizeof(S) == 2) o = __builtin_bit_cast(uint16_t, (__bf16)y);
+        else o = y;
+        orow[(int64_t)i * p.out_st] = o;
+      }
+#pragma unroll
+      for (int j = 0; j + 1 < LMAX; ++j) win[j] = win[j + 1];
+      win[LMAX - 1] = xi;
+    }
+  }
+  if (!live || pad) return;
+  // The last L inputs back into the state: win[LMAX - l] is the input at
+  // position s0 + seqlen - l, ring column (r1 - l) mod L.
+  const int r1 = (p.ring && L > 0) ? (int)((uint32_t)(s0 + p.seqlen) % (uint32_t)L) : 0;
+#pragma unroll
+  for (int l = 1; l <= LMAX; ++l) {
+    if (l > L) break;
+    int col = p.ring ? r1 - l : L - l;
+    if (col < 0) col += L;
+    srow[(int64_t)col * p.ss_k] = win[LMAX - l];
+  }
+}
+
+template <typename D, int LMAX>
+static void launch_upd_tok(int W, const UpdTokParams& p, uint32_t g, uint32_t th, hipStream_t s) {
+  switch (W) {
+    case 1: hipLaunchKernelGGL((update_tokens_kernel<D, 1, LMAX>), dim3(g), dim3(th), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((update_tokens_kernel<D, 2, LMAX>), dim3(g), dim3(th), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((update_tokens_kernel<D, 3, LMAX>), dim3(g), dim3(th), 0, s, p); break;
+    default: hipLaunchKernelGGL((update_tokens_kernel<D, 4, LMAX>), dim3(g), dim3(th), 0, s, p); break;
+  }
+}
+
+// Shared by causal_conv1d_update_tokens and the ring form of
+// causal_conv1d_update.
+static int update_tokens_launch(
+    const char* fn, const void* x, int64_t x_sb, int64_t x_sc, int64_t x_st, int32_t seqlen,
+    void* conv_states, int64_t num_slots, int32_t state_len, int64_t ss_slot, int64_t ss_c,
+    int64_t ss_k, const void* weight, int64_t w_sc, int64_t w_sk, const void* bias,
+    const int32_t* cache_seqlens, const int32_t* conv_state_indices, void* out, int64_t out_sb,
+    int64_t out_sc, int64_t out_st, int32_t batch, int32_t dim, int32_t W, int32_t dtype,
+    int32_t activation, int32_t pad_slot_id, hipStream_t stream) {
+  if (batch < 0 || dim < 0 || seqlen < 0)
+    return fail(SCONV_ERR_INVALID, "%s: batch, dim and seqlen must be >= 0", fn);
+  if (W < 1 || W > 4) return fail(SCONV_ERR_INVALID, "%s: W=%d outside [1, 4]", fn, W);
+  if (!valid_dtype(dtype)) return fail(SCONV_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (!valid_act(activation))
+    return fail(SCONV_ERR_INVALID, "%s: unknown activation %d", fn, activation);
+  if (state_len < W - 1 || state_len < 0)
+    return fail(SCONV_ERR_INVALID, "%s: state_len=%d shorter than W-1", fn, state_len);
+  if (cache_seqlens && state_len < 1)
+    return fail(SCONV_ERR_INVALID, "%s: a ring state needs state_len >= 1", fn);
+  if (state_len > 8)
+    return fail(SCONV_ERR_UNSUPPORTED, "%s: state_len=%d above 8", fn, state_len);
+  if (batch == 0 || dim == 0 || seqlen == 0) return SCONV_OK;
+  if (!x || !weight || !out || (state_len > 0 && !conv_states))
+    return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
+  if (state_len > 0 && !conv_state_indices && num_slots < batch)
+    return fail(SCONV_ERR_INVALID, "%s: state pool has fewer slots than rows", fn);
+  if (w_sc < 1 || w_sk < 1 || x_sb < 0 || x_sc < 0 || x_st < 0 || out_sb < 0 || out_sc < 0 ||
+      out_st < 0 || (state_len > 0 && (num_slots < 1 || ss_slot < 1 || ss_c < 1 || ss_k < 1)))
+    return fail(SCONV_ERR_INVALID, "%s: strides too small", fn);
+  const bool inplace = out == x;
+  if (inplace && (out_sb != x_sb || out_sc != x_sc || out_st != x_st))
+    return fail(SCONV_ERR_INVALID, "%s: in-place call needs identical strides", fn);
+  const int64_t es = elem_size(dtype);
+  if (!inplace) {
+    const int64_t xb = ((int64_t)(batch - 1) * x_sb + (int64_t)(dim - 1) * x_sc +
+                        (int64_t)(seqlen - 1) * x_st + 1) * es;
+    const int64_t ob = ((int64_t)(batch - 1) * out_sb + (int64_t)(dim - 1) * out_sc +
+                        (int64_t)(seqlen - 1) * out_st + 1) * es;
+    if (overlap(x, xb, out, ob)) return fail(SCONV_ERR_INVALID, "%s: out partially overlaps x", fn);
+  }
+  const int64_t threads_total = (int64_t)batch * dim;
+  if (threads_total + 256 > INT32_MAX)
+    return fail(SCONV_ERR_UNSUPPORTED, "%s: batch * dim too large", fn);
+  UpdTokParams p = {};
+  p.x = x; p.out = out; p.states = conv_states; p.w = weight;
+  p.bias = bias ? bias : weight; p.idx = conv_state_indices; p.seqlens = cache_seqlens;
+  p.x_sb = x_sb; p.x_sc = x_sc; p.x_st = x_st;
+  p.out_sb = out_sb; p.out_sc = out_sc; p.out_st = out_st;
+  p.ss_slot = ss_slot; p.ss_c = ss_c; p.ss_k = ss_k; p.w_sc = w_sc; p.w_sk = w_sk;
+  p.batch = batch; p.dim = dim; p.seqlen = seqlen; p.L = state_len;
+  p.silu = activation == SCONV_ACT_SILU; p.pad_slot_id = pad_slot_id;
+  p.has_bias = bias != nullptr; p.has_idx = conv_state_indices != nullptr;
+  p.ring = cache_seqlens != nullptr;
+  if (state_len == 0) {  // W == 1: no state to read or write
+    p.states = const_cast<void*>(weight); p.ss_slot = 0; p.ss_c = 0; p.ss_k = 0;
+  }
+  const uint32_t th = threads_total >= 256 * 512 ? 256 : 64;
+  p.threads = (int32_t)th;
+  const int64_t grid = cdiv(threads_total, th);
+  if (dtype == SCONV_BF16) {
+    if (state_len <= 4) launch_upd_tok<Bf16, 4>(W, p, (uint32_t)grid, th, stream);
+    else launch_upd_tok<Bf16, 8>(W, p, (uint32_t)grid, th, stream);
+  } else {
+    if (state_len <= 4) launch_upd_tok<F32, 4>(W, p, (uint32_t)grid, th, stream);
+    else launch_upd_tok<F32, 8>(W, p, (uint32_t)grid, th, stream);
+  }
+  return check_launch(fn);
+}
+
 // ---------------------------------------------------------------- dispatch
 
 template <typename D, int VEC>
@@ -465,8 +676,12 @@ extern "C" int causal_conv1d_update(const void* x, int64_t x_stride_b, void* con
   if (!valid_dtype(dtype)) return fail(SCONV_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
   if (!valid_act(activation))
     return fail(SCONV_ERR_INVALID, "%s: unknown activation %d", fn, activation);
-  if (cache_seqlens)
-    return fail(SCONV_ERR_UNSUPPORTED, "%s: cache_seqlens (circular states) not supported", fn);
+  if (cache_seqlens && W > 1)  // ring state of W-1 columns, one token (W = 1 has no state)
+    return update_tokens_launch(fn, x, x_stride_b, 1, 0, 1, conv_states, num_slots, W - 1,
+                                st_stride_slot, st_stride_c, st_stride_k, weight, w_stride_c,
+                                w_stride_k, bias, cache_seqlens, conv_state_indices, out,
+                                out_stride_b, 1, 0, batch, dim, W, dtype, activation,
+                                pad_slot_id, stream);
   if (batch == 0 || dim == 0) return SCONV_OK;
   if (!x || !weight || !out || (W > 1 && !conv_states))
     return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
@@ -515,4 +730,22 @@ extern "C" int causal_conv1d_update(const void* x, int64_t x_stride_b, void* con
     else launch_update<F32, 1>(W, p, (uint32_t)grid, th, stream);
   }
   return check_launch(fn);
+}
+
+extern "C" int causal_conv1d_update_tokens(
+    const void* x, int64_t x_stride_b, int64_t x_stride_c, int64_t x_stride_t, int32_t seqlen,
+    void* conv_states, int64_t num_slots, int32_t state_len, int64_t st_stride_slot,
+    int64_t st_stride_c, int64_t st_stride_k, const void* weight, int64_t w_stride_c,
+    int64_t w_stride_k, const void* bias, const int32_t* cache_seqlens,
+    const int32_t* conv_state_indices, void* out, int64_t out_stride_b, int64_t out_stride_c,
+    int64_t out_stride_t, int32_t batch, int32_t dim, int32_t W, int32_t dtype,
+    int32_t activation, int32_t pad_slot_id, hipStream_t stream) {
+  using namespace sconv;
+  clear_error();
+  return update_tokens_launch("causal_conv1d_update_tokens", x, x_stride_b, x_stride_c,
+                              x_stride_t, seqlen, conv_states, num_slots, state_len,
+                              st_stride_slot, st_stride_c, st_stride_k, weight, w_stride_c,
+                              w_stride_k, bias, cache_seqlens, conv_state_indices, out,
+                              out_stride_b, out_stride_c, out_stride_t, batch, dim, W, dtype,
+                              activation, pad_slot_id, stream);
 }

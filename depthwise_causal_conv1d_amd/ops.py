@@ -304,6 +304,9 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
         _vec(bias, x.dtype, "bias", dim)
     if conv_state_indices is not None:
         _vec(conv_state_indices, torch.int32, "conv_state_indices", batch)
+    if cache_seqlens is not None:
+        _dev(cache_seqlens)
+        _vec(cache_seqlens, torch.int32, "cache_seqlens", batch)
     rc = _lib.load().causal_conv1d_update(
         _ptr(x), x.stride(0), _ptr(conv_state), conv_state.shape[0], conv_state.stride(0),
         conv_state.stride(1), conv_state.stride(2), _ptr(weight), weight.stride(0),
@@ -311,6 +314,47 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
         out.stride(0), batch, dim, W, dt, _lib.ACT_SILU if silu_activation else _lib.ACT_NONE,
         int(pad_slot_id), _stream(x))
     _lib.check(rc, "causal_conv1d_update")
+    return out
+
+
+def causal_conv1d_update_tokens(x: torch.Tensor, conv_state: torch.Tensor, weight: torch.Tensor,
+                                bias: Optional[torch.Tensor], silu_activation: bool,
+                                cache_seqlens: Optional[torch.Tensor] = None,
+                                conv_state_indices: Optional[torch.Tensor] = None,
+                                pad_slot_id: int = -1, out: Optional[torch.Tensor] = None
+                                ) -> torch.Tensor:
+    """seqlen decode tokens per row: x [batch, dim, seqlen] (any strides);
+    conv_state [num_slots, dim, state_len] (W-1 <= state_len <= 8) updated in
+    place, a ring indexed by position when ``cache_seqlens`` (int32 [batch])
+    is given.  With ``out`` None the result overwrites x."""
+    if out is None:
+        out = x
+    if x.dim() != 3 or weight.dim() != 2 or conv_state.dim() != 3 or out.shape != x.shape:
+        raise ValueError("x and out [batch, dim, seqlen], weight [dim, W], "
+                         "conv_state [slots, dim, state_len]")
+    batch, dim, seqlen = x.shape
+    W = weight.shape[1]
+    _dev(x, conv_state, weight, bias, conv_state_indices, cache_seqlens, out)
+    dt = _dtype(x)
+    for t in (weight, conv_state, out) + ((bias,) if bias is not None else ()):
+        if t.dtype != x.dtype:
+            raise TypeError("x, weight, bias, conv_state and out must share one element type")
+    if weight.shape[0] != dim or conv_state.shape[1] != dim:
+        raise ValueError("weight / conv_state shapes do not match x")
+    if bias is not None:
+        _vec(bias, x.dtype, "bias", dim)
+    if conv_state_indices is not None:
+        _vec(conv_state_indices, torch.int32, "conv_state_indices", batch)
+    if cache_seqlens is not None:
+        _vec(cache_seqlens, torch.int32, "cache_seqlens", batch)
+    rc = _lib.load().causal_conv1d_update_tokens(
+        _ptr(x), x.stride(0), x.stride(1), x.stride(2), seqlen, _ptr(conv_state),
+        conv_state.shape[0], conv_state.shape[2], conv_state.stride(0), conv_state.stride(1),
+        conv_state.stride(2), _ptr(weight), weight.stride(0), weight.stride(1), _ptr(bias),
+        _ptr(cache_seqlens), _ptr(conv_state_indices), _ptr(out), out.stride(0), out.stride(1),
+        out.stride(2), batch, dim, W, dt, _lib.ACT_SILU if silu_activation else _lib.ACT_NONE,
+        int(pad_slot_id), _stream(x))
+    _lib.check(rc, "causal_conv1d_update_tokens")
     return out
 
 

@@ -275,8 +275,10 @@ int causal_conv1d_varlen_fwd(const void* x, int64_t x_stride_c, int64_t x_stride
  *
  *   x        [batch, dim] row stride x_stride_b, channels contiguous
  *   conv_states as in causal_conv1d_varlen_fwd (read and written)
- *   cache_seqlens: must be NULL (circular-buffer states are not part of
- *            this build; non-NULL returns SCONV_ERR_UNSUPPORTED)
+ *   cache_seqlens: NULL (shift state, below) or int32 [batch]: the state's
+ *            W-1 columns are then a ring, exactly as in
+ *            causal_conv1d_update_tokens with seqlen 1 and state_len W-1
+ *            (ignored when W == 1, which keeps no state)
  *   conv_state_indices int32 [batch] (NULL: b); pad_slot_id skips a row
  *   out      [batch, dim] row stride out_stride_b; may be x itself
  *
@@ -295,6 +297,52 @@ int causal_conv1d_update(const void* x, int64_t x_stride_b, void* conv_states,
                          void* out, int64_t out_stride_b, int32_t batch, int32_t dim,
                          int32_t W, int32_t dtype, int32_t activation,
                          int32_t pad_slot_id, hipStream_t stream);
+
+/*
+ * causal_conv1d_update_tokens -- seqlen new tokens per row against the state
+ * pool, with a shift or a ring state.
+ *
+ * Source: sglang page "Implementation:Sgl project Sglang Mamba Ops",
+ * causal_conv1d_update (Signature, I/O Contract), which lists cache_seqlens
+ * without semantics; the ring reading below is this library's, chosen to
+ * match the absolute-position taps of sconv_fused_insert_conv.
+ *
+ *   x        [batch, dim, seqlen] strides (x_stride_b, x_stride_c, x_stride_t)
+ *   conv_states [num_slots, dim, state_len] strides (st_stride_slot,
+ *            st_stride_c, st_stride_k); W-1 <= state_len <= 8 (read and written)
+ *   cache_seqlens NULL, or int32 [batch] >= 0: position of x[b, :, 0]
+ *   conv_state_indices int32 [batch] (NULL: b); pad_slot_id skips a row
+ *   out      [batch, dim, seqlen] strides (out_stride_*); may be x itself
+ *
+ * Shift state (cache_seqlens NULL): the state holds the last state_len
+ * inputs, oldest first.  Token i convolves the W entries ending at it in
+ * state ++ x[b, c, :]; afterwards the state holds the last state_len
+ * entries of state ++ x[b, c, :].
+ * Ring state: the input at position p lives in column p % state_len.  Token
+ * i at position q = cache_seqlens[b] + i reads lag l from x if q - l >=
+ * cache_seqlens[b], from the ring if 0 <= q - l < cache_seqlens[b], and
+ * zero if q - l < 0; afterwards column (cache_seqlens[b] + i) % state_len
+ * holds x[b, c, i].  cache_seqlens is read only.
+ * In both: out[b, c, i] = act(bias[c] + sum_k weight[c, k] * tap_k).
+ *
+ * Device-data contract: state slots of non-PAD rows are distinct and in
+ * [0, num_slots).
+ *
+ * Host errors (SCONV_ERR_INVALID): batch, dim or seqlen < 0, W outside
+ * [1, 4], state_len < W-1 (or < 1 with a ring), NULL required pointer,
+ * unknown dtype or activation, partial overlap of out and x.
+ * SCONV_ERR_UNSUPPORTED: state_len above 8.
+ */
+int causal_conv1d_update_tokens(const void* x, int64_t x_stride_b, int64_t x_stride_c,
+                                int64_t x_stride_t, int32_t seqlen, void* conv_states,
+                                int64_t num_slots, int32_t state_len, int64_t st_stride_slot,
+                                int64_t st_stride_c, int64_t st_stride_k, const void* weight,
+                                int64_t w_stride_c, int64_t w_stride_k, const void* bias,
+                                const int32_t* cache_seqlens, const int32_t* conv_state_indices,
+                                void* out, int64_t out_stride_b, int64_t out_stride_c,
+                                int64_t out_stride_t, int32_t batch, int32_t dim, int32_t W,
+                                int32_t dtype, int32_t activation, int32_t pad_slot_id,
+                                hipStream_t stream);
 
 /*
  * gather_intermediate_conv_window -- conditional gather of the length-d_conv

@@ -98,8 +98,17 @@ def test_ssm_ops_reject_bad_scalars(lib):
     u = lib.causal_conv1d_update
     one = ctypes.c_int32(1)
     assert u(NULL, 8, NULL, 1, 24, 3, 1, NULL, 4, 1, NULL, ctypes.addressof(one), NULL, NULL, 8,
-             1, 8, 4, 1, 1, -1, NULL) == 2          # cache_seqlens not supported
-    assert b"cache_seqlens" in lib.sconv_last_error()
+             1, 8, 4, 1, 1, -1, NULL) == 1          # ring form: NULL x is still rejected
+    t = lib.causal_conv1d_update_tokens
+    args = lambda sl, L, W=4, ring=None: (NULL, 64, 1, 8, sl, NULL, 4, L, 24, L, 1, NULL, W, 1,
+                                          NULL, ring, NULL, NULL, 64, 1, 8, 2, 8, W, 1, 1, -1,
+                                          NULL)
+    assert t(*args(3, 2)) == 1                          # state_len < W-1
+    assert b"shorter than W-1" in lib.sconv_last_error()
+    assert t(*args(3, 9)) == 2                          # state_len above 8
+    assert t(*args(3, 0, W=1, ring=ctypes.addressof(one))) == 1   # ring needs a column
+    assert t(*args(0, 3)) == 0                          # seqlen 0: no-op
+    assert t(*args(3, 3)) == 1                          # NULL pointers
     assert u(NULL, 8, NULL, 1, 24, 3, 1, NULL, 4, 1, NULL, NULL, NULL, NULL, 8, 1, 8, 9, 1, 1,
              -1, NULL) == 1
     g = lib.gather_intermediate_conv_window

@@ -666,3 +666,83 @@ def test_ssm_state_gather_graph_replay_with_device_count():
         torch.cuda.synchronize()
         out_r = oracle.gather_ssm_state(to_np(states), to_np(idx), n, to_np(out0))
         assert_bits_equal(to_np(out), out_r, f"replay n={n}")
+
+
+# ------------------------------------------------------------------ multi-token / ring update
+
+UPD_TOKENS = [
+    # name, dtype, W, state_len, seqlen, ring, layout, in_place, bias, indices
+    ("bf16-w4-shift-1", torch.bfloat16, 4, 3, 1, False, "bdt", True, True, True),
+    ("bf16-w4-ring-1", torch.bfloat16, 4, 3, 1, True, "bdt", False, True, True),
+    ("bf16-w4-shift-4", torch.bfloat16, 4, 3, 4, False, "btd", True, True, True),
+    ("bf16-w4-ring-7-L5", torch.bfloat16, 4, 5, 7, True, "btd", False, False, True),
+    ("f32-w3-ring-4-L8", torch.float32, 3, 8, 4, True, "bdt", True, True, False),
+    ("f32-w2-shift-7-L6", torch.float32, 2, 6, 7, False, "bdt", False, True, True),
+    ("bf16-w1-shift-3", torch.bfloat16, 1, 0, 3, False, "btd", False, True, True),
+    ("f32-w4-ring-9-L4", torch.float32, 4, 4, 9, True, "btd", True, False, True),
+]
+
+
+@pytest.mark.parametrize("spec", UPD_TOKENS, ids=[s[0] for s in UPD_TOKENS])
+def test_update_tokens_sweep(spec):
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    name, dt, W, L, T, ring, layout, in_place, has_bias, has_idx = spec
+    g = torch.Generator().manual_seed(zlib.crc32(name.encode()) % 1000)
+    batch, dim, slots = 7, 40, 12
+    xs = torch.randn(batch, dim, T, generator=g).to(dt)
+    if layout == "btd":  # tokens outer, channels contiguous
+        x = xs.permute(0, 2, 1).contiguous().permute(0, 2, 1)
+    else:
+        x = xs.contiguous()
+    w = (torch.randn(dim, W, generator=g) * 0.5).to(dt)
+    bias = (torch.randn(dim, generator=g) * 0.1).to(dt) if has_bias else None
+    st = torch.full((slots, dim, max(L, 1)), float("nan")).to(dt)[:, :, :L]
+    idx = torch.randperm(slots, generator=g)[:batch].to(torch.int32) if has_idx else None
+    if idx is not None:
+        idx[3] = -1  # PAD row
+    live_slots = idx[idx >= 0].long() if idx is not None else torch.arange(batch)
+    st[live_slots] = torch.randn(live_slots.numel(), dim, L, generator=g).to(dt)
+    seqlens = torch.randint(0, 20, (batch,), generator=g).to(torch.int32) if ring else None
+    if ring:
+        seqlens[0] = 0
+        seqlens[1] = 1
+        seqlens[2] = 2
+    say(f"update_tokens {name}: batch {batch} dim {dim} W {W} state_len {L} seqlen {T}")
+    out0 = torch.full_like(xs, SENTINEL)
+    out_r, st_r = oracle.causal_conv1d_update_tokens(
+        to_np(xs), to_np(st), to_np(w), None if bias is None else to_np(bias), "silu",
+        None if seqlens is None else to_np(seqlens), None if idx is None else to_np(idx), -1,
+        out_init=to_np(xs if in_place else out0))
+    xg = x.to(DEV) if layout == "bdt" else x.to(DEV).permute(0, 2, 1).contiguous().permute(0, 2, 1)
+    stg = st.to(DEV)
+    outg = None if in_place else out0.to(DEV).clone()
+    res = lib.causal_conv1d_update_tokens(
+        xg, stg, w.to(DEV), None if bias is None else bias.to(DEV), True,
+        None if seqlens is None else seqlens.to(DEV), None if idx is None else idx.to(DEV), -1,
+        out=outg)
+    live = np.ones(batch, bool) if idx is None else to_np(idx) >= 0
+    got = to_np(res)
+    assert_close(got[live], out_r[live], dtype_name(dt), f"{name} out")
+    assert_bits_equal(got[~live], out_r[~live], f"{name} PAD rows untouched")
+    assert_bits_equal(to_np(stg), st_r, f"{name} state pool")
+
+
+def test_update_ring_form_equals_tokens_entry():
+    """causal_conv1d_update with cache_seqlens is the one-token ring update."""
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    g = torch.Generator().manual_seed(17)
+    batch, dim, W = 9, 64, 4
+    x = torch.randn(batch, dim, generator=g).to(torch.bfloat16)
+    w = (torch.randn(dim, W, generator=g) * 0.5).to(torch.bfloat16)
+    bias = (torch.randn(dim, generator=g) * 0.1).to(torch.bfloat16)
+    st = torch.randn(batch, dim, W - 1, generator=g).to(torch.bfloat16)
+    seqlens = torch.randint(0, 9, (batch,), generator=g).to(torch.int32)
+    out_r, st_r = oracle.causal_conv1d_update_tokens(to_np(x)[:, :, None], to_np(st), to_np(w),
+                                                     to_np(bias), "silu", to_np(seqlens), None, -1)
+    stg = st.to(DEV)
+    out = lib.causal_conv1d_update(x.to(DEV), stg, w.to(DEV), bias.to(DEV), True,
+                                   seqlens.to(DEV), None, -1, out=torch.empty_like(x, device=DEV))
+    assert_close(to_np(out), out_r[:, :, 0], "bf16", "ring update out")
+    assert_bits_equal(to_np(stg), st_r, "ring update state")
