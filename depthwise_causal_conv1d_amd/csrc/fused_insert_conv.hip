@@ -59,6 +59,7 @@ struct FusedParams {
   uint32_t n_magic, n_s1, n_s2;
   int32_t num_reqs;         // with qsl
   int32_t nt_x;             // host choice: streaming input loads (one wave generation)
+  int32_t bt_pref;          // block-table entries of row t read ahead (kQslGuess; 0: off)
   void* cache;
   const int64_t* positions;
   const int32_t* bt;
@@ -132,11 +133,23 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #ifndef SCONV_FUSED_ENOUGH_WAVES
 #define SCONV_FUSED_ENOUGH_WAVES 4096
 #endif
+#ifndef SCONV_FUSED_BT_ROW
+#define SCONV_FUSED_BT_ROW 1  // one-row tiles of decode-shaped launches guess request t
+#endif
 
 // Where a row's request and request start come from (template QM).
 constexpr int kQslOff = 0;   // the per-row seq_idx / query_start buffers
 constexpr int kQslRegs = 1;  // the offsets qsl, read whole into registers
 constexpr int kQslSearch = 2;  // the offsets qsl, searched in device memory
+// For one-row tiles of launches with no more rows than requests (decode,
+// where row t is usually request t): the guess r = t is checked against
+// offsets t and t+1, read with the row's other metadata, and block-table
+// row t is read at the same time, so a row that is request t has its
+// request and its history blocks one dependent round trip earlier.  A row
+// that is not searches device memory and looks its blocks up there.
+constexpr int kQslGuess = 3;
+// Entries of row t read ahead: four 256-byte loads per wave.
+constexpr int kBtRowMax = 256;
 #ifndef SCONV_FUSED_QSL_REG_MAX
 #define SCONV_FUSED_QSL_REG_MAX 512
 #endif
@@ -147,7 +160,7 @@ static_assert(kQslRegMax <= 512, "8 offsets per lane");
 // NTX: input rows loaded as streaming (non-temporal) reads.  MS: several
 // streams, each wave finding its own (one-stream launches read entry 0).
 template <typename D, int VEC, int W, int BT, int QM, bool NTX, bool MS>
-__global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParams p) {
+__global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kernel(const FusedParams p) {
   using S = typename D::storage;
   using P = Pack<D, VEC>;
   S* __restrict__ cache = static_cast<S*>(p.cache);
@@ -166,6 +179,9 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
   if constexpr (MS)
     asm volatile("" ::"s"(p.num_streams), "s"(p.st[1].slab0), "s"(p.st[2].slab0),
                  "s"(p.st[3].slab0));
+  constexpr bool kGuess = QM == kQslGuess;
+  static_assert(!kGuess || BT == 1, "request guess for one-row tiles only");
+  if constexpr (kGuess) asm volatile("" ::"s"(p.bt), "s"(p.bt_rs), "s"(p.bt_pref));
   const int lane = threadIdx.x & 63;
   // The launch geometry comes in the parameters (loaded with them in one
   // batch) rather than from the implicit arguments, which would cost a
@@ -195,15 +211,15 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 
   // Row metadata of the whole tile in one gather: lane L loads field L % F
   // of row t0 + L / F (position, slot low and high words, and without QSL
-  // the request index and request start), then every value is broadcast to
-  // scalar registers.  One instruction cannot be split or sunk below the
+  // the request index and request start, or with the request guess the
+  // offsets t and t+1), then every value is broadcast to scalar registers.  One instruction cannot be split or sunk below the
   // PAD tests, so the whole tile's metadata costs one round trip.
   // Every load below is unconditional, from an address clamped into the
   // buffers (rows past T, lanes past C): a conditional load would join its
   // value with a default and force an immediate wait for it.
   const int64_t t_last = p.T - 1;
   constexpr int QSL = QM != kQslOff;
-  constexpr int F = QSL ? 3 : 5;
+  constexpr int F = QSL && !kGuess ? 3 : 5;
   constexpr int NM = F * BT;
   constexpr int NI = (NM + 63) / 64;
   int32_t mv[NI];
@@ -213,9 +229,16 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     const int r = L / F;
     const int f = L - r * F;
     const int64_t t = t0 + r < t_last ? t0 + r : t_last;
-    const int32_t* src =
-        f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
-              : (f == 3 ? seq_idx : qstart) + t;
+    const int32_t* src;
+    if constexpr (kGuess) {
+      // offsets t and t+1 (t clamped below num_reqs: both exist)
+      const int64_t tq = t < (int64_t)p.num_reqs - 1 ? t : p.num_reqs - 1;
+      src = f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
+                  : p.qsl + tq + (f == 4);
+    } else {
+      src = f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
+                  : (f == 3 ? seq_idx : qstart) + t;
+    }
     mv[g] = *src;
   }
   // Up to 512 request offsets: ov[j] of lane L is offset 64*j + L, so each
@@ -227,6 +250,18 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     for (int j = 0; j < 8; ++j) {
       const int r = j * 64 + lane;
       ov[j] = p.qsl[r < p.num_reqs ? r : p.num_reqs - 1];
+    }
+  }
+  // Block-table row t (the row's guessed request, clamped into the table):
+  // entry 64*j + L in brow[j] of lane L, bt_pref entries, clamped.
+  int32_t brow[4];
+  const int32_t row_guess = (int32_t)(t0 < (int64_t)p.num_reqs - 1 ? t0 : p.num_reqs - 1);
+  if constexpr (kGuess) {
+    const int32_t* row = btab + (int64_t)row_guess * p.bt_rs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = j * 64 + lane;
+      brow[j] = row[e < p.bt_pref ? e : p.bt_pref - 1];
     }
   }
 
@@ -315,12 +350,30 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     const int32_t lo = __builtin_amdgcn_readlane(mv[(b + 1) / 64], (b + 1) % 64);
     const int32_t hi = __builtin_amdgcn_readlane(mv[(b + 2) / 64], (b + 2) % 64);
     slot[i] = (hi < 0 || !live_wave || t0 + i > t_last) ? -1 : lo;
-    if constexpr (!QSL) {
+    if constexpr (!QSL || kGuess) {
       req[i] = __builtin_amdgcn_readlane(mv[(b + 3) / 64], (b + 3) % 64);
       qs[i] = __builtin_amdgcn_readlane(mv[(b + 4) / 64], (b + 4) % 64);
     } else {
       req[i] = 0;
       qs[i] = 0;
+    }
+  }
+  if constexpr (kGuess) {
+    // req / qs hold offsets t and t+1.  Row t is request t exactly when
+    // off[t] <= t < off[t+1] (offsets are non-decreasing, so no later
+    // request starts at or before t); otherwise (empty or multi-row
+    // requests before it, rows past the last offset) a live row searches.
+    const int32_t t = (int32_t)(t0 < t_last ? t0 : t_last);
+    const int32_t lo = req[0], hi = qs[0];
+    if (t == row_guess && lo <= t && t < hi) {
+      req[0] = t;
+      qs[0] = lo;
+    } else if (slot[0] >= 0) {
+      req[0] = find_request(p.qsl, p.num_reqs, t, lane);
+      qs[0] = uniform(p.qsl[req[0]]);
+    } else {
+      req[0] = 0;
+      qs[0] = 0;
     }
   }
   if constexpr (QM == kQslRegs) {
@@ -419,7 +472,7 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 #else
   constexpr bool kLdsHalo = false;
 #endif
-  constexpr int kWavesMax = 256 / 64;
+  constexpr int kWavesMax = SCONV_FUSED_WG_THREADS / 64;
   __shared__ typename P::raw_t s_halo[kLdsHalo ? kWavesMax : 1][kHalo][64];
   const int wig = (int)(threadIdx.x >> 6);  // wave in workgroup
   bool halo_from_lds = false;
@@ -511,18 +564,40 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
     const int32_t d = (int32_t)(t - qs[i]);  // row offset inside its request
     if (slot[i] >= 0 && d < W - 1 && req[i] != hist_req && pos[i] - d > 0) {
       // first > 0, so history row 1 (position first-1) is read by this row
-      // and its block-table entry is valid.  Every lookup and load below is
+      // and its block-table entry is valid.  The history loads below are
       // unconditional (a load inside a branch would wait for its value at
       // the join): rows this request does not read, m > W-1-d or before
-      // position 0, are fetched from history row 1's address instead.
+      // position 0, are fetched from history row 1's address instead.  The
+      // block-table entries come from registers or from one uniform branch
+      // of lookups, whose values the history addresses need at once anyway.
       const int32_t first = pos[i] - d;
       int32_t hblk[kHalo], hoff[kHalo];
+      uint32_t hlb[kHalo];
 #pragma unroll
       for (int m = 1; m <= W - 1; ++m) {
         const int32_t src = first - m >= 0 ? first - m : 0;
-        const uint32_t lb = div_n((uint32_t)src, p);
-        hoff[m - 1] = src - (int32_t)lb * p.N;
-        hblk[m - 1] = btab[(int64_t)req[i] * p.bt_rs + lb];
+        hlb[m - 1] = div_n((uint32_t)src, p);
+        hoff[m - 1] = src - (int32_t)hlb[m - 1] * p.N;
+      }
+      // History row 1 has the largest block index of the W-1.
+      bool in_regs = false;
+      if constexpr (kGuess) in_regs = req[i] == row_guess && hlb[0] < (uint32_t)p.bt_pref;
+      if (in_regs) {
+#pragma unroll
+        for (int m = 1; m <= W - 1; ++m) {
+          const int32_t l = (int32_t)(hlb[m - 1] & 63), q = (int32_t)(hlb[m - 1] >> 6);
+          int32_t v = __builtin_amdgcn_readlane(brow[0], l);
+#pragma unroll
+          for (int jj = 1; jj < 4; ++jj) {
+            const int32_t vj = __builtin_amdgcn_readlane(brow[jj], l);
+            v = q == jj ? vj : v;
+          }
+          hblk[m - 1] = v;
+        }
+      } else {
+#pragma unroll
+        for (int m = 1; m <= W - 1; ++m)
+          hblk[m - 1] = btab[(int64_t)req[i] * p.bt_rs + hlb[m - 1]];
       }
 #pragma unroll
       for (int m = 2; m <= W - 1; ++m) {
@@ -598,6 +673,13 @@ __global__ __launch_bounds__(256) void fused_insert_conv_kernel(const FusedParam
 
 template <typename D, int VEC, int W, int BT, bool NTX, bool MS>
 static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
+  if constexpr (BT == 1 && W > 1) {
+    if (p.bt_pref > 0) {
+      hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslGuess, NTX, MS>),
+                         dim3(grid), dim3(threads), 0, s, p);
+      return;
+    }
+  }
   if (p.qsl && p.num_reqs <= kQslRegMax) {
     hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs, NTX, MS>), dim3(grid),
                        dim3(threads), 0, s, p);
@@ -778,6 +860,11 @@ static int fused_launch(
   p.num_slabs = (int32_t)slabs;
   const int bt = pick_bt(T, p.num_slabs);
   p.num_tiles = cdiv(T, bt);
+  // Decode-shaped launches (one-row tiles, no more rows than requests)
+  // guess that row t is request t.
+  p.bt_pref = (SCONV_FUSED_BT_ROW && qsl && bt == 1 && W > 1 && T <= num_reqs)
+                  ? (max_blocks < kBtRowMax ? max_blocks : kBtRowMax)
+                  : 0;
 
   const int64_t waves = p.num_tiles * p.num_slabs;
   if (waves > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);

@@ -147,8 +147,13 @@ int sconv_fused_insert_conv(const void* x, int64_t x_row_stride,
  * Each non-PAD row t belongs to the last request r with qsl[r] <= t (rows
  * past qsl[num_reqs] clamp to the last request), and query_start = qsl[r].
  * Up to 512 requests the offsets are read whole into registers; larger
- * batches are searched in device memory once per row tile.  The launch
- * allocates nothing and needs no LDS.
+ * batches are searched in device memory once per row tile.  A launch with
+ * no more rows than requests (decode) first checks whether row t is
+ * request t (qsl[t] <= t < qsl[t+1]) and, for the rows that are, takes
+ * their block-table entries from row t of block_table, read in advance
+ * (the first min(max_blocks, 256) entries of that row: every row
+ * [0, num_reqs) of block_table must be readable).  The launch allocates
+ * nothing.
  *
  * Errors: as sconv_fused_insert_conv, plus SCONV_ERR_INVALID for
  * num_reqs < 1 (or a NULL query_start_loc) with T > 0.

@@ -192,6 +192,62 @@ def test_folded_empty_request_runs(run_len, runs, live, lens):
     check_fused(case, f"{len(new)} requests, runs of {run_len} empty", fold=True)
 
 
+def _decode_shaped_lens(rng, R, tail):
+    """Request lengths in {0, 1, 2} whose rows, tail included, number at most
+    R: empty and two-row requests move rows off row t == request t."""
+    new = [int(v) for v in rng.choice([0, 1, 1, 2], R)]
+    while sum(new) + tail > R:
+        i = new.index(max(new))
+        new[i] -= 1
+    return new
+
+
+# name, seed, R, lens ("ones" or "mixed"), ctx max, N, W, dtype, H, ws, D, off_s, pad, tail
+DECODE_ROW = [
+    ("ones-narrow-table", 41, 200, "ones", 300, 16, 4, torch.bfloat16, 4, 32, 64, 32, 10, 0),
+    ("mixed-rows", 42, 400, "mixed", 200, 16, 4, torch.bfloat16, 4, 32, 64, 0, 20, 3),
+    ("ones-beyond-256-blocks", 43, 128, "ones", 2500, 4, 4, torch.bfloat16, 2, 64, 64, 0, 4, 0),
+    ("mixed-beyond-256-blocks", 44, 256, "mixed", 2500, 4, 4, torch.bfloat16, 2, 64, 64, 0, 6, 2),
+    ("w2-f32", 45, 96, "mixed", 100, 8, 2, torch.float32, 4, 8, 16, 8, 3, 1),
+    ("w3-scalar", 46, 150, "ones", 120, 16, 3, torch.bfloat16, 3, 6, 16, 3, 5, 0),
+    ("one-request", 47, 1, "ones", 70, 16, 4, torch.bfloat16, 2, 64, 64, 0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("spec", DECODE_ROW, ids=[s[0] for s in DECODE_ROW])
+def test_folded_decode_block_row(spec):
+    """Folded launches with no more rows than requests (one-row tiles) read
+    block-table row t along with the metadata and take a row's history
+    blocks from it when the row is request t and its blocks lie within the
+    first 256 entries; other rows look their blocks up in memory.  Cases:
+    every row its own request, empty and two-row requests shifting rows off
+    that guess, history past the first 256 blocks (block size 4), a table
+    narrower than 256 entries, W 2 and 3, fp32, the one-channel kernels and
+    PAD rows."""
+    name, seed, R, lens, cmax, N, W, dt, H, ws, D, off, pad, tail = spec
+    rng = np.random.default_rng(seed)
+    new = [1] * R if lens == "ones" else _decode_shaped_lens(rng, R, tail)
+    ctx = [int(v) for v in rng.integers(0, cmax + 1, R)]
+    assert sum(new) + tail <= R
+    case = workloads.fused_case(seed, new, ctx, H=H, D=D, ws=ws, off_s=off, block_size=N, W=W,
+                                dtype=dt, pad_count=min(pad, sum(new)), tail_pad=tail)
+    check_fused(case, f"decode-shaped {name}", fold=True)
+
+
+def test_streams_decode_block_row_shifted():
+    """The same read-ahead in a four-stream launch, rows shifted off their
+    guess by empty and two-row requests."""
+    rng = np.random.default_rng(48)
+    R = 300
+    new = _decode_shaped_lens(rng, R, 2)
+    ctx = [int(v) for v in rng.integers(0, 900, R)]
+    cases = workloads.fused_streams_case(48, new, ctx, H=8, D=128,
+                                         streams=[(0, 32), (32, 32), (64, 32), (96, 32)],
+                                         block_size=4, W=4, dtype=torch.bfloat16,
+                                         pad_count=8, tail_pad=2)
+    check_streams(cases, "decode-shaped streams, shifted rows", True)
+
+
 _STREAMS_ORACLE = {}
 
 
