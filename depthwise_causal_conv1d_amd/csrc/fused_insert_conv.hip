@@ -14,9 +14,10 @@
 //     channels; each lane owns VEC consecutive channels (16 bytes: 8 bf16 or
 //     4 fp32), so every x / out row access of a wave is one contiguous
 //     coalesced segment and every cache access is 16 bytes per lane;
-//   * the row index is wave-uniform, so positions / slots / request ids and
-//     block-table entries arrive through scalar loads (SGPRs) and every
-//     PAD / same-forward / pre-forward decision is a uniform branch;
+//   * the row index is wave-uniform: a tile's positions, slots and request
+//     data arrive in one per-lane gather and are broadcast to SGPRs, block-
+//     table entries come through scalar registers, and every PAD / same-
+//     forward / pre-forward decision is a uniform branch;
 //   * the W-1 previous input rows a tap needs stay in the lane's registers:
 //     rows inside the tile are the tile's own loads, rows before the tile
 //     (the halo, at most W-1) are loaded once per tile only when a row of

@@ -118,8 +118,14 @@ template <typename T, int N>
 __device__ __forceinline__ T pick(const T (&a)[N], int idx) {
   T r = a[0];
 #pragma unroll
-  for (int q = 1; q < N; ++q)
-    if (idx == q) r = a[q];
+  for (int q = 1; q < N; ++q) {
+    // An empty statement makes each element an opaque register value: a
+    // select between two reads of the array would otherwise be folded into
+    // one read at a computed index, which keeps the array in memory.
+    T v = a[q];
+    asm("" : "+v"(v));
+    r = idx == q ? v : r;
+  }
   return r;
 }
 

@@ -248,6 +248,31 @@ def test_streams_decode_block_row_shifted():
     check_streams(cases, "decode-shaped streams, shifted rows", True)
 
 
+# Block size 1 000 003 (prime) with 2147 table entries: max_blocks * N is
+# 2 147 006 441, just under the 2^31 the launch accepts.
+_BIG_N = 1_000_003
+_NEAR_MAX = [
+    # name, new rows per request, positions of each request's first new row
+    ("prefill-shaped", [5, 1, 3, 2], [2_147_000_000 - 5, 2146 * _BIG_N + 1, 1000 * _BIG_N + 2, 0]),
+    ("decode-shaped", [1, 1, 1, 1], [2_147_000_000 - 1, 2146 * _BIG_N + 2, 255 * _BIG_N + 1, 5]),
+]
+
+
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
+@pytest.mark.parametrize("spec", _NEAR_MAX, ids=[s[0] for s in _NEAR_MAX])
+def test_fused_positions_near_int31(spec, fold):
+    """Positions up to ~2.147e9 and block indices up to 2146 with a block size
+    that is not a power of two: the 32-bit position and slot arithmetic and
+    the division by N at the top of their range, histories that straddle a
+    block boundary, and (decode-shaped, folded) history blocks far past the
+    entries a decode launch reads ahead."""
+    name, new, ctx = spec
+    case = workloads.fused_case(61, new, ctx, H=1, D=8, ws=8, off_s=0, block_size=_BIG_N, W=4,
+                                dtype=torch.bfloat16)
+    assert case.block_table.shape[1] * _BIG_N < 2 ** 31
+    check_fused(case, f"positions near 2^31, {name}", fold=fold)
+
+
 _STREAMS_ORACLE = {}
 
 
