@@ -380,12 +380,6 @@ struct UpdTokParams {
   int32_t silu, pad_slot_id, has_bias, has_idx, ring, threads;
 };
 
-// Non-negative p mod L for any p (L >= 1).
-__device__ __forceinline__ int64_t pmod(int64_t p, int64_t L) {
-  const int64_t r = p % L;
-  return r < 0 ? r + L : r;
-}
-
 // One thread per (row, channel).  win[LMAX - l] holds the input at lag l
 // (l = 1..LMAX) before the current token: loaded straight from the state
 // column that holds it (shift state: column L - l; ring state: the column

@@ -95,6 +95,13 @@ def _fused_checks(x, weight, cache, positions, block_table, slot_mapping, off_s,
     return dt
 
 
+def _table_rows(block_table: torch.Tensor, num_reqs: int):
+    # With the request offsets the launch may read any row below num_reqs.
+    if block_table.shape[0] < num_reqs:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows, needs num_reqs="
+                         f"{num_reqs}")
+
+
 def sconv_fused_insert_conv(x: torch.Tensor, weight: torch.Tensor, cache: torch.Tensor,
                             positions: torch.Tensor, block_table: torch.Tensor,
                             seq_idx: torch.Tensor, slot_mapping: torch.Tensor,
@@ -148,6 +155,7 @@ def sconv_fused_insert_conv_qsl(x: torch.Tensor, weight: torch.Tensor, cache: to
     T = x.shape[0]
     _dev(query_start_loc)
     _vec(query_start_loc, torch.int32, "query_start_loc", num_reqs + 1)
+    _table_rows(block_table, num_reqs)
     nb, H, N, D = cache.shape
     rc = _lib.load().sconv_fused_insert_conv_qsl(
         _ptr(x), x.stride(0), _ptr(weight), weight.stride(0), weight.stride(1),
@@ -206,6 +214,7 @@ def sconv_fused_insert_conv_streams(xs: Sequence[torch.Tensor], weights: Sequenc
             raise ValueError("give query_start_loc with num_reqs, or seq_idx and query_start")
         _dev(query_start_loc)
         _vec(query_start_loc, torch.int32, "query_start_loc", num_reqs + 1)
+        _table_rows(block_table, num_reqs)
     else:
         if seq_idx is None or query_start is None:
             raise ValueError("give query_start_loc with num_reqs, or seq_idx and query_start")

@@ -234,6 +234,23 @@ def test_folded_decode_block_row(spec):
     check_fused(case, f"decode-shaped {name}", fold=True)
 
 
+def test_folded_table_needs_num_reqs_rows():
+    """The folded forms may read any block-table row below num_reqs, so the
+    binding refuses a shorter table before launching."""
+    import depthwise_causal_conv1d_amd as lib
+    case = workloads.fused_case(49, [1, 1, 1], [5, 9, 2], H=2, D=16, ws=8, block_size=16, W=4,
+                                dtype=torch.bfloat16)
+    x, w, cache = case.x.to(DEV), case.weight.to(DEV), case.cache.to(DEV)
+    pos, sm = case.positions.to(DEV), case.slot_mapping.to(DEV)
+    qsl = case.query_start_loc.to(DEV)
+    bt = case.block_table.to(DEV)
+    with pytest.raises(ValueError, match="num_reqs"):
+        lib.sconv_fused_insert_conv_qsl(x, w, cache, pos, bt[:2], qsl, 3, sm, 0, 8, 16)
+    with pytest.raises(ValueError, match="num_reqs"):
+        lib.sconv_fused_insert_conv_streams([x], [w], cache, pos, bt[:2], sm, [0], [8], 16,
+                                            query_start_loc=qsl, num_reqs=3)
+
+
 def test_streams_decode_block_row_shifted():
     """The same read-ahead in a four-stream launch, rows shifted off their
     guess by empty and two-row requests."""
