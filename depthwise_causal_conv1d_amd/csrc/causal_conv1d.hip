@@ -31,6 +31,16 @@ namespace sconv {
 #ifndef SCONV_VARLEN_NT_STORES
 #define SCONV_VARLEN_NT_STORES 1   // streaming stores of the outputs
 #endif
+#ifndef SCONV_UPDATE_TOKENS_VEC
+#define SCONV_UPDATE_TOKENS_VEC 1  // vector-lane kernel for packed multi-token updates
+#endif
+// Channels per lane of the packed update kernels.  These launches are small
+// (a decode batch): two channels per lane keep enough waves in flight to
+// use every CU, where 16-byte lanes left most of them idle (measured on
+// MI355X at 8..256 rows of 8192 channels).
+#ifndef SCONV_UPDATE_LANE_CHANNELS
+#define SCONV_UPDATE_LANE_CHANNELS 2
+#endif
 
 struct VarlenParams {
   const void* x;
@@ -265,7 +275,7 @@ __device__ __forceinline__ void loaded_here(const T& v) {
 // state shifted by one.  Loads are unconditional from valid addresses (a
 // PAD row reads slot 0 and stores nothing; a missing bias reads the weights
 // and is replaced by zero), so the only dependent step is index -> state.
-// The 16-byte-lane kernels take packed [dim, W] weights and the packed
+// The vector-lane kernels take packed [dim, W] weights and the packed
 // [slot, dim, W-1] state layout and move each as W (W-1) lane vectors: the
 // VEC channels' taps are contiguous, flat index e*W + k (e*(W-1) + m).  The
 // one-channel kernels read any strides, one element per vector.
@@ -378,6 +388,7 @@ struct UpdTokParams {
   int64_t ss_slot, ss_c, ss_k, w_sc, w_sk;
   int32_t batch, dim, seqlen, L;
   int32_t silu, pad_slot_id, has_bias, has_idx, ring, threads;
+  int32_t nvec;  // lane vectors per row (vector-lane kernel)
 };
 
 // One thread per (row, channel).  win[LMAX - l] holds the input at lag l
@@ -490,6 +501,163 @@ __global__ __launch_bounds__(256) void update_tokens_kernel(const UpdTokParams p
   }
 }
 
+// The same update with vector lanes, for the packed layout: x and out with
+// contiguous channels, weights [dim, W] and states [slot, dim, W-1] packed.
+// A lane owns VEC channels of one row.  Each token of x and out is one lane
+// vector; the lane's W-1 state columns are W-1 vectors (element e*(W-1) +
+// column of channel e) and its taps W vectors (element e*W + k).  The
+// window wl[l-1] holds the raw inputs at lag l, taken from the column of
+// each lag: a per-lane choice among W-1 columns (rows, and with them the
+// ring rotation, can change inside a wave), made with selects on values
+// already in registers.  Values stay raw bits until used, so a state
+// written back is an exact copy of the inputs it holds.
+template <typename D, int VEC, int W>
+__global__ __launch_bounds__(256) void update_tokens_vec_kernel(const UpdTokParams p) {
+  using S = typename D::storage;
+  using P = Pack<D, VEC>;
+  using E = typename P::Elems;
+  constexpr int L = W - 1;
+  static_assert(L >= 1, "the packed kernel has a state");
+  constexpr int kChunk = 4;  // tokens loaded together
+  asm volatile("" ::"s"(p.x), "s"(p.out), "s"(p.states), "s"(p.w), "s"(p.bias), "s"(p.idx),
+               "s"(p.seqlens), "s"(p.x_sb), "s"(p.x_st), "s"(p.ss_slot));
+  const S* x = static_cast<const S*>(p.x);
+  S* out = static_cast<S*>(p.out);
+  S* st = static_cast<S*>(p.states);
+  const S* __restrict__ wt = static_cast<const S*>(p.w);
+  const S* __restrict__ bs = static_cast<const S*>(p.bias);
+
+  // The host bounds batch * nvec below 2^31.
+  const uint32_t gid = blockIdx.x * (uint32_t)p.threads + threadIdx.x;
+  uint32_t b = gid / (uint32_t)p.nvec;
+  const bool live = b < (uint32_t)p.batch;
+  int c0 = (int)(gid - b * (uint32_t)p.nvec) * VEC;
+  if (!live) {
+    b = p.batch - 1;
+    c0 = 0;
+  }
+  // Independent of the state: taps, bias (or the weights as a stand-in),
+  // the first tokens.
+  P wv[W], bv;
+#pragma unroll
+  for (int k = 0; k < W; ++k) wv[k].load(wt + (int64_t)c0 * W + k * VEC);
+  bv.load(bs + (p.has_bias ? c0 : 0));
+  const S* xrow = x + (int64_t)b * p.x_sb + c0;
+  S* orow = out + (int64_t)b * p.out_sb + c0;
+  P xc[kChunk];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u)
+    xc[u].load(xrow + (int64_t)(u < p.seqlen ? u : p.seqlen - 1) * p.x_st);
+
+  // State index and ring position, then the state columns.
+  int32_t slot_in = (int32_t)b;
+  if (p.has_idx) slot_in = p.idx[b];
+  int32_t s0 = L;  // shift state: its columns are positions 0 .. L-1
+  if (p.ring) s0 = p.seqlens[b];
+  const bool pad = slot_in == p.pad_slot_id;
+  S* srow = st + (int64_t)(pad ? 0 : slot_in) * p.ss_slot + (int64_t)c0 * L;
+  P sv[L];
+#pragma unroll
+  for (int m = 0; m < L; ++m) sv[m].load(srow + m * VEC);
+
+  float wk[W][VEC], bias[VEC];
+  bv.to_float(bias);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    if (!p.has_bias) bias[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) wk[k][e] = to_float<D>(elem_at(wv, e * W + k));
+  }
+  // Lag l sits in column (r0 - l) mod L of a ring (r0 = s0 mod L), in
+  // column L - l of a shift state.
+  const int r0 = p.ring ? (int)((uint32_t)s0 % (uint32_t)L) : 0;
+  E wl[L];
+#pragma unroll
+  for (int l = 1; l <= L; ++l) {
+    int col = p.ring ? r0 - l : L - l;
+    if (col < 0) col += L;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      S v = elem_at(sv, e * L);
+#pragma unroll
+      for (int q = 1; q < L; ++q) v = col == q ? elem_at(sv, e * L + q) : v;
+      wl[l - 1].e[e] = v;
+    }
+  }
+
+  for (int i0 = 0; i0 < p.seqlen; i0 += kChunk) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int i = i0 + u < p.seqlen ? i0 + u : p.seqlen - 1;  // clamped: a valid row
+        xc[u].load(xrow + (int64_t)i * p.x_st);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int i = i0 + u;
+      if (i >= p.seqlen) break;
+      const E xe = __builtin_bit_cast(E, xc[u].raw);
+      float y[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float acc = bias[e];
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          const int l = W - 1 - k;
+          float v = to_float<D>(l == 0 ? xe.e[e] : wl[l > 0 ? l - 1 : 0].e[e]);
+          if (l > 0 && p.ring && s0 + i - l < 0) v = 0.f;  // before position 0
+          acc = __builtin_fmaf(wk[k][e], v, acc);
+        }
+        y[e] = p.silu ? silu(acc) : acc;
+      }
+      if (live && !pad) {
+        P o;
+        o.from_float(y);
+        o.store(orow + (int64_t)i * p.out_st);
+      }
+#pragma unroll
+      for (int l = L; l >= 2; --l) wl[l - 1] = wl[l - 2];
+      wl[0] = xe;
+    }
+  }
+  if (!live || pad) return;
+  // New state: column q receives the input at lag l(q) after the last
+  // token, the lag whose column is q: (r1 - q) mod L in (0, L] for a ring
+  // (r1 = (s0 + seqlen) mod L), L - q for a shift state.
+  const int r1 = p.ring ? (int)((uint32_t)(s0 + p.seqlen) % (uint32_t)L) : 0;
+  E so[L];
+#pragma unroll
+  for (int q = 0; q < L; ++q) {
+    int lq = p.ring ? r1 - q : L - q;
+    if (lq <= 0) lq += L;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      S v = wl[0].e[e];
+#pragma unroll
+      for (int l = 2; l <= L; ++l) v = lq == l ? wl[l - 1].e[e] : v;
+      const int flat = e * L + q;
+      so[flat / VEC].e[flat % VEC] = v;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < L; ++m) {
+    P pk;
+    pk.raw = __builtin_bit_cast(typename P::raw_t, so[m]);
+    pk.store(srow + m * VEC);
+  }
+}
+
+template <typename D, int VEC>
+static void launch_upd_tok_vec(int W, const UpdTokParams& p, uint32_t g, uint32_t th,
+                               hipStream_t s) {
+  switch (W) {
+    case 2: hipLaunchKernelGGL((update_tokens_vec_kernel<D, VEC, 2>), dim3(g), dim3(th), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((update_tokens_vec_kernel<D, VEC, 3>), dim3(g), dim3(th), 0, s, p); break;
+    default: hipLaunchKernelGGL((update_tokens_vec_kernel<D, VEC, 4>), dim3(g), dim3(th), 0, s, p); break;
+  }
+}
+
 template <typename D, int LMAX>
 static void launch_upd_tok(int W, const UpdTokParams& p, uint32_t g, uint32_t th, hipStream_t s) {
   switch (W) {
@@ -540,7 +708,17 @@ static int update_tokens_launch(
                         (int64_t)(seqlen - 1) * out_st + 1) * es;
     if (overlap(x, xb, out, ob)) return fail(SCONV_ERR_INVALID, "%s: out partially overlaps x", fn);
   }
-  const int64_t threads_total = (int64_t)batch * dim;
+  // Vector lanes for the packed layout (state_len = W-1, channels
+  // contiguous, every row start and row step a whole number of vectors).
+  constexpr int kLC = SCONV_UPDATE_LANE_CHANNELS;
+  const int64_t lb = kLC * es;  // bytes per lane vector
+  const bool vec = SCONV_UPDATE_TOKENS_VEC && W >= 2 && state_len == W - 1 && x_sc == 1 &&
+                   out_sc == 1 && dim % kLC == 0 && x_sb % kLC == 0 && x_st % kLC == 0 &&
+                   out_sb % kLC == 0 && out_st % kLC == 0 && aligned_to(x, lb) &&
+                   aligned_to(out, lb) && w_sc == W && w_sk == 1 && aligned_to(weight, lb) &&
+                   (!bias || aligned_to(bias, lb)) && ss_k == 1 && ss_c == state_len &&
+                   ss_slot % kLC == 0 && aligned_to(conv_states, lb);
+  const int64_t threads_total = (int64_t)batch * (vec ? dim / kLC : dim);
   if (threads_total + 256 > INT32_MAX)
     return fail(SCONV_ERR_UNSUPPORTED, "%s: batch * dim too large", fn);
   UpdTokParams p = {};
@@ -558,7 +736,13 @@ static int update_tokens_launch(
   }
   const uint32_t th = threads_total >= 256 * 512 ? 256 : 64;
   p.threads = (int32_t)th;
+  p.nvec = vec ? dim / kLC : dim;
   const int64_t grid = cdiv(threads_total, th);
+  if (vec) {
+    if (dtype == SCONV_BF16) launch_upd_tok_vec<Bf16, kLC>(W, p, (uint32_t)grid, th, stream);
+    else launch_upd_tok_vec<F32, kLC>(W, p, (uint32_t)grid, th, stream);
+    return check_launch(fn);
+  }
   if (dtype == SCONV_BF16) {
     if (state_len <= 4) launch_upd_tok<Bf16, 4>(W, p, (uint32_t)grid, th, stream);
     else launch_upd_tok<Bf16, 8>(W, p, (uint32_t)grid, th, stream);
@@ -694,14 +878,15 @@ extern "C" int causal_conv1d_update(const void* x, int64_t x_stride_b, void* con
     if (overlap(x, xb, out, ob))
       return fail(SCONV_ERR_INVALID, "%s: out partially overlaps x", fn);
   }
-  const int vec16 = (int)(16 / es);
-  // 16-byte lanes need packed weights and states, aligned rows and bias.
-  const bool vec = dim % vec16 == 0 && x_stride_b % vec16 == 0 && out_stride_b % vec16 == 0 &&
-                   aligned16(x) && aligned16(out) && w_stride_c == W && w_stride_k == 1 &&
-                   aligned16(weight) && (!bias || aligned16(bias)) &&
+  // Vector lanes need packed weights and states, aligned rows and bias.
+  constexpr int kLC = SCONV_UPDATE_LANE_CHANNELS;
+  const int64_t lb = kLC * es;  // bytes per lane vector
+  const bool vec = dim % kLC == 0 && x_stride_b % kLC == 0 && out_stride_b % kLC == 0 &&
+                   aligned_to(x, lb) && aligned_to(out, lb) && w_stride_c == W &&
+                   w_stride_k == 1 && aligned_to(weight, lb) && (!bias || aligned_to(bias, lb)) &&
                    (W == 1 || (st_stride_k == 1 && st_stride_c == W - 1 &&
-                               st_stride_slot % vec16 == 0 && aligned16(conv_states)));
-  const int VEC = vec ? vec16 : 1;
+                               st_stride_slot % kLC == 0 && aligned_to(conv_states, lb)));
+  const int VEC = vec ? kLC : 1;
   UpdateParams p = {};
   p.x = x; p.states = conv_states; p.w = weight; p.bias = bias; p.idx = conv_state_indices;
   p.out = out; p.x_rs = x_stride_b; p.ss_slot = st_stride_slot; p.ss_c = st_stride_c;
@@ -717,10 +902,10 @@ extern "C" int causal_conv1d_update(const void* x, int64_t x_stride_b, void* con
   p.threads = (int32_t)th;
   const int64_t grid = cdiv(threads_total, th);
   if (dtype == SCONV_BF16) {
-    if (vec) launch_update<Bf16, 8>(W, p, (uint32_t)grid, th, stream);
+    if (vec) launch_update<Bf16, kLC>(W, p, (uint32_t)grid, th, stream);
     else launch_update<Bf16, 1>(W, p, (uint32_t)grid, th, stream);
   } else {
-    if (vec) launch_update<F32, 4>(W, p, (uint32_t)grid, th, stream);
+    if (vec) launch_update<F32, kLC>(W, p, (uint32_t)grid, th, stream);
     else launch_update<F32, 1>(W, p, (uint32_t)grid, th, stream);
   }
   return check_launch(fn);

@@ -17,6 +17,10 @@ void clear_error();
 int check_launch(const char* what);
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// p is a multiple of `bytes` (a power of two).
+inline bool aligned_to(const void* p, int64_t bytes) {
+  return ((uintptr_t)p & (uintptr_t)(bytes - 1)) == 0;
+}
 
 inline int64_t elem_size(int32_t dtype) { return dtype == SCONV_F32 ? 4 : 2; }
 

@@ -601,7 +601,9 @@ def test_config_ssm_varlen_and_updates():
 @pytest.mark.parametrize("dt,W,dim,idx,inplace", [
     (torch.bfloat16, 4, 64, True, False), (torch.bfloat16, 4, 60, True, True),
     (torch.float32, 4, 32, False, False), (torch.float32, 2, 10, True, True),
-    (torch.bfloat16, 3, 40, True, False), (torch.bfloat16, 1, 16, True, False)])
+    (torch.bfloat16, 3, 40, True, False), (torch.bfloat16, 1, 16, True, False),
+    # odd dims: the one-channel kernel
+    (torch.bfloat16, 4, 37, True, False), (torch.float32, 3, 13, False, True)])
 def test_update_sweep(dt, W, dim, idx, inplace):
     import depthwise_causal_conv1d_amd as lib
     import oracle
@@ -781,13 +783,40 @@ UPD_TOKENS = [
 ]
 
 
+# Cases of the vector-lane kernel: state_len = W-1, channels contiguous
+# ("btd"), dim a multiple of the lane width.  Dims 40 and 64 put several
+# rows, with their own ring rotations, in one wave; dim 1024 spreads a row
+# over several waves.  Seqlens 5 and 9 span several 4-token chunks.
+UPD_TOKENS_VEC = [
+    # name, dtype, W, state_len, seqlen, ring, layout, in_place, bias, indices, dim
+    ("vec-bf16-w4-ring-4", torch.bfloat16, 4, 3, 4, True, "btd", False, True, True, 64),
+    ("vec-bf16-w4-shift-5", torch.bfloat16, 4, 3, 5, False, "btd", True, True, False, 64),
+    ("vec-bf16-w3-ring-9", torch.bfloat16, 3, 2, 9, True, "btd", False, False, True, 128),
+    ("vec-bf16-w2-ring-1", torch.bfloat16, 2, 1, 1, True, "btd", True, True, True, 64),
+    ("vec-f32-w4-ring-3", torch.float32, 4, 3, 3, True, "btd", False, True, True, 40),
+    ("vec-f32-w2-shift-8", torch.float32, 2, 1, 8, False, "btd", False, True, True, 40),
+    ("vec-bf16-w4-ring-1-wide", torch.bfloat16, 4, 3, 1, True, "btd", False, True, True, 1024),
+]
+
+
 @pytest.mark.parametrize("spec", UPD_TOKENS, ids=[s[0] for s in UPD_TOKENS])
 def test_update_tokens_sweep(spec):
+    check_update_tokens(*spec, dim=40)
+
+
+@pytest.mark.parametrize("spec", UPD_TOKENS_VEC, ids=[s[0] for s in UPD_TOKENS_VEC])
+def test_update_tokens_vec_sweep(spec):
+    check_update_tokens(*spec)
+
+
+def check_update_tokens(name, dt, W, L, T, ring, layout, in_place, has_bias, has_idx, dim):
+    """One multi-token update against the oracle: outputs (PAD rows
+    untouched) and the whole state pool, bit for bit.  x and out share the
+    layout: "bdt" (tokens contiguous) or "btd" (channels contiguous)."""
     import depthwise_causal_conv1d_amd as lib
     import oracle
-    name, dt, W, L, T, ring, layout, in_place, has_bias, has_idx = spec
     g = torch.Generator().manual_seed(zlib.crc32(name.encode()) % 1000)
-    batch, dim, slots = 7, 40, 12
+    batch, slots = 7, 12
     xs = torch.randn(batch, dim, T, generator=g).to(dt)
     if layout == "btd":  # tokens outer, channels contiguous
         x = xs.permute(0, 2, 1).contiguous().permute(0, 2, 1)
@@ -812,9 +841,12 @@ def test_update_tokens_sweep(spec):
         to_np(xs), to_np(st), to_np(w), None if bias is None else to_np(bias), "silu",
         None if seqlens is None else to_np(seqlens), None if idx is None else to_np(idx), -1,
         out_init=to_np(xs if in_place else out0))
-    xg = x.to(DEV) if layout == "bdt" else x.to(DEV).permute(0, 2, 1).contiguous().permute(0, 2, 1)
+    def on_dev(t):  # same values, in this case's layout
+        t = t.to(DEV)
+        return t.contiguous() if layout == "bdt" else t.permute(0, 2, 1).contiguous().permute(0, 2, 1)
+    xg = on_dev(x)
     stg = st.to(DEV)
-    outg = None if in_place else out0.to(DEV).clone()
+    outg = None if in_place else on_dev(out0)
     res = lib.causal_conv1d_update_tokens(
         xg, stg, w.to(DEV), None if bias is None else bias.to(DEV), True,
         None if seqlens is None else seqlens.to(DEV), None if idx is None else idx.to(DEV), -1,
