@@ -608,7 +608,7 @@ class SsmSpecDecodeBench(Workload):
     dim 8192 per step against ring states (W-1 columns, positions
     uniform[0, 4096)), through causal_conv1d_update_tokens; 64 steps per
     graph, each with its own inputs and outputs."""
-    kernel_name = "update_tokens_kernel"
+    kernel_name = "update_tokens_vec_kernel"
     B, T, DIM, W, STEPS = 8, 4, 8192, 4, 64
 
     def __init__(self, dev="cuda"):

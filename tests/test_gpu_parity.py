@@ -715,6 +715,25 @@ SSM_GATHER = [
 ]
 
 
+def test_config_ssm_state_gather():
+    """The benchmarked extraction at full size: 128 chunk states of 2 MiB
+    (64 x 64 x 128 fp32), 128 slots at distinct indices, 96 live; the whole
+    output bit for bit (dead slots keep their sentinel)."""
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    g = torch.Generator().manual_seed(13)
+    nc, shape, mc, live = 128, (64, 64, 128), 128, 96
+    states = torch.randn((nc,) + shape, generator=g)
+    idx = torch.randperm(nc, generator=g)
+    out0 = torch.full((mc,) + shape, SENTINEL)
+    say("ssm gather at full size: 128 x 2 MiB rows, 96 live")
+    out_r = oracle.gather_ssm_state(to_np(states), to_np(idx), live, to_np(out0))
+    out_g = out0.to(DEV)
+    lib.gather_intermediate_ssm_state(states.to(DEV), idx.to(DEV),
+                                      torch.tensor([live], dtype=torch.int32, device=DEV), out_g)
+    assert_bits_equal(to_np(out_g), out_r, "full-size SSM-state gather")
+
+
 @pytest.mark.parametrize("spec", SSM_GATHER, ids=[s[0] for s in SSM_GATHER])
 def test_ssm_state_gather_sweep(spec):
     import depthwise_causal_conv1d_amd as lib
@@ -856,6 +875,36 @@ def check_update_tokens(name, dt, W, L, T, ring, layout, in_place, has_bias, has
     assert_close(got[live], out_r[live], dtype_name(dt), f"{name} out")
     assert_bits_equal(got[~live], out_r[~live], f"{name} PAD rows untouched")
     assert_bits_equal(to_np(stg), st_r, f"{name} state pool")
+
+
+def test_config_ssm_spec_decode():
+    """The benchmarked speculative step at full size: 8 rows x 4 draft tokens
+    x 8192 channels, channels contiguous (the vector-lane kernel), ring
+    states of W-1 columns in a 1024-slot pool at positions uniform in
+    [0, 4096); three steps in a row, each checked against the oracle (out,
+    and the whole pool bit for bit)."""
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    g = torch.Generator().manual_seed(12)
+    B, T, dim, W, slots = 8, 4, 8192, 4, 1024
+    w = (torch.randn(dim, W, generator=g) * 0.5).to(torch.bfloat16)
+    bias = (torch.randn(dim, generator=g) * 0.1).to(torch.bfloat16)
+    pool = torch.randn(slots, dim, W - 1, generator=g).to(torch.bfloat16)
+    ci = torch.randperm(slots, generator=g)[:B].to(torch.int32)
+    pool_g, w_g, b_g, ci_g = pool.to(DEV), w.to(DEV), bias.to(DEV), ci.to(DEV)
+    pool_r = to_np(pool)
+    for step in range(3):
+        x = torch.randn(B, T, dim, generator=g).to(torch.bfloat16)  # tokens outer
+        seqlens = torch.randint(0, 4096, (B,), generator=g).to(torch.int32)
+        say(f"ssm spec decode step {step}")
+        out_r, pool_r = oracle.causal_conv1d_update_tokens(
+            to_np(x.permute(0, 2, 1).contiguous()), pool_r, to_np(w), to_np(bias), "silu",
+            to_np(seqlens), to_np(ci), -1)
+        out_g = torch.empty(B, T, dim, dtype=torch.bfloat16, device=DEV)
+        lib.causal_conv1d_update_tokens(x.to(DEV).permute(0, 2, 1), pool_g, w_g, b_g, True,
+                                        seqlens.to(DEV), ci_g, -1, out=out_g.permute(0, 2, 1))
+        assert_close(to_np(out_g.permute(0, 2, 1).contiguous()), out_r, "bf16", f"step {step} out")
+        assert_bits_equal(to_np(pool_g), pool_r, f"step {step} pool")
 
 
 def test_update_ring_form_equals_tokens_entry():
