@@ -5,16 +5,24 @@
 Default workload (the headline): batched decode -- 256 requests x 1 token,
 history lengths uniform in [1, 4096], H=32, D=128, ws=32 (C=1024), W=4,
 N=16, bf16, SiLU and residual.  One step is one pass of the hot path over one
-decode batch: sconv_seq_metadata + sconv_fused_insert_conv, replayed from a
-hipGraph.  Other workloads (same JSON shape, one line each):
-  mixed_prefill  16 requests, ~17-20k rows, 4 streams of C=4096 over one
-                 cache, 10% PAD rows; step = metadata + 4 fused launches
-  spec_decode    512 requests x 4 draft rows, C=4096, N=32; step = metadata
-                 + fused launch + conv-window gather (device real_count)
-  ssm_prefill    8 x 4096 tokens, dim 8192, channel-major, state pool of
-                 1024 slots; step = causal_conv1d_varlen_fwd
-  ssm_decode     8 rows x dim 8192 against the same pool; step =
-                 causal_conv1d_update
+decode batch, replayed from a hipGraph: by default one launch of
+sconv_fused_insert_conv_qsl (request search, insert and conv);
+`--metadata separate` runs sconv_seq_metadata + sconv_fused_insert_conv.
+Other workloads (same JSON shape, one line each):
+  decode_layer      the decode batch with all four streams of a layer
+                    (ws=32 each) in one sconv_fused_insert_conv_streams launch
+  mixed_prefill     16 requests, ~17-20k rows, 4 streams of C=4096 over one
+                    cache, 10% PAD rows; step = metadata + 4 fused launches
+  spec_decode       512 requests x 4 draft rows, C=4096, N=32; step = folded
+                    fused launch + conv-window gather (device real_count)
+  ssm_prefill       8 x 4096 tokens, dim 8192, channel-major, state pool of
+                    1024 slots; step = causal_conv1d_varlen_fwd
+  ssm_decode        8 rows x dim 8192 against the same pool; step =
+                    causal_conv1d_update
+  ssm_spec_decode   8 rows x 4 draft tokens x dim 8192, ring states; step =
+                    causal_conv1d_update_tokens
+  ssm_state_gather  96 live of 128 slots, 2 MiB fp32 state rows; step =
+                    gather_intermediate_ssm_state (device real_count)
 
 Successive steps cycle through independent replicas of the workload's
 inputs (own inputs, outputs, tables and cache blocks) so that at least
@@ -767,7 +775,7 @@ def main():
                          "reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: libsconv has no multi-GPU path "
               "(the op shards per request or per head with no exchange); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

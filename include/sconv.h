@@ -35,7 +35,7 @@ typedef struct ihipStream_t* hipStream_t;
 enum {
   SCONV_OK = 0,
   SCONV_ERR_INVALID = 1,     /* bad host scalar, shape, stride or pointer */
-  SCONV_ERR_UNSUPPORTED = 2, /* valid request this build does not cover   */
+  SCONV_ERR_UNSUPPORTED = 2, /* valid request the library does not cover */
   SCONV_ERR_HIP = 3          /* the HIP runtime reported a launch error   */
 };
 
