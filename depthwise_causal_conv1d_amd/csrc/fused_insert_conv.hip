@@ -204,14 +204,27 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   const uint32_t total_waves = (uint32_t)p.num_tiles * (uint32_t)p.num_slabs;
   const bool live_wave = wave < total_waves;
   if (!live_wave) wave = total_waves - 1;
+  // Slab-major: consecutive waves walk consecutive tiles of one slab, so
+  // the chip advances over rows as one band.  A multi-stream launch of
+  // one-row tiles (a layer's decode step) runs tile-major instead: the
+  // slabs of all streams for one row are then neighbours on one XCD, and
+  // the streams' pieces of a cache row, which share 128-byte lines, meet
+  // in one L2.
 #if SCONV_FUSED_SLAB_MAJOR
-  const uint32_t slab_u = wave / (uint32_t)p.num_tiles;
-  const uint32_t tile = wave - slab_u * (uint32_t)p.num_tiles;
-  const int slab = (int)slab_u;
+  constexpr bool kSlabMajor = !(MS && BT == 1);
 #else
-  const uint32_t tile = wave / (uint32_t)p.num_slabs;
-  const int slab = (int)(wave - tile * (uint32_t)p.num_slabs);
+  constexpr bool kSlabMajor = false;
 #endif
+  uint32_t tile;
+  int slab;
+  if constexpr (kSlabMajor) {
+    const uint32_t slab_u = wave / (uint32_t)p.num_tiles;
+    tile = wave - slab_u * (uint32_t)p.num_tiles;
+    slab = (int)slab_u;
+  } else {
+    tile = wave / (uint32_t)p.num_slabs;
+    slab = (int)(wave - tile * (uint32_t)p.num_slabs);
+  }
   const int64_t t0 = (int64_t)tile * BT;
 
 
@@ -473,8 +486,8 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // of its slab, still load their halo.  Only launches of several wave
   // generations do this: when all waves are resident at once, the barrier
   // would hold back the history lookups that bound such launches.
-#if SCONV_FUSED_LDS_HALO && SCONV_FUSED_SLAB_MAJOR
-  constexpr bool kLdsHalo = !NTX && W > 1 && BT >= W - 1;
+#if SCONV_FUSED_LDS_HALO
+  constexpr bool kLdsHalo = kSlabMajor && !NTX && W > 1 && BT >= W - 1;
 #else
   constexpr bool kLdsHalo = false;
 #endif

@@ -327,6 +327,8 @@ STREAM_SPECS = [
      [None, "silu", "silu"], [True, True, True], [5, 17], [2, 40], 2, 0),
     ("bf16-w3-two", torch.bfloat16, 3, 8, 64, 32, [(32, 32), (0, 16)],
      ["silu", "silu"], [False, True], [3, 60, 1], [100, 7, 0], 5, 3),
+    ("bf16-w2-three", torch.bfloat16, 2, 4, 64, 16, [(0, 16), (16, 16), (48, 16)],
+     ["silu", None, "silu"], [True, True, False], [7, 30, 2, 1], [5, 0, 40, 17], 3, 1),
 ]
 
 
