@@ -89,6 +89,33 @@ def test_fused_rejects_bad_scalars(lib):
     assert b"overlaps" in lib.sconv_last_error()
 
 
+def _fused_qsl(lib, **kw):
+    a = dict(x=NULL, xrs=16, w=NULL, wsc=4, wsk=1, cache=NULL, nb=8, H=2, N=16, D=32,
+             cs0=1024, cs1=512, cs2=32, pos=NULL, bt=NULL, btrs=4, mb=4, qsl=NULL, nreq=2,
+             sm=NULL, out=NULL, ors=16, T=64, off=0, ws=8, W=4, dt=0, act=1, res=1)
+    a.update(kw)
+    return lib.sconv_fused_insert_conv_qsl(*a.values(), NULL)
+
+
+def test_folded_entry_rejects_bad_scalars(lib):
+    """sconv_fused_insert_conv_qsl: the request offsets are required with
+    rows to process, num_reqs must be >= 1, and every check of the
+    per-row entry applies as well.  No call reaches a launch."""
+    assert _fused_qsl(lib) == 1 and b"query_start_loc" in lib.sconv_last_error()
+    one = ctypes.c_int32(0)
+    q = ctypes.addressof(one)
+    assert _fused_qsl(lib, qsl=q, nreq=0) == 1     # NULL buffers are checked first
+    buf = (ctypes.c_uint8 * 1024)()
+    b = ctypes.addressof(buf)
+    # stand-in addresses, never dereferenced: validation fails first
+    dev = dict(x=b, w=b, cache=b + (1 << 20), pos=b, bt=b, sm=b, out=b + (1 << 21))
+    assert _fused_qsl(lib, qsl=q, nreq=0, **dev) == 1
+    assert b"num_reqs" in lib.sconv_last_error()
+    assert _fused_qsl(lib, qsl=q, W=5) == 1 and b"W=5" in lib.sconv_last_error()
+    assert _fused_qsl(lib, qsl=q, off=28) == 1
+    assert _fused_qsl(lib, T=0) == 0             # empty batch: no-op, offsets not needed
+
+
 def test_ssm_ops_reject_bad_scalars(lib):
     v = lib.causal_conv1d_varlen_fwd
     assert v(NULL, 1, 1, NULL, 4, 1, NULL, NULL, 1, 1, 1, 1, NULL, 1, NULL, NULL, NULL, 1, 1, 8,
