@@ -136,7 +136,7 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_ENOUGH_WAVES 4096
 #endif
 #ifndef SCONV_FUSED_NT_HIST
-#define SCONV_FUSED_NT_HIST 1  // streaming history loads where no one reads the rest of the line
+#define SCONV_FUSED_NT_HIST 1  // streaming history loads in one-row tiles with sub-line pieces
 #endif
 #ifndef SCONV_FUSED_BT_ROW
 #define SCONV_FUSED_BT_ROW 1  // one-row tiles of decode-shaped launches guess request t
@@ -715,8 +715,8 @@ static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipS
 
 template <typename D, int VEC, int W, int BT, bool MS>
 static void launch_n(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
-  // Streaming history loads are built for one-stream one-row tiles (decode).
-  if constexpr (BT == 1 && W > 1 && !MS) {
+  // Streaming history loads are built for one-row tiles (decode).
+  if constexpr (BT == 1 && W > 1) {
     if (p.nt_hist) {
       launch_q<D, VEC, W, BT, false, MS, true>(p, grid, threads, s);
       return;
@@ -905,14 +905,16 @@ static int fused_launch(
   // resident at once the launch is latency-bound and streaming loads win;
   // over several generations the halo re-reads must find the rows in L2.
   p.nt_x = waves <= SCONV_FUSED_NT_LOADS_MAX_WAVES;
-  // A history piece of one head is ws elements of a cache row.  When it is
-  // less than a 128-byte line and no other stream of the launch reads the
-  // rest of that line, a streaming load skips keeping a line that no one
-  // will read again: measured faster on one-stream decode (4.48 -> 4.18 us
-  // at 256 requests, 19.8 -> 18.1 us at 4096).  Where other pieces of the
-  // line are read (several streams) or pieces are whole lines, it was
-  // slower, so those launches keep ordinary loads.
-  p.nt_hist = SCONV_FUSED_NT_HIST && num_streams == 1 && bt == 1 && streams[0].ws * es < 128;
+  // A history piece of one head is ws elements of a cache row.  In one-row
+  // tiles (decode) whose pieces are less than a 128-byte line, streaming
+  // loads measured faster: one stream 4.48 -> 4.18 us at 256 requests and
+  // 19.8 -> 18.1 us at 4096; four streams of ws = 32, whose pieces share
+  // lines and whose launch runs tile-major, 5.93 -> 5.53 us.  Four-row
+  // tiles with whole-line pieces (spec decode) were 7-10% slower with them,
+  // and so was the four-stream launch in slab-major order.
+  int64_t widest = 0;  // the largest piece of any stream, in elements
+  for (int s = 0; s < num_streams; ++s) widest = streams[s].ws > widest ? streams[s].ws : widest;
+  p.nt_hist = SCONV_FUSED_NT_HIST && bt == 1 && widest * es < 128;
   p.waves_per_group = (int32_t)(threads / 64);
 
   if (dtype == SCONV_BF16) {
