@@ -417,6 +417,76 @@ def test_config_spec_decode(fold):
 
 # ------------------------------------------------------------------ hipGraph replay
 
+def test_graph_replay_folded_decode_layouts():
+    """One captured folded decode launch (48 rows, 48 requests), replayed on
+    three request layouts written into its buffers: every row its own
+    request (the request guess holds), empty and two-row requests with
+    padded tail rows (rows off the guess), and histories past the first 256
+    block-table entries.  The choice between these paths is made on the
+    device at each replay; every replay equals the oracle, outputs and the
+    whole cache."""
+    import depthwise_causal_conv1d_amd as lib
+    R, N, H, D, ws, WBT, POOL = 48, 4, 4, 64, 32, 400, 128
+    rng = np.random.default_rng(71)
+    mixed = _decode_shaped_lens(rng, R, 4)
+    layouts = [("one row per request", [1] * R, [int(v) for v in rng.integers(0, 300, R)]),
+               ("empty and two-row requests", mixed, [int(v) for v in rng.integers(0, 300, R)]),
+               ("histories past 256 blocks", [1] * R,
+                [int(v) for v in rng.integers(1000, 1590, R)])]
+    cases = []
+    for k, (name, new, ctx) in enumerate(layouts):
+        c = workloads.fused_case(72 + k, new, ctx, H=H, D=D, ws=ws, block_size=N, W=4,
+                                 dtype=torch.bfloat16, pool_blocks=POOL, pad_count=2,
+                                 tail_pad=R - sum(new))
+        assert c.T == R and c.block_table.shape[1] <= WBT
+        bt = torch.full((R, WBT), c.poison_block, dtype=torch.int32)
+        bt[:, :c.block_table.shape[1]] = c.block_table
+        cases.append((name, c, bt))
+    c0 = cases[0][1]
+    x_b = torch.zeros(R, c0.C, dtype=torch.bfloat16, device=DEV)
+    w_b = torch.zeros_like(c0.weight, device=DEV)
+    cache_b = torch.zeros_like(c0.cache, device=DEV)
+    pos_b = torch.zeros(R, dtype=torch.int64, device=DEV)
+    sm_b = torch.zeros(R, dtype=torch.int64, device=DEV)
+    qsl_b = torch.zeros(R + 1, dtype=torch.int32, device=DEV)
+    bt_b = torch.zeros(R, WBT, dtype=torch.int32, device=DEV)
+    out_b = torch.zeros_like(x_b)
+
+    def load(c, bt):
+        for dst, src in ((x_b, c.x), (w_b, c.weight), (cache_b, c.cache), (pos_b, c.positions),
+                         (sm_b, c.slot_mapping), (qsl_b, c.query_start_loc), (bt_b, bt)):
+            dst.copy_(src.to(DEV))
+        out_b.fill_(SENTINEL)
+
+    def step():
+        lib.sconv_fused_insert_conv_qsl(x_b, w_b, cache_b, pos_b, bt_b, qsl_b, R, sm_b, 0, ws, N,
+                                        "silu", True, out=out_b)
+
+    load(c0, cases[0][2])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for name, c, bt in cases + cases[:1]:
+        load(c, bt)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        out_r, cache_r, _, _ = oracle_fused(c)
+        live = live_rows(c)
+        got = to_np(out_b)
+        assert_close(got, out_r, "bf16", f"{name} out", mask=live)
+        assert_bits_equal(got[~live], out_r[~live], f"{name} PAD rows untouched")
+        assert_bits_equal(to_np(cache_b), cache_r, f"{name} cache")
+        say(f"  replay '{name}' ok")
+
+
 @pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
 def test_graph_replay_decode_steps(fold):
     """Capture metadata + fused conv once for a decode batch; replay it for
