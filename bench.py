@@ -180,6 +180,20 @@ def sub_case(case, rows, reqs, poison):
                                   "used_blocks": torch.sort(u).values})
 
 
+def repeat_until(budget, once):
+    """Oracle timing loop of the CPU baseline: call once(n) for n = 0, 1, ...
+    (each call returns the tokens it covered and the seconds it took) until
+    `budget` seconds of oracle time are spent, at least once.  Returns
+    (tokens, seconds, calls)."""
+    tokens, spent, n = 0, 0.0, 0
+    while n == 0 or spent < budget:
+        u, t = once(n)
+        tokens += u
+        spent += t
+        n += 1
+    return tokens, spent, n
+
+
 def time_oracle_fused(case, activation="silu"):
     """Seconds the oracle spends on one fused launch of `case` (compact cache)."""
     import oracle
@@ -265,16 +279,15 @@ class DecodeBench(Workload):
                 "graph": "hipGraph", "replicas": self.R}
 
     def oracle_sample(self, budget):
-        # Whole sub-batches of 256 requests, until the budget is spent.
-        done, spent, i = 0, 0.0, 0
+        # Whole sub-batches of 256 requests, cycled, until the budget is spent.
         n_sub = self.R * self.B // 256
-        while i < n_sub and (spent < budget or done == 0):
-            rows = slice(256 * i, 256 * (i + 1))
-            sub = sub_case(self.case, rows, rows, self.case.poison_block)
-            spent += time_oracle_fused(sub)
-            done += 256
-            i += 1
-        return done / spent, f"{i} decode sub-batches of 256 requests ({done} tokens)", spent
+
+        def once(n):
+            rows = slice(256 * (n % n_sub), 256 * (n % n_sub + 1))
+            return 256, time_oracle_fused(sub_case(self.case, rows, rows, self.case.poison_block))
+        done, spent, n = repeat_until(budget, once)
+        return (done / spent, f"{n} decode sub-batches of 256 requests ({done} tokens, cycling "
+                f"the {n_sub} distinct ones)", spent)
 
 
 class DecodeLayerBench(Workload):
@@ -345,17 +358,17 @@ class DecodeLayerBench(Workload):
                 "activation": "silu", "residual": True, "graph": "hipGraph", "replicas": self.R}
 
     def oracle_sample(self, budget):
-        # Whole sub-batches of 256 requests x 4 streams, until the budget is spent.
-        done, spent, i = 0, 0.0, 0
+        # Whole sub-batches of 256 requests x 4 streams, cycled, until the
+        # budget is spent.
         n_sub = self.R * self.B // 256
-        while i < n_sub and (spent < budget or done == 0):
-            rows = slice(256 * i, 256 * (i + 1))
-            for k in self.cases:
-                sub = sub_case(k, rows, rows, k.poison_block)
-                spent += time_oracle_fused(sub)
-            done += 256
-            i += 1
-        return done / spent, f"{i} decode sub-batches of 256 requests x 4 streams ({done} tokens)", spent
+
+        def once(n):
+            rows = slice(256 * (n % n_sub), 256 * (n % n_sub + 1))
+            return 256, sum(time_oracle_fused(sub_case(k, rows, rows, k.poison_block))
+                            for k in self.cases)
+        done, spent, n = repeat_until(budget, once)
+        return (done / spent, f"{n} decode sub-batches of 256 requests x 4 streams ({done} tokens, "
+                f"cycling the {n_sub} distinct ones)", spent)
 
 
 class MixedPrefillBench(Workload):
@@ -428,9 +441,11 @@ class MixedPrefillBench(Workload):
                 "activation": "silu", "residual": True}
 
     def oracle_sample(self, budget):
-        # Stream 0 in full; the other three streams cost the same.
-        spent = time_oracle_fused(self.streams[0])
-        return self.live / (4 * spent), "stream 0 of 4, all rows, time x4", spent
+        # Whole streams (all rows), in turn, until the budget is spent; a
+        # token counts once for its four streams.
+        done, spent, n = repeat_until(
+            budget, lambda n: (self.live / 4, time_oracle_fused(self.streams[n % 4])))
+        return done / spent, f"{n} whole-stream passes over all {self.live} live rows", spent
 
 
 class SpecDecodeBench(Workload):
@@ -499,14 +514,14 @@ class SpecDecodeBench(Workload):
                 "replicas": self.R}
 
     def oracle_sample(self, budget):
-        done, spent, i = 0, 0.0, 0
-        while i < self.R and (spent < budget or done == 0):
+        def once(n):
+            i = n % self.R
             sub = sub_case(self.case, self.rows(i), slice(512 * i, 512 * (i + 1)),
                            self.case.poison_block)
-            spent += time_oracle_fused(sub)
-            done += self.B
-            i += 1
-        return done / spent, f"fused conv of {i} whole spec batches ({done} tokens)", spent
+            return self.B, time_oracle_fused(sub)
+        done, spent, n = repeat_until(budget, once)
+        return (done / spent, f"fused conv of {n} whole spec batches ({done} tokens, cycling the "
+                f"{self.R} distinct ones)", spent)
 
 
 class SsmPrefillBench(Workload):
@@ -551,19 +566,26 @@ class SsmPrefillBench(Workload):
         import oracle
         from tests.helpers import to_np
         c = self.case
-        # Two of the eight sequences (one with a state, one without).
-        keep = [int(torch_where(c.has_initial_state)[0]), int(torch_where(~c.has_initial_state)[0])]
+        import numpy as np
+        # Pairs of sequences (one with a state, one without), in turn, all
+        # channels, until the budget is spent.
+        with_st = [int(v) for v in torch_where(c.has_initial_state)]
+        without = [int(v) for v in torch_where(~c.has_initial_state)]
         L = 4096
         xs = to_np(c.x)
-        import numpy as np
-        x2 = np.ascontiguousarray(np.concatenate([xs[:, k * L:(k + 1) * L] for k in keep], 1))
-        args = (x2, to_np(c.weight), to_np(c.bias), to_np(c.conv_states),
-                np.array([0, L, 2 * L], np.int32), to_np(c.cache_indices)[keep],
-                to_np(c.has_initial_state)[keep], "silu", -1)
-        t0 = time.perf_counter()
-        oracle.causal_conv1d_varlen_fwd(*args)
-        spent = time.perf_counter() - t0
-        return 2 * L / spent, "2 of the 8 sequences (8192 tokens, all channels)", spent
+        w, b, st, ci, hi = (to_np(c.weight), to_np(c.bias), to_np(c.conv_states),
+                            to_np(c.cache_indices), to_np(c.has_initial_state))
+
+        def once(n):
+            keep = [with_st[n % len(with_st)], without[n % len(without)]]
+            x2 = np.ascontiguousarray(np.concatenate([xs[:, k * L:(k + 1) * L] for k in keep], 1))
+            t0 = time.perf_counter()
+            oracle.causal_conv1d_varlen_fwd(x2, w, b, st, np.array([0, L, 2 * L], np.int32),
+                                            ci[keep], hi[keep], "silu", -1)
+            return 2 * L, time.perf_counter() - t0
+        done, spent, n = repeat_until(budget, once)
+        return (done / spent, f"{n} pairs of 4096-token sequences, one with a state and one "
+                f"without ({done} tokens, all channels)", spent)
 
 
 class SsmDecodeBench(Workload):
@@ -602,13 +624,16 @@ class SsmDecodeBench(Workload):
         import oracle
         from tests.helpers import to_np
         c = self.case
-        st = to_np(c.conv_states)
-        x = to_np(self.x[0])
-        t0 = time.perf_counter()
-        oracle.causal_conv1d_update(x, st, to_np(c.weight), to_np(c.bias), "silu",
-                                    to_np(c.cache_indices), -1)
-        spent = time.perf_counter() - t0
-        return 8 / spent, "one decode step (8 rows)", spent
+        st, w, b, ci = (to_np(c.conv_states), to_np(c.weight), to_np(c.bias),
+                        to_np(c.cache_indices))
+        xs = [to_np(self.x[i]) for i in range(min(self.R, 8))]
+
+        def once(n):
+            t0 = time.perf_counter()
+            oracle.causal_conv1d_update(xs[n % len(xs)], st, w, b, "silu", ci, -1)
+            return 8, time.perf_counter() - t0
+        done, spent, n = repeat_until(budget, once)
+        return done / spent, f"{n} decode steps of 8 rows ({done} tokens)", spent
 
 
 class SsmSpecDecodeBench(Workload):
@@ -659,13 +684,18 @@ class SsmSpecDecodeBench(Workload):
         import oracle
         from tests.helpers import to_np
         c = self.case
-        x = to_np(self.x[0].permute(0, 2, 1).cpu())
-        t0 = time.perf_counter()
-        oracle.causal_conv1d_update_tokens(x, to_np(c.conv_states), to_np(c.weight),
-                                           to_np(c.bias), "silu", to_np(self.seqlens[0].cpu()),
-                                           to_np(c.cache_indices), -1)
-        spent = time.perf_counter() - t0
-        return self.B * self.T / spent, "one step (8 rows x 4 tokens)", spent
+        st, w, b, ci = (to_np(c.conv_states), to_np(c.weight), to_np(c.bias),
+                        to_np(c.cache_indices))
+        steps = [(to_np(self.x[i].permute(0, 2, 1).cpu()), to_np(self.seqlens[i].cpu()))
+                 for i in range(min(self.R, 8))]
+
+        def once(n):
+            x, sl = steps[n % len(steps)]
+            t0 = time.perf_counter()
+            oracle.causal_conv1d_update_tokens(x, st, w, b, "silu", sl, ci, -1)
+            return self.B * self.T, time.perf_counter() - t0
+        done, spent, n = repeat_until(budget, once)
+        return done / spent, f"{n} steps of 8 rows x 4 tokens ({done} tokens)", spent
 
 
 class SsmStateGatherBench(Workload):
@@ -712,10 +742,13 @@ class SsmStateGatherBench(Workload):
         st = self.states[0][:16].cpu().numpy()
         idx = (self.idx[0].cpu() % 16).numpy()
         out0 = self.out[0][:32].cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.gather_ssm_state(st, idx, 32, out0)
-        spent = time.perf_counter() - t0
-        return 32 / spent, "32 slots from 16 chunk states", spent
+
+        def once(n):
+            t0 = time.perf_counter()
+            oracle.gather_ssm_state(st, idx, 32, out0)
+            return 32, time.perf_counter() - t0
+        done, spent, n = repeat_until(budget, once)
+        return done / spent, f"{n} gathers of 32 slots from 16 chunk states ({done} slots)", spent
 
 
 def torch_where(mask):
