@@ -293,6 +293,81 @@ def test_fused_positions_near_int31(spec, fold):
 _STREAMS_ORACLE = {}
 
 
+_KINDS = ("decode", "decode-shifted", "prefill", "spec", "empty-runs", "large")
+
+
+def _random_fused_spec(k):
+    """Case k of the seeded random sweep: the layout kind cycles through
+    _KINDS; dtype, W, block size, heads, streams (16-byte-lane or odd widths,
+    gaps between column ranges), history lengths, PAD and tail rows and the
+    metadata form are drawn from a generator seeded with k."""
+    rng = np.random.default_rng(4000 + k)
+    kind = _KINDS[k % len(_KINDS)]
+    dt = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    lane = 8 if dt == torch.bfloat16 else 4
+    W = int(rng.integers(1, 5))
+    N = int(rng.choice([1, 4, 8, 16, 24, 32]))
+    if kind == "large":
+        H, nst, unit, cmax = 32, 1, lane, 600
+        widths = [128 if dt == torch.bfloat16 else 64]
+    else:
+        H = int(rng.integers(1, 9))
+        nst = int(rng.choice([1, 1, 2, 3, 4]))
+        unit = lane if rng.random() < 0.75 else 1
+        widths = [unit * int(rng.integers(1, 5)) for _ in range(nst)]
+        cmax = int(rng.choice([0, 40, 3000]))
+    offs, at = [], unit * int(rng.integers(0, 2))
+    for w_ in widths:
+        offs.append(at)
+        at += w_ + unit * int(rng.integers(0, 2))
+    D = at + unit * int(rng.integers(0, 2))
+    if kind == "decode":
+        R = int(rng.integers(1, 600))
+        new = [1] * R
+    elif kind == "decode-shifted":
+        R = int(rng.integers(2, 600))
+        new = _decode_shaped_lens(rng, R, 0)
+    elif kind == "prefill":
+        R = int(rng.integers(1, 12))
+        new = [int(v) for v in rng.integers(1, 300, R)]
+    elif kind == "spec":
+        R = int(rng.integers(1, 300))
+        new = [4] * R
+    elif kind == "empty-runs":
+        R = int(rng.integers(60, 700))
+        new = [int(v) for v in rng.choice([0, 0, 0, 1, 3], R)]
+        new[-1] = max(new[-1], 1)
+    else:
+        R = int(rng.integers(2, 6))
+        new = [int(v) for v in rng.integers(1500, 3000, R)]
+    ctx = [int(v) for v in rng.integers(0, cmax + 1, R)]
+    T = sum(new)
+    pad = int(rng.integers(0, T // 8 + 1))
+    tail = int(rng.integers(0, 4))
+    fold = bool(rng.random() < 0.5)
+    return dict(kind=kind, dt=dt, W=W, N=N, H=H, D=D, streams=list(zip(offs, widths)), new=new,
+                ctx=ctx, pad=pad, tail=tail, fold=fold)
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_fused_random_sweep(k):
+    """24 seeded random launches of the fused op, single- or multi-stream,
+    against the oracle (outputs, PAD rows untouched, whole cache)."""
+    c = _random_fused_spec(k)
+    if len(c["streams"]) == 1:
+        off, ws = c["streams"][0]
+        case = workloads.fused_case(5000 + k, c["new"], c["ctx"], H=c["H"], D=c["D"], ws=ws,
+                                    off_s=off, block_size=c["N"], W=c["W"], dtype=c["dt"],
+                                    pad_count=c["pad"], tail_pad=c["tail"])
+        check_fused(case, f"random {k} ({c['kind']})", fold=c["fold"])
+    else:
+        cases = workloads.fused_streams_case(5000 + k, c["new"], c["ctx"], H=c["H"], D=c["D"],
+                                             streams=c["streams"], block_size=c["N"], W=c["W"],
+                                             dtype=c["dt"], pad_count=c["pad"],
+                                             tail_pad=c["tail"])
+        check_streams(cases, f"random {k} ({c['kind']})", c["fold"])
+
+
 def check_streams(cases, what, fold, cache_compare="full"):
     """One multi-stream launch against the oracle's multi-stream op: every
     stream's output (PAD rows untouched) and the shared cache, bit for bit."""
