@@ -1072,3 +1072,65 @@ def test_update_ring_form_equals_tokens_entry():
                                    seqlens.to(DEV), None, -1, out=torch.empty_like(x, device=DEV))
     assert_close(to_np(out), out_r[:, :, 0], "bf16", "ring update out")
     assert_bits_equal(to_np(stg), st_r, "ring update state")
+
+
+# ------------------------------------------------------------------ random SSM-side sweep
+
+def _ssm_rng(op, k):
+    return np.random.default_rng(zlib.crc32(f"{op}-{k}".encode()))
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_varlen_random_sweep(k):
+    """Seeded random varlen launches: lengths including 0 and 1, vector and
+    odd dims, W 1-4, some sequences with a state, PAD sequences, padded x
+    rows, bias and activation drawn at random; out-of-place and in place."""
+    rng = _ssm_rng("varlen", k)
+    dt = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    lane = 8 if dt == torch.bfloat16 else 4
+    n = int(rng.integers(1, 7))
+    lens = [int(v) for v in rng.choice([0, 1, 2, 3, 17, 64, 255, 513, 1000], n)]
+    dim = lane * int(rng.integers(1, 6)) if rng.random() < 0.6 else int(rng.integers(1, 40))
+    W = int(rng.integers(1, 5))
+    spec = (f"random-varlen-{k}", dt, lens, dim, W, int(rng.integers(0, n + 1)),
+            int(rng.integers(0, n // 2 + 1)), None if rng.random() < 0.3 else 0.1,
+            "silu" if rng.random() < 0.7 else None, int(rng.choice([0, 0, 5])))
+    test_varlen_sweep(spec)
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_update_tokens_random_sweep(k):
+    """Seeded random multi-token updates: seqlen 1-9, state length W-1..8,
+    shift or ring states, both x layouts, vector or odd dims, in place or
+    not, with and without bias and indices."""
+    rng = _ssm_rng("update_tokens", k)
+    dt = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    W = int(rng.integers(1, 5))
+    L = W - 1 if rng.random() < 0.5 else int(rng.integers(W - 1, 9))
+    ring = bool(L >= 1 and rng.random() < 0.6)
+    dim = 2 * int(rng.integers(1, 40)) if rng.random() < 0.7 else 2 * int(rng.integers(1, 20)) + 1
+    check_update_tokens(f"random-update-tokens-{k}", dt, W, L, int(rng.integers(1, 10)), ring,
+                        "btd" if rng.random() < 0.6 else "bdt", bool(rng.random() < 0.4),
+                        bool(rng.random() < 0.7), bool(rng.random() < 0.7), dim)
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_update_random_sweep(k):
+    """Seeded random one-token updates: W 1-4, vector or odd dims, with or
+    without indices (one PAD row), in place or not."""
+    rng = _ssm_rng("update", k)
+    dt = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    dim = 2 * int(rng.integers(1, 100)) if rng.random() < 0.7 else 2 * int(rng.integers(1, 50)) + 1
+    test_update_sweep(dt, int(rng.integers(1, 5)), dim, bool(rng.random() < 0.7),
+                      bool(rng.random() < 0.4))
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_gather_random_sweep(k):
+    """Seeded random conv-window gathers: odd or vector channel counts,
+    d_conv 1-4, short and long sources, live counts 0, some and all."""
+    rng = _ssm_rng("gather", k)
+    dt = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    lane = 8 if dt == torch.bfloat16 else 4
+    conv_dim = lane * int(rng.integers(1, 70)) if rng.random() < 0.6 else int(rng.integers(1, 90))
+    test_gather_sweep(dt, conv_dim, int(rng.integers(1, 5)), int(rng.integers(1, 300)))
