@@ -20,6 +20,12 @@
 #ifndef SCONV_GATHER_NT_STORES_LDS
 #define SCONV_GATHER_NT_STORES_LDS 1  // streaming stores for the 1 KB runs
 #endif
+// Neighbouring slots' windows overlap, so source rows are read again
+// through L2: streaming reads measured 25% slower (4.9 -> 6.1 us on the
+// 512-slot spec-decode extraction).
+#ifndef SCONV_GATHER_NT_LOADS
+#define SCONV_GATHER_NT_LOADS 0  // streaming reads of the source rows
+#endif
 
 
 namespace sconv {
@@ -73,7 +79,11 @@ __global__ __launch_bounds__(256) void gather_window_kernel(const GatherParams p
     row = row < 0 ? 0 : (row > p.seq_len - 1 ? p.seq_len - 1 : row);
     Pack<D, VEC> pk;
     if constexpr (VEC > 1) {
+#if SCONV_GATHER_NT_LOADS
+      pk.load_nt(src + row * p.src_ss + c0);
+#else
       pk.load(src + row * p.src_ss + c0);
+#endif
     } else {
       pk.raw = __builtin_bit_cast(typename Pack<D, 1>::raw_t, src[row * p.src_ss + (int64_t)c0 * p.src_sc]);
     }
@@ -173,14 +183,20 @@ struct SsmGatherParams {
   int32_t max_count, threads;
 };
 
+// Measured on the 96-slot, 2 MiB-row extraction: 2 units per thread with
+// streaming reads 67 us (6.0 TB/s); 4 units 71 us, 1 unit 69 us, ordinary
+// reads 3-5% slower, 8 units 103 us.
 #ifndef SCONV_SSM_GATHER_UNROLL
-#define SCONV_SSM_GATHER_UNROLL 4  // units of T per thread
+#define SCONV_SSM_GATHER_UNROLL 2  // units of T per thread
+#endif
+#ifndef SCONV_SSM_GATHER_NT_LOADS
+#define SCONV_SSM_GATHER_NT_LOADS 1  // streaming reads of the source rows (read once)
 #endif
 
 // One workgroup per (column block, slot): the live count and the slot's
 // source row are fetched in one round trip, dead slots leave at once, and
 // live ones copy U units of T per thread (T = 16 bytes when the rows allow
-// it), with streaming stores.
+// it), with streaming reads and stores.
 template <typename T, int U>
 __global__ __launch_bounds__(256) void gather_ssm_kernel(const SsmGatherParams p) {
   const int slot = (int)blockIdx.y;  // grid: (column blocks, max_count)
@@ -198,7 +214,11 @@ __global__ __launch_bounds__(256) void gather_ssm_kernel(const SsmGatherParams p
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t i = base + (int64_t)u * p.threads;
+#if SCONV_SSM_GATHER_NT_LOADS
+    if (i < p.nvec) v[u] = __builtin_nontemporal_load(src + i);
+#else
     if (i < p.nvec) v[u] = src[i];
+#endif
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
