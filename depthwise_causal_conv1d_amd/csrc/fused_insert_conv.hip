@@ -60,6 +60,8 @@ struct FusedParams {
   uint32_t n_magic, n_s1, n_s2;
   int32_t num_reqs;         // with qsl
   int32_t nt_x;             // host choice: streaming input loads (one wave generation)
+  int32_t guess;            // host choice: kQslGuess (row t's request guessed as t / k)
+  uint32_t k_magic, k_s1, k_s2;  // division by k = rows per request (same scheme as N)
   int32_t bt_pref;          // block-table entries of row t read ahead (kQslGuess; 0: off)
   int32_t nt_hist;          // host choice: streaming history loads (one-row tiles)
   void* cache;
@@ -96,9 +98,13 @@ __device__ __forceinline__ int32_t find_request(const int32_t* off, int32_t n, i
   return uniform(base);
 }
 
+__device__ __forceinline__ uint32_t div_magic(uint32_t v, uint32_t magic, uint32_t s1,
+                                              uint32_t s2) {
+  const uint32_t t = __umulhi(v, magic);
+  return (t + ((v - t) >> s1)) >> s2;
+}
 __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
-  const uint32_t t = __umulhi(v, p.n_magic);
-  return (t + ((v - t) >> p.n_s1)) >> p.n_s2;
+  return div_magic(v, p.n_magic, p.n_s1, p.n_s2);
 }
 
 // Build-time tuning knobs (defaults chosen by measurement on MI355X).
@@ -146,15 +152,18 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 constexpr int kQslOff = 0;   // the per-row seq_idx / query_start buffers
 constexpr int kQslRegs = 1;  // the offsets qsl, read whole into registers
 constexpr int kQslSearch = 2;  // the offsets qsl, searched in device memory
-// For one-row tiles of launches with no more rows than requests (decode,
-// where row t is usually request t): the guess r = t is checked against
-// offsets t and t+1, read with the row's other metadata, and block-table
-// row t is read at the same time, so a row that is request t has its
-// request and its history blocks one dependent round trip earlier.  A row
-// that is not searches device memory and looks its blocks up there.
+// For launches whose requests have the same small number k of rows (decode:
+// k = 1; speculative decode: k = drafts): row t's request is guessed as
+// g = t / k and checked against offsets g and g+1, read with the row's
+// other metadata; a row that fails the check searches device memory.  One-
+// row tiles with k = 1 also read block-table row t at the same time, so a
+// row that is request t has its history blocks one dependent round trip
+// earlier.
 constexpr int kQslGuess = 3;
 // Entries of row t read ahead: four 256-byte loads per wave.
 constexpr int kBtRowMax = 256;
+// Largest rows-per-request count that takes the guess.
+constexpr int kGuessMaxRows = 8;
 #ifndef SCONV_FUSED_QSL_REG_MAX
 #define SCONV_FUSED_QSL_REG_MAX 512
 #endif
@@ -186,8 +195,9 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     asm volatile("" ::"s"(p.num_streams), "s"(p.st[1].slab0), "s"(p.st[2].slab0),
                  "s"(p.st[3].slab0));
   constexpr bool kGuess = QM == kQslGuess;
-  static_assert(!kGuess || BT == 1, "request guess for one-row tiles only");
-  if constexpr (kGuess) asm volatile("" ::"s"(p.bt), "s"(p.bt_rs), "s"(p.bt_pref));
+  constexpr bool kRowAhead = kGuess && BT == 1;  // block-table row read ahead
+  if constexpr (kGuess) asm volatile("" ::"s"(p.k_magic), "s"(p.k_s1), "s"(p.k_s2));
+  if constexpr (kRowAhead) asm volatile("" ::"s"(p.bt), "s"(p.bt_rs), "s"(p.bt_pref));
   const int lane = threadIdx.x & 63;
   // The launch geometry comes in the parameters (loaded with them in one
   // batch) rather than from the implicit arguments, which would cost a
@@ -250,10 +260,12 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     const int64_t t = t0 + r < t_last ? t0 + r : t_last;
     const int32_t* src;
     if constexpr (kGuess) {
-      // offsets t and t+1 (t clamped below num_reqs: both exist)
-      const int64_t tq = t < (int64_t)p.num_reqs - 1 ? t : p.num_reqs - 1;
+      // offsets g and g+1 of the row's guessed request (clamped below
+      // num_reqs: both exist)
+      const int32_t g = (int32_t)div_magic((uint32_t)t, p.k_magic, p.k_s1, p.k_s2);
+      const int32_t gq = g < p.num_reqs - 1 ? g : p.num_reqs - 1;
       src = f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
-                  : p.qsl + tq + (f == 4);
+                  : p.qsl + gq + (f == 4);
     } else {
       src = f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
                   : (f == 3 ? seq_idx : qstart) + t;
@@ -275,7 +287,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // entry 64*j + L in brow[j] of lane L, bt_pref entries, clamped.
   int32_t brow[4];
   const int32_t row_guess = (int32_t)(t0 < (int64_t)p.num_reqs - 1 ? t0 : p.num_reqs - 1);
-  if constexpr (kGuess) {
+  if constexpr (kRowAhead) {
     const int32_t* row = btab + (int64_t)row_guess * p.bt_rs;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -378,21 +390,27 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     }
   }
   if constexpr (kGuess) {
-    // req / qs hold offsets t and t+1.  Row t is request t exactly when
-    // off[t] <= t < off[t+1] (offsets are non-decreasing, so no later
-    // request starts at or before t); otherwise (empty or multi-row
-    // requests before it, rows past the last offset) a live row searches.
-    const int32_t t = (int32_t)(t0 < t_last ? t0 : t_last);
-    const int32_t lo = req[0], hi = qs[0];
-    if (t == row_guess && lo <= t && t < hi) {
-      req[0] = t;
-      qs[0] = lo;
-    } else if (slot[0] >= 0) {
-      req[0] = find_request(p.qsl, p.num_reqs, t, lane);
-      qs[0] = uniform(p.qsl[req[0]]);
-    } else {
-      req[0] = 0;
-      qs[0] = 0;
+    // req / qs hold offsets g and g+1 of each row's guess g.  Row t lies in
+    // request g exactly when off[g] <= t < off[g+1] (offsets are non-
+    // decreasing, so no later request starts at or before t); otherwise
+    // (empty or longer requests before it, rows past the last offset) a
+    // live row searches device memory.
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      const int32_t t = (int32_t)(t0 + i < t_last ? t0 + i : t_last);
+      const int32_t g = (int32_t)div_magic((uint32_t)t, p.k_magic, p.k_s1, p.k_s2);
+      const int32_t gq = g < p.num_reqs - 1 ? g : p.num_reqs - 1;
+      const int32_t lo = req[i], hi = qs[i];
+      if (lo <= t && t < hi) {
+        req[i] = gq;
+        qs[i] = lo;
+      } else if (slot[i] >= 0) {
+        req[i] = find_request(p.qsl, p.num_reqs, t, lane);
+        qs[i] = uniform(p.qsl[req[i]]);
+      } else {
+        req[i] = 0;
+        qs[i] = 0;
+      }
     }
   }
   if constexpr (QM == kQslRegs) {
@@ -600,7 +618,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
       }
       // History row 1 has the largest block index of the W-1.
       bool in_regs = false;
-      if constexpr (kGuess) in_regs = req[i] == row_guess && hlb[0] < (uint32_t)p.bt_pref;
+      if constexpr (kRowAhead) in_regs = req[i] == row_guess && hlb[0] < (uint32_t)p.bt_pref;
       if (in_regs) {
 #pragma unroll
         for (int m = 1; m <= W - 1; ++m) {
@@ -694,8 +712,8 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
 
 template <typename D, int VEC, int W, int BT, bool NTX, bool MS, bool NTH = false>
 static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
-  if constexpr (BT == 1 && W > 1) {
-    if (p.bt_pref > 0) {
+  if constexpr (W > 1) {
+    if (p.guess) {
       hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslGuess, NTX, MS, NTH>),
                          dim3(grid), dim3(threads), 0, s, p);
       return;
@@ -777,6 +795,23 @@ static int pick_bt(int64_t T, int64_t slabs) {
 }  // namespace sconv
 
 namespace sconv {
+
+// Parameters of the branch-free division by d used by div_magic:
+// q = (t + ((v - t) >> s1)) >> s2 with t = mulhi(v, magic) (Granlund &
+// Montgomery, round-up variant; exact for every uint32 v).  d = 1: (0, 0,
+// 0); d = 2^k: (1, 1, k-1); otherwise the magic number.
+static void magic_for(uint32_t d, uint32_t& magic, uint32_t& s1, uint32_t& s2) {
+  if (d == 1) {
+    magic = 0; s1 = 0; s2 = 0;
+  } else if ((d & (d - 1)) == 0) {
+    magic = 1; s1 = 1; s2 = (uint32_t)__builtin_ctz(d) - 1;
+  } else {
+    const uint32_t l = 32 - __builtin_clz(d - 1);  // ceil(log2 d)
+    magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+    s1 = 1;
+    s2 = l - 1;
+  }
+}
 
 // Shared launcher of both entry points: per-row metadata (seq_idx,
 // query_start) or request offsets (qsl, num_reqs) searched in the kernel.
@@ -861,16 +896,7 @@ static int fused_launch(
   p.cs0 = cs0; p.cs1 = cs1; p.cs2 = cs2; p.bt_rs = bt_row_stride;
   p.T = T;
   p.N = N;
-  if (N == 1) {
-    p.n_magic = 0; p.n_s1 = 0; p.n_s2 = 0;
-  } else if ((N & (N - 1)) == 0) {
-    p.n_magic = 1; p.n_s1 = 1; p.n_s2 = (uint32_t)__builtin_ctz((unsigned)N) - 1;
-  } else {
-    const uint32_t l = 32 - __builtin_clz((unsigned)(N - 1));  // ceil(log2 N)
-    p.n_magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - N)) / N + 1);
-    p.n_s1 = 1;
-    p.n_s2 = l - 1;
-  }
+  magic_for(N, p.n_magic, p.n_s1, p.n_s2);
   p.num_streams = num_streams;
   int64_t slabs = 0;
   for (int s = 0; s < num_streams; ++s) {
@@ -888,9 +914,19 @@ static int fused_launch(
   p.num_slabs = (int32_t)slabs;
   const int bt = pick_bt(T, p.num_slabs);
   p.num_tiles = cdiv(T, bt);
-  // Decode-shaped launches (one-row tiles, no more rows than requests)
-  // guess that row t is request t.
-  p.bt_pref = (SCONV_FUSED_BT_ROW && qsl && bt == 1 && W > 1 && T <= num_reqs)
+  // Decode-shaped launches, where every request has the same small number
+  // k of rows (k = 1 when there are no more rows than requests), guess row
+  // t's request as t / k.  Larger k are prefill shapes: a coincidental
+  // multiple would send most rows to the device-memory search.
+  // (Only the folded forms have request offsets; they were checked above
+  // to have num_reqs >= 1.)
+  const bool folded = qsl != nullptr && num_reqs >= 1;
+  const int64_t k = !folded || T <= num_reqs ? 1 : T / num_reqs;
+  p.guess = SCONV_FUSED_BT_ROW && folded && W > 1 && k <= kGuessMaxRows &&
+            (T <= num_reqs || T % num_reqs == 0);
+  magic_for((uint32_t)(k > 0 ? k : 1), p.k_magic, p.k_s1, p.k_s2);
+  // One-row tiles with one row per request also read block-table row t.
+  p.bt_pref = (p.guess && bt == 1 && k == 1)
                   ? (max_blocks < kBtRowMax ? max_blocks : kBtRowMax)
                   : 0;
 
