@@ -199,3 +199,88 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+_HOST_PATHS = r'''
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from depthwise_causal_conv1d_amd import _lib
+from depthwise_causal_conv1d_amd._lib import StreamT
+lib = _lib.load()
+arena = (ctypes.c_uint8 * (64 << 20))()
+base = (ctypes.addressof(arena) + 4095) & ~4095
+nxt = [base]
+def buf(nbytes):  # distinct, 4 KiB-aligned host regions: never dereferenced here
+    p = nxt[0]; nxt[0] += (nbytes + 4095) & ~4095; return p
+results = []
+def expect(name, rc):
+    results.append((name, rc))
+for dt, es in ((0, 4), (1, 2)):
+    for H, ws, D, T, R in ((4, 32, 128, 64, 64), (4, 32, 128, 64, 16), (4, 32, 128, 60, 17),
+                           (2, 6, 16, 40, 3), (32, 128, 512, 20000, 16)):
+        C = H * ws
+        x, w, out = buf(T * C * es), buf(C * 4 * es), buf(T * C * es)
+        cache = buf(64 * H * 16 * D * es)
+        pos, sm, bt = buf(T * 8), buf(T * 8), buf(R * 300 * 4)
+        si, qs, qsl = buf(T * 4), buf(T * 4), buf((R + 1) * 4)
+        expect(f"fused dt{dt} T{T} R{R}", lib.sconv_fused_insert_conv(
+            x, C, w, 4, 1, cache, 64, H, 16, D, H * 16 * D, 16 * D, D, pos, bt, 300, 300,
+            si, sm, qs, out, C, T, 0, ws, 4, dt, 1, 1, None))
+        expect(f"fused-qsl dt{dt} T{T} R{R}", lib.sconv_fused_insert_conv_qsl(
+            x, C, w, 4, 1, cache, 64, H, 16, D, H * 16 * D, 16 * D, D, pos, bt, 300, 300,
+            qsl, R, sm, out, C, T, 0, ws, 4, dt, 1, 1, None))
+        if D >= 2 * ws:
+            arr = (StreamT * 2)(StreamT(x, C, w, 4, 1, out, C, 0, ws, 1, 1),
+                                StreamT(buf(T * C * es), C, buf(C * 4 * es), 4, 1,
+                                        buf(T * C * es), C, ws, ws, 0, 0))
+            for q in (qsl, None):
+                expect(f"streams dt{dt} T{T} R{R} folded={q is not None}",
+                       lib.sconv_fused_insert_conv_streams(
+                           arr, 2, cache, 64, H, 16, D, H * 16 * D, 16 * D, D, pos, bt, 300, 300,
+                           None if q else si, None if q else qs, q, R, sm, T, 4, dt, None))
+    dim = 64
+    xs, st = buf(dim * 4096 * es), buf(16 * dim * 3 * es)
+    expect(f"varlen dt{dt}", lib.causal_conv1d_varlen_fwd(
+        xs, 4096, 1, buf(dim * 4 * es), 4, 1, buf(dim * es), st, 16, dim * 3, 3, 1, buf(12), 2,
+        buf(8), buf(2), buf(dim * 4096 * es), 4096, 1, dim, 4096, 4, dt, 1, -1, None))
+    for ring in (None, buf(32)):
+        expect(f"update dt{dt} ring={ring is not None}", lib.causal_conv1d_update(
+            buf(8 * dim * es), dim, st, 16, dim * 3, 3, 1, buf(dim * 4 * es), 4, 1, buf(dim * es),
+            ring, buf(32), buf(8 * dim * es), dim, 8, dim, 4, dt, 1, -1, None))
+        expect(f"update_tokens dt{dt} ring={ring is not None}", lib.causal_conv1d_update_tokens(
+            buf(8 * 4 * dim * es), 4 * dim, 1, dim, 4, st, 16, 3, dim * 3, 3, 1,
+            buf(dim * 4 * es), 4, 1, buf(dim * es), ring, buf(32), buf(8 * 4 * dim * es), 4 * dim,
+            1, dim, 8, dim, 4, dt, 1, -1, None))
+    expect(f"gather window dt{dt}", lib.gather_intermediate_conv_window(
+        buf(2048 * dim * es), 2048, dim, dim, 1, buf(512 * 4), buf(4), 512, buf(512 * dim * 3 * es),
+        dim * 3, 3, dt, None))
+    expect(f"gather state dt{dt}", lib.gather_intermediate_ssm_state(
+        buf(8 * 4096 * es), 8, 4096, 4096, buf(8 * 16), buf(4), 16, buf(16 * 4096 * es), 4096, dt,
+        None))
+expect("metadata", lib.sconv_seq_metadata(buf(68), 16, 64, 64, buf(256), 64, buf(256), 64, None))
+for name, rc in results:
+    print(name, rc)
+'''
+
+
+def test_host_paths_reach_the_launch(tmp_path):
+    """Every entry point, with valid host arguments of several shapes
+    (decode-, spec- and prefill-shaped fused launches, folded or not, one
+    and two streams, both dtypes, ring and shift updates), runs its whole
+    host-side set-up and returns SCONV_ERR_HIP from the launch only because
+    no GPU is present.  Runs in a child process so that a host crash fails
+    the test instead of the run; skipped where a GPU is visible, since the
+    buffers are host memory standing in for device pointers."""
+    import subprocess
+    import sys
+
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: these stand-in pointers must not reach a launch")
+    r = subprocess.run([sys.executable, "-c", _HOST_PATHS, ROOT], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, f"host path crashed (exit {r.returncode}): {r.stderr[-2000:]}"
+    lines = [l.rsplit(" ", 1) for l in r.stdout.strip().splitlines()]
+    assert len(lines) >= 40
+    bad = [(n, rc) for n, rc in lines if rc != "3"]
+    assert not bad, f"expected the launch error (3) everywhere, got {bad}"
