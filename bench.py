@@ -60,12 +60,21 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _strip_comments(text: str) -> str:
+    """C/C++ source without its comments, blank lines and trailing blanks
+    (none of these sources has a comment marker inside a string literal)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_digest() -> str:
-    """Hash of the GPU sources, to tell whether stored counters still apply."""
+    """Hash of the GPU sources without their comments, to tell whether
+    stored counters were taken on the kernels as they are now."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + _strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

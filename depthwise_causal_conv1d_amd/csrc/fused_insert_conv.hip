@@ -1,5 +1,5 @@
 // fused_insert_conv.hip -- single-launch insert + depthwise causal conv over
-// a paged cache (one conv stream), for gfx950.
+// a paged cache (one conv stream, or all streams of a layer), for gfx950.
 //
 // Source: vLLM page "vllm.models.inkling.nvidia.ops.sconv", module
 // description and function fused_sconv.  Per row: the input row is copied
@@ -20,9 +20,13 @@
 //     forward / pre-forward decision is a uniform branch;
 //   * the W-1 previous input rows a tap needs stay in the lane's registers:
 //     rows inside the tile are the tile's own loads, rows before the tile
-//     (the halo, at most W-1) are loaded once per tile only when a row of
-//     the tile reads them, and the XCD-contiguous workgroup order puts the
-//     tile that loaded them last in the same L2;
+//     (the halo, at most W-1) come from the previous wave of the workgroup
+//     through LDS, or are loaded once per tile only when a row of the tile
+//     reads them;
+//   * decode-shaped launches (requests of a few rows each) guess each row's
+//     request and check the guess against two offsets, and with one row per
+//     request read the row's block-table row ahead; their history rows,
+//     pieces of 128-byte lines, are loaded as streaming reads;
 //   * fp32 FMA accumulation in VGPRs, SiLU via exp2 + reciprocal, bf16
 //     rounding by v_cvt_pk_bf16_f32 (round to nearest even);
 //   * the grid depends only on T and C, so the decode path replays under a
