@@ -234,6 +234,33 @@ def test_folded_decode_block_row(spec):
     check_fused(case, f"decode-shaped {name}", fold=True)
 
 
+@pytest.mark.parametrize("layout", ["search-one-row-tiles", "guess-k4-mostly-wrong"])
+def test_folded_search_and_failed_guess(layout):
+    """Two folded request-search paths the other shapes rarely reach: more
+    than 512 requests with more rows than requests (not a multiple), so
+    one-row tiles search device memory; and rows a multiple of the requests
+    (k = 4) but uneven request lengths, so the guess t / 4 mostly fails and
+    rows fall back to the search one by one."""
+    rng = np.random.default_rng(91 if layout.startswith("search") else 92)
+    if layout.startswith("search"):
+        R = 600
+        new = [int(v) for v in rng.choice([1, 1, 2], R)]
+        assert sum(new) > R and sum(new) % R != 0
+    else:
+        R = 50
+        new = [int(v) for v in rng.integers(1, 8, R)]
+        while sum(new) != 4 * R:           # adjust to exactly 4 rows per request on average
+            i = int(rng.integers(0, R))
+            if sum(new) > 4 * R and new[i] > 1:
+                new[i] -= 1
+            elif sum(new) < 4 * R and new[i] < 7:
+                new[i] += 1
+    ctx = [int(v) for v in rng.integers(0, 200, R)]
+    case = workloads.fused_case(93, new, ctx, H=4, D=64, ws=32, off_s=16, block_size=16, W=4,
+                                dtype=torch.bfloat16, pad_count=5)
+    check_fused(case, f"folded {layout}", fold=True)
+
+
 def test_folded_table_needs_num_reqs_rows():
     """The folded forms may read any block-table row below num_reqs, so the
     binding refuses a shorter table before launching."""
