@@ -355,14 +355,15 @@ __global__ __launch_bounds__(256) void update_kernel(const UpdateParams p) {
   o.from_float(y);
   o.store(out + (int64_t)b * p.out_rs + c0);
 
-  // Shifted state: window entries 1 .. W-1.
+  // Shifted state: window entries 1 .. W-1 (no state when W = 1; SA is SL
+  // whenever the loop runs).
   const typename P::Elems xe = __builtin_bit_cast(typename P::Elems, xv.raw);
 #pragma unroll
   for (int m = 0; m < SL; ++m) {
     typename P::Elems v;
 #pragma unroll
     for (int q = 0; q < VEC; ++q) {
-      const int flat = m * VEC + q, e = flat / SL, j = flat % SL;
+      const int flat = m * VEC + q, e = flat / SA, j = flat % SA;
       v.e[q] = j + 1 < SL ? elem_at(sv, e * SL + j + 1) : xe.e[e];
     }
     P pk;
