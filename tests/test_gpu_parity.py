@@ -463,6 +463,19 @@ def test_streams_decode_layer():
     check_streams(cases, "decode layer", True, cache_compare="compact")
 
 
+def test_streams_spec_decode_four_row_tiles():
+    """A layer's speculative step in one folded launch: 512 requests x 4
+    drafts over four streams (ws=128 each, D=512), enough waves for
+    four-row tiles, where each tile's rows are checked against the guess
+    t / 4."""
+    g = torch.Generator().manual_seed(94)
+    ctx = [int(v) for v in torch.randint(1, 2000, (512,), generator=g)]
+    cases = workloads.fused_streams_case(94, [4] * 512, ctx, H=8, D=512,
+                                         streams=[(0, 128), (128, 128), (256, 128), (384, 128)],
+                                         block_size=16, W=4, dtype=torch.bfloat16, pad_count=20)
+    check_streams(cases, "spec decode, four streams", True, cache_compare="compact")
+
+
 def test_streams_one_stream_equals_single_entry():
     """A one-stream call gives the same bits as sconv_fused_insert_conv."""
     case = workloads.batched_decode(seed=9)
