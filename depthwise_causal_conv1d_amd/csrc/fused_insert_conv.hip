@@ -612,13 +612,24 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
       // block-table entries come from registers or from one uniform branch
       // of lookups, whose values the history addresses need at once anyway.
       const int32_t first = pos[i] - d;
-      int32_t hblk[kHalo], hoff[kHalo];
+      // Entries read lie in [0, num_blocks): unsigned, so widening one for
+      // the address does not wait on its load the way sign-extension does.
+      uint32_t hblk[kHalo];
+      int32_t hoff[kHalo];
       uint32_t hlb[kHalo];
 #pragma unroll
       for (int m = 1; m <= W - 1; ++m) {
         const int32_t src = first - m >= 0 ? first - m : 0;
         hlb[m - 1] = div_n((uint32_t)src, p);
         hoff[m - 1] = src - (int32_t)hlb[m - 1] * p.N;
+      }
+      // A row this request does not read takes history row 1's place.
+#pragma unroll
+      for (int m = 2; m <= W - 1; ++m) {
+        if (!(m <= W - 1 - d && first - m >= 0)) {
+          hlb[m - 1] = hlb[0];
+          hoff[m - 1] = hoff[0];
+        }
       }
       // History row 1 has the largest block index of the W-1.
       bool in_regs = false;
@@ -633,19 +644,21 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
             const int32_t vj = __builtin_amdgcn_readlane(brow[jj], l);
             v = q == jj ? vj : v;
           }
-          hblk[m - 1] = v;
+          hblk[m - 1] = (uint32_t)v;
         }
       } else {
+        // Scalar loads (the table is read-only for the launch): their wait
+        // counts apart from the vector loads in flight, so the history
+        // loads need not wait for the tile's input rows to land.
+        const __attribute__((address_space(4))) int32_t* bt_c =
+            (const __attribute__((address_space(4))) int32_t*)btab;
 #pragma unroll
         for (int m = 1; m <= W - 1; ++m)
-          hblk[m - 1] = btab[(int64_t)req[i] * p.bt_rs + hlb[m - 1]];
-      }
-#pragma unroll
-      for (int m = 2; m <= W - 1; ++m) {
-        if (!(m <= W - 1 - d && first - m >= 0)) {
-          hblk[m - 1] = hblk[0];
-          hoff[m - 1] = hoff[0];
-        }
+          hblk[m - 1] = (uint32_t)bt_c[(int64_t)req[i] * p.bt_rs + hlb[m - 1]];
+        // All lookups in flight before any of them is used (the scheduler
+        // would otherwise start on the first one's address arithmetic and
+        // wait for it before issuing the next).
+        __builtin_amdgcn_sched_barrier(0);
       }
       auto fetch = [&](int m, P& dst) {
         const S* src = cache + (int64_t)hblk[m - 1] * p.cs0 + (int64_t)hoff[m - 1] * p.cs2 + (on ? lane_off : 0);
