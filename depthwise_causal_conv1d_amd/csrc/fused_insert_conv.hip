@@ -266,8 +266,8 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     if constexpr (kGuess) {
       // offsets g and g+1 of the row's guessed request (clamped below
       // num_reqs: both exist)
-      const int32_t g = (int32_t)div_magic((uint32_t)t, p.k_magic, p.k_s1, p.k_s2);
-      const int32_t gq = g < p.num_reqs - 1 ? g : p.num_reqs - 1;
+      const int32_t gr = (int32_t)div_magic((uint32_t)t, p.k_magic, p.k_s1, p.k_s2);
+      const int32_t gq = gr < p.num_reqs - 1 ? gr : p.num_reqs - 1;
       src = f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
                   : p.qsl + gq + (f == 4);
     } else {
@@ -424,21 +424,21 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     // popcount.  A tile whose first and last rows count the same lies in
     // one request.
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j * 64 + lane >= p.num_reqs) ov[j] = INT32_MAX;
-    auto count_le = [&](int32_t t) -> int32_t {
+    for (int run = 0; run < 8; ++run)
+      if (run * 64 + lane >= p.num_reqs) ov[run] = INT32_MAX;
+    auto count_le = [&](int32_t row) -> int32_t {
       int32_t c = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c += (int32_t)__popcll(__ballot(ov[j] <= t));
+      for (int run = 0; run < 8; ++run) c += (int32_t)__popcll(__ballot(ov[run] <= row));
       return c;
     };
     auto offset_of = [&](int32_t r) -> int32_t {
-      const int32_t l = r & 63, j = r >> 6;
+      const int32_t l = r & 63, run = r >> 6;
       int32_t v = __builtin_amdgcn_readlane(ov[0], l);
 #pragma unroll
       for (int q = 1; q < 8; ++q) {
         const int32_t vq = __builtin_amdgcn_readlane(ov[q], l);
-        v = j == q ? vq : v;
+        v = run == q ? vq : v;
       }
       return v;
     };
