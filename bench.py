@@ -108,6 +108,7 @@ def fused_algorithmic_bytes(case, rows=None) -> int:
     live = sm[lo:hi] >= 0
     n_live = int(live.sum())
     need = live.copy()
+    before = set()  # rows ahead of the range read as same-forward taps
     taps = 0
     bt_entries = 0
     for r in range(case.num_reqs):
@@ -124,12 +125,15 @@ def fused_algorithmic_bytes(case, rows=None) -> int:
                 if src < 0:
                     continue
                 if t - lag >= int(qsl[r]):
-                    need[t - lag - lo] = True
+                    if t - lag >= lo:
+                        need[t - lag - lo] = True
+                    else:
+                        before.add(t - lag)
                 elif src < first:
                     tapped.add(src)
         taps += len(tapped)
         bt_entries += len({p // N for p in tapped})
-    x_rows = int(need.sum())
+    x_rows = int(need.sum()) + len(before)
     return (x_rows + taps + 2 * n_live) * C * e + C * W * e + 24 * (hi - lo) + 4 * bt_entries
 
 
