@@ -146,14 +146,19 @@ int sconv_fused_insert_conv(const void* x, int64_t x_row_stride,
  *
  * Each non-PAD row t belongs to the last request r with qsl[r] <= t (rows
  * past qsl[num_reqs] clamp to the last request), and query_start = qsl[r].
- * Up to 512 requests the offsets are read whole into registers; larger
- * batches are searched in device memory once per row tile.  A launch with
- * no more rows than requests (decode) first checks whether row t is
- * request t (qsl[t] <= t < qsl[t+1]) and, for the rows that are, takes
- * their block-table entries from row t of block_table, read in advance
- * (the first min(max_blocks, 256) entries of that row: every row
- * [0, num_reqs) of block_table must be readable).  The launch allocates
- * nothing.
+ * How the launch finds r (the result is the same either way):
+ *   - When every request may hold the same k <= 8 rows (T <= num_reqs,
+ *     k = 1; or T a multiple of num_reqs, k = T / num_reqs) and W > 1, row
+ *     t first tries request g = t / k, kept when qsl[g] <= t < qsl[g+1].
+ *     With k = 1 (decode) and one-row tiles, the rows that keep it take
+ *     their block-table entries from row t of block_table, read in
+ *     advance (its first min(max_blocks, 256) entries: every row
+ *     [0, num_reqs) of block_table must be readable).
+ *     A row that misses its guess searches the offsets in device memory.
+ *   - Other launches read the offsets whole into registers up to 512
+ *     requests, and above that search them in device memory once per row
+ *     tile.
+ * The launch allocates nothing.
  *
  * Errors: as sconv_fused_insert_conv, plus SCONV_ERR_INVALID for
  * num_reqs < 1 (or a NULL query_start_loc) with T > 0.
