@@ -820,6 +820,12 @@ def main():
                     help="run one plain device copy of this many MiB first (a known-size "
                          "reference for hardware byte counters)")
     args = ap.parse_args()
+    if args.steps is not None and args.steps < 1:
+        ap.error("--steps must be at least 1")
+    if args.warmup is not None and args.warmup < 0:
+        ap.error("--warmup must be non-negative")
+    if args.requests < 1:
+        ap.error("--requests must be at least 1")
     if args.gpus != 1:
         print("bench.py measures one GPU only: libsconv has no multi-GPU path "
               "(the op shards per request or per head with no exchange); run with --gpus 1.",

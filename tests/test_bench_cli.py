@@ -15,3 +15,11 @@ def test_several_gpus_are_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_bad_step_counts_are_refused():
+    for argv in (["--steps", "0"], ["--warmup", "-1"], ["--requests", "0"]):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + argv,
+                           capture_output=True, text=True, timeout=120, cwd=ROOT)
+        assert r.returncode == 2, argv
+        assert "must be" in r.stderr and r.stdout.strip() == ""
