@@ -75,6 +75,9 @@ def _fused_checks(x, weight, cache, positions, block_table, slot_mapping, off_s,
     T = x.shape[0]
     if x.dim() != 2 or weight.dim() != 2 or cache.dim() != 4 or block_table.dim() != 2:
         raise ValueError("x [T, C], weight [C, W], cache [nb, H, N, D], block_table [R, M]")
+    if block_table.shape[1] > 1 and block_table.stride(1) != 1:
+        # the C ABI takes a row stride only: entries of a row are contiguous
+        raise ValueError("block_table needs contiguous entries within a row")
     _dev(x, weight, cache, positions, block_table, slot_mapping, out)
     dt = _dtype(x)
     if weight.dtype != x.dtype or cache.dtype != x.dtype or out.dtype != x.dtype:

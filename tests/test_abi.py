@@ -201,6 +201,28 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
         _lib.load()
 
 
+def test_binding_rejects_strided_block_table_entries():
+    """The C ABI takes one row stride for block_table, so the binding refuses
+    a view whose entries within a row are not contiguous (checked before
+    anything touches a device)."""
+    import torch
+
+    import depthwise_causal_conv1d_amd as sc
+    T, H, ws, N, D, W = 4, 2, 8, 4, 16, 4
+    x = torch.zeros(T, H * ws)
+    w = torch.zeros(H * ws, W)
+    cache = torch.zeros(8, H, N, D)
+    pos = torch.arange(T, dtype=torch.int64)
+    sm = torch.arange(T, dtype=torch.int64)
+    bt = torch.zeros(1, 8, dtype=torch.int32)[:, ::2]  # stride(1) == 2
+    meta = torch.zeros(T, dtype=torch.int32)
+    with pytest.raises(ValueError, match="contiguous entries"):
+        sc.sconv_fused_insert_conv(x, w, cache, pos, bt, meta, sm, meta, 0, ws, N)
+    with pytest.raises(ValueError, match="contiguous entries"):
+        sc.sconv_fused_insert_conv_qsl(x, w, cache, pos, bt, torch.tensor([0, T], dtype=torch.int32),
+                                       1, sm, 0, ws, N)
+
+
 _HOST_PATHS = r'''
 import ctypes, sys
 sys.path.insert(0, sys.argv[1])
