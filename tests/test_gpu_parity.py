@@ -111,6 +111,11 @@ SWEEP = [
     ("n32-w2", torch.bfloat16, 2, 8, 16, 64, 32, 32, [20, 1, 3], [100, 31, 0], 2, 4, "silu", True),
     ("w1", torch.float32, 1, 2, 8, 16, 8, 16, [7, 3], [9, 0], 1, 0, "silu", True),
     ("w3-f32", torch.float32, 3, 4, 4, 12, 4, 4, [11, 2, 5], [0, 7, 3], 2, 1, "silu", True),
+    # minimal launches: one row with a history, one row at position 0, and
+    # every row PAD (nothing may be written)
+    ("single-row", torch.bfloat16, 4, 4, 16, 48, 16, 16, [1], [37], 0, 0, "silu", True),
+    ("single-row-pos0", torch.bfloat16, 4, 2, 8, 16, 0, 16, [1], [0], 0, 0, "silu", True),
+    ("all-pad", torch.float32, 4, 2, 8, 16, 8, 16, [3, 5], [4, 0], 8, 2, "silu", True),
 ]
 
 
