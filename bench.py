@@ -173,24 +173,10 @@ def _bt_bytes(case, rows=None) -> int:
     return 4 * n
 
 
-def sub_case(case, rows, reqs, poison):
+def sub_case(case, rows, reqs, poison=None):
     """The requests `reqs` (rows `rows`) of a multi-batch case as a case of
     their own, for the oracle."""
-    import torch
-
-    import workloads
-    bt = case.block_table[reqs]
-    u = torch.unique(bt.long())
-    if not (u == poison).any():
-        u = torch.cat([u, torch.tensor([poison])])
-    qsl = case.query_start_loc[reqs.start:reqs.stop + 1] - case.query_start_loc[reqs.start]
-    return workloads.FusedCase(**{**case.__dict__, "x": case.x[rows],
-                                  "positions": case.positions[rows], "block_table": bt,
-                                  "slot_mapping": case.slot_mapping[rows],
-                                  "query_start_loc": qsl.to(torch.int32),
-                                  "num_reqs": reqs.stop - reqs.start,
-                                  "num_actual": rows.stop - rows.start,
-                                  "used_blocks": torch.sort(u).values})
+    return case.select(rows, reqs)
 
 
 def repeat_until(budget, once):

@@ -17,6 +17,7 @@ from .ops import (
     sconv_fused_insert_conv,
     sconv_fused_insert_conv_qsl,
     sconv_fused_insert_conv_streams,
+    sconv_fused_plan,
     sconv_seq_metadata,
 )
 
@@ -31,5 +32,6 @@ __all__ = [
     "sconv_fused_insert_conv",
     "sconv_fused_insert_conv_qsl",
     "sconv_fused_insert_conv_streams",
+    "sconv_fused_plan",
     "sconv_seq_metadata",
 ]

@@ -26,6 +26,7 @@ EXPORTS = (
     "sconv_fused_insert_conv",
     "sconv_fused_insert_conv_qsl",
     "sconv_fused_insert_conv_streams",
+    "sconv_fused_plan",
     "causal_conv1d_varlen_fwd",
     "causal_conv1d_update",
     "causal_conv1d_update_tokens",
@@ -45,6 +46,14 @@ class StreamT(ctypes.Structure):
                 ("ws", I32), ("activation", I32), ("use_residual", I32)]
 
 
+class FusedPlan(ctypes.Structure):
+    """sconv_fused_plan_t of include/sconv.h (the launch a fused call makes)."""
+    _fields_ = [("lane_elems", I32), ("rows_per_tile", I32), ("request_mode", I32),
+                ("rows_per_request", I32), ("bt_row_entries", I32), ("stream_x_loads", I32),
+                ("stream_hist_loads", I32), ("tile_major", I32), ("wg_threads", I32),
+                ("reserved", I32), ("waves", I64), ("workgroups", I64)]
+
+
 _SIGS = {
     "sconv_seq_metadata": [P, I32, I64, I64, P, I64, P, I64, P],
     "sconv_fused_insert_conv": [P, I64, P, I64, I64, P, I64, I32, I32, I32, I64, I64, I64,
@@ -56,6 +65,9 @@ _SIGS = {
     "sconv_fused_insert_conv_streams": [ctypes.POINTER(StreamT), I32, P, I64, I32, I32, I32,
                                         I64, I64, I64, P, P, I64, I32, P, P, P, I32, P, I64,
                                         I32, I32, P],
+    "sconv_fused_plan": [ctypes.POINTER(StreamT), I32, P, I64, I32, I32, I32, I64, I64, I64,
+                         P, P, I64, I32, P, P, P, I32, P, I64, I32, I32,
+                         ctypes.POINTER(FusedPlan)],
     "causal_conv1d_varlen_fwd": [P, I64, I64, P, I64, I64, P, P, I64, I64, I64, I64, P, I32,
                                  P, P, P, I64, I64, I32, I64, I32, I32, I32, I32, P],
     "causal_conv1d_update": [P, I64, P, I64, I64, I64, I64, P, I64, I64, P, P, P, P, I64,

@@ -152,6 +152,13 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_BT_ROW 1  // one-row tiles of decode-shaped launches guess request t
 #endif
 
+// Wave order of a launch: slab-major (consecutive waves walk consecutive
+// tiles of one slab), except for several streams in one-row tiles, which
+// run tile-major.
+__host__ __device__ constexpr bool slab_major_order(bool multi_stream, int rows_per_tile) {
+  return SCONV_FUSED_SLAB_MAJOR && !(multi_stream && rows_per_tile == 1);
+}
+
 // Where a row's request and request start come from (template QM).
 constexpr int kQslOff = 0;   // the per-row seq_idx / query_start buffers
 constexpr int kQslRegs = 1;  // the offsets qsl, read whole into registers
@@ -224,11 +231,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // slabs of all streams for one row are then neighbours on one XCD, and
   // the streams' pieces of a cache row, which share 128-byte lines, meet
   // in one L2.
-#if SCONV_FUSED_SLAB_MAJOR
-  constexpr bool kSlabMajor = !(MS && BT == 1);
-#else
-  constexpr bool kSlabMajor = false;
-#endif
+  constexpr bool kSlabMajor = slab_major_order(MS, BT);
   uint32_t tile;
   int slab;
   if constexpr (kSlabMajor) {
@@ -832,13 +835,15 @@ static void magic_for(uint32_t d, uint32_t& magic, uint32_t& s1, uint32_t& s2) {
 
 // Shared launcher of both entry points: per-row metadata (seq_idx,
 // query_start) or request offsets (qsl, num_reqs) searched in the kernel.
+// With `plan` non-NULL the launch is only planned: the arguments are
+// checked as for a launch, the plan is filled in and nothing is enqueued.
 static int fused_launch(
     const char* fn, const sconv_stream_t* streams, int32_t num_streams, void* cache,
     int64_t num_blocks, int32_t H, int32_t N, int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
     const int64_t* positions, const int32_t* block_table, int64_t bt_row_stride,
     int32_t max_blocks, const int32_t* seq_idx, const int32_t* query_start, const int32_t* qsl,
     int32_t num_reqs, const int64_t* slot_mapping, int64_t T, int32_t W, int32_t dtype,
-    hipStream_t stream) {
+    hipStream_t stream, sconv_fused_plan_t* plan = nullptr) {
   if (T < 0) return fail(SCONV_ERR_INVALID, "%s: T < 0", fn);
   if (!valid_dtype(dtype)) return fail(SCONV_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
   if (W < 1 || W > 4) return fail(SCONV_ERR_INVALID, "%s: W=%d outside [1, 4]", fn, W);
@@ -879,7 +884,10 @@ static int fused_launch(
           q.x_row_stride % vec16 == 0 && q.out_row_stride % vec16 == 0 && aligned16(q.x) &&
           aligned16(q.out);
   }
-  if (T == 0) return SCONV_OK;
+  if (T == 0) {
+    if (plan) *plan = sconv_fused_plan_t{};
+    return SCONV_OK;
+  }
   if (!cache || !positions || !block_table || !slot_mapping ||
       (qsl ? false : (!seq_idx || !query_start)))
     return fail(SCONV_ERR_INVALID, "%s: NULL pointer", fn);
@@ -942,10 +950,15 @@ static int fused_launch(
   p.guess = SCONV_FUSED_BT_ROW && folded && W > 1 && k <= kGuessMaxRows &&
             (T <= num_reqs || T % num_reqs == 0);
   magic_for((uint32_t)(k > 0 ? k : 1), p.k_magic, p.k_s1, p.k_s2);
-  // One-row tiles with one row per request also read block-table row t.
-  p.bt_pref = (p.guess && bt == 1 && k == 1)
-                  ? (max_blocks < kBtRowMax ? max_blocks : kBtRowMax)
-                  : 0;
+  // Guessed one-row tiles read block-table row t ahead (the kernel's
+  // kRowAhead form): with one row per request all of it that fits in the
+  // lanes' registers; otherwise (k > 1, where row t is rarely the row's
+  // request) its first entry only, so that every entry the kernel reads
+  // lies inside the row.  Every other form reads no row ahead.
+  if (p.guess && bt == 1)
+    p.bt_pref = k == 1 ? (max_blocks < kBtRowMax ? max_blocks : kBtRowMax) : 1;
+  else
+    p.bt_pref = 0;
 
   const int64_t waves = p.num_tiles * p.num_slabs;
   if (waves > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
@@ -969,6 +982,23 @@ static int fused_launch(
   for (int s = 0; s < num_streams; ++s) widest = streams[s].ws > widest ? streams[s].ws : widest;
   p.nt_hist = SCONV_FUSED_NT_HIST && bt == 1 && widest * es < 128;
   p.waves_per_group = (int32_t)(threads / 64);
+
+  if (plan) {
+    plan->lane_elems = VEC;
+    plan->rows_per_tile = bt;
+    plan->request_mode = p.guess ? kQslGuess
+                         : !qsl ? kQslOff
+                         : num_reqs <= kQslRegMax ? kQslRegs : kQslSearch;
+    plan->rows_per_request = (int32_t)(k > 0 ? k : 1);
+    plan->bt_row_entries = p.bt_pref;
+    plan->stream_x_loads = p.nt_x;
+    plan->stream_hist_loads = p.nt_hist;
+    plan->tile_major = !slab_major_order(num_streams > 1, bt);
+    plan->wg_threads = (int32_t)threads;
+    plan->waves = waves;
+    plan->workgroups = grid;
+    return SCONV_OK;
+  }
 
   if (dtype == SCONV_BF16) {
     if (VEC == 8) launch_w<Bf16, 8>(W, bt, p, (uint32_t)grid, threads, stream);
@@ -1047,4 +1077,24 @@ extern "C" int sconv_fused_insert_conv_streams(
                              cs2, positions, block_table, bt_row_stride, max_blocks, seq_idx,
                              query_start, query_start_loc, num_reqs, slot_mapping, T, W, dtype,
                              stream);
+}
+
+extern "C" int sconv_fused_plan(
+    const sconv_stream_t* streams, int32_t num_streams, void* cache, int64_t num_blocks,
+    int32_t H, int32_t N, int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
+    const int64_t* positions, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t max_blocks, const int32_t* seq_idx, const int32_t* query_start,
+    const int32_t* query_start_loc, int32_t num_reqs, const int64_t* slot_mapping, int64_t T,
+    int32_t W, int32_t dtype, sconv_fused_plan_t* plan) {
+  const char* fn = "sconv_fused_plan";
+  sconv::clear_error();
+  if (!plan) return sconv::fail(SCONV_ERR_INVALID, "%s: NULL plan", fn);
+  const bool per_row = seq_idx || query_start;
+  if (per_row == (query_start_loc != nullptr))
+    return sconv::fail(SCONV_ERR_INVALID,
+                       "%s: give either seq_idx and query_start, or query_start_loc", fn);
+  return sconv::fused_launch(fn, streams, num_streams, cache, num_blocks, H, N, D, cs0, cs1,
+                             cs2, positions, block_table, bt_row_stride, max_blocks, seq_idx,
+                             query_start, query_start_loc, num_reqs, slot_mapping, T, W, dtype,
+                             nullptr, plan);
 }

@@ -65,13 +65,16 @@ extern "C" int sconv_seq_metadata(const int32_t* query_start_loc, int32_t num_re
     return fail(SCONV_ERR_INVALID, "sconv_seq_metadata: num_actual_tokens < 0");
   if (num_padded_tokens < num_actual_tokens)
     return fail(SCONV_ERR_INVALID,
-                "sconv_seq_metadata: num_padded_tokens must cover all actual tokens");
+                "sconv_seq_metadata: num_padded_tokens (%lld) is below num_actual_tokens (%lld)",
+                (long long)num_padded_tokens, (long long)num_actual_tokens);
   if (num_padded_tokens > seq_idx_len)
     return fail(SCONV_ERR_INVALID,
-                "sconv_seq_metadata: seq_idx_out is too small for the padded token count");
+                "sconv_seq_metadata: seq_idx_out holds %lld entries, %lld rows requested",
+                (long long)seq_idx_len, (long long)num_padded_tokens);
   if (num_padded_tokens > query_start_len)
     return fail(SCONV_ERR_INVALID,
-                "sconv_seq_metadata: query_start_out is too small for the padded token count");
+                "sconv_seq_metadata: query_start_out holds %lld entries, %lld rows requested",
+                (long long)query_start_len, (long long)num_padded_tokens);
   if (num_actual_tokens > 0 && num_reqs < 1)
     return fail(SCONV_ERR_INVALID, "sconv_seq_metadata: num_reqs < 1 with actual tokens");
   if (num_padded_tokens == 0) return SCONV_OK;

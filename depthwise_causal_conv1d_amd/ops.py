@@ -7,6 +7,7 @@ HIP kernels; there is no CPU path.  Argument names follow the source pages.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import List, Optional, Sequence
 
 import torch
@@ -191,18 +192,56 @@ def sconv_fused_insert_conv_streams(xs: Sequence[torch.Tensor], weights: Sequenc
     ``seq_idx`` / ``query_start`` or, inside the launch, from
     ``query_start_loc`` with ``num_reqs``.  Returns the outputs.
     """
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    args = _streams_args(xs, weights, cache, positions, block_table, slot_mapping, off_s, ws,
+                         block_size, activation, use_residual, seq_idx, query_start,
+                         query_start_loc, num_reqs, outs)
+    if args is None:
+        return list(outs)
+    rc = _lib.load().sconv_fused_insert_conv_streams(*args, _stream(xs[0]))
+    _lib.check(rc, "sconv_fused_insert_conv_streams")
+    return list(outs)
+
+
+def sconv_fused_plan(xs: Sequence[torch.Tensor], weights: Sequence[torch.Tensor],
+                     cache: torch.Tensor, positions: torch.Tensor, block_table: torch.Tensor,
+                     slot_mapping: torch.Tensor, off_s: Sequence[int], ws: Sequence[int],
+                     block_size: int, activation=None, use_residual=True,
+                     seq_idx: Optional[torch.Tensor] = None,
+                     query_start: Optional[torch.Tensor] = None,
+                     query_start_loc: Optional[torch.Tensor] = None,
+                     num_reqs: Optional[int] = None,
+                     outs: Optional[Sequence[torch.Tensor]] = None) -> dict:
+    """The launch sconv_fused_insert_conv_streams would make for these
+    arguments, as a dict of the plan's fields; nothing is launched."""
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    plan = _lib.FusedPlan()
+    args = _streams_args(xs, weights, cache, positions, block_table, slot_mapping, off_s, ws,
+                         block_size, activation, use_residual, seq_idx, query_start,
+                         query_start_loc, num_reqs, outs)
+    if args is not None:
+        rc = _lib.load().sconv_fused_plan(*args, ctypes.byref(plan))
+        _lib.check(rc, "sconv_fused_plan")
+    return {name: getattr(plan, name) for name, _ in _lib.FusedPlan._fields_}
+
+
+def _streams_args(xs, weights, cache, positions, block_table, slot_mapping, off_s, ws,
+                  block_size, activation, use_residual, seq_idx, query_start, query_start_loc,
+                  num_reqs, outs):
+    """Checked C arguments of the multi-stream entry points (without the
+    stream), or None when there is nothing to launch."""
     n = len(xs)
     if not (len(weights) == len(off_s) == len(ws) == n):
         raise ValueError("xs, weights, off_s and ws need one entry per stream")
     acts = list(activation) if isinstance(activation, (list, tuple)) else [activation] * n
     ress = list(use_residual) if isinstance(use_residual, (list, tuple)) else [use_residual] * n
-    if outs is None:
-        outs = [torch.empty_like(x) for x in xs]
     if len(acts) != n or len(ress) != n or len(outs) != n:
         raise ValueError("activation, use_residual and outs need one entry per stream")
     T = xs[0].shape[0] if n else 0
     if n == 0 or T == 0:
-        return list(outs)
+        return None
     if any(x.shape[0] != T for x in xs):
         raise ValueError("every stream needs the same rows T")
     dt = None
@@ -230,14 +269,11 @@ def sconv_fused_insert_conv_streams(xs: Sequence[torch.Tensor], weights: Sequenc
                               o.stride(0), int(off_s[i]), int(ws[i]), _act(acts[i]),
                               int(bool(ress[i])))
     nb, H, N, D = cache.shape
-    rc = _lib.load().sconv_fused_insert_conv_streams(
-        arr, n, _ptr(cache), nb, H, N, D, cache.stride(0), cache.stride(1), cache.stride(2),
-        _ptr(positions), _ptr(block_table), block_table.stride(0), block_table.shape[1],
-        _ptr(seq_idx), _ptr(query_start), _ptr(query_start_loc),
-        int(num_reqs) if num_reqs is not None else 0, _ptr(slot_mapping), T,
-        weights[0].shape[1], dt, _stream(xs[0]))
-    _lib.check(rc, "sconv_fused_insert_conv_streams")
-    return list(outs)
+    return (arr, n, _ptr(cache), nb, H, N, D, cache.stride(0), cache.stride(1), cache.stride(2),
+            _ptr(positions), _ptr(block_table), block_table.stride(0), block_table.shape[1],
+            _ptr(seq_idx), _ptr(query_start), _ptr(query_start_loc),
+            int(num_reqs) if num_reqs is not None else 0, _ptr(slot_mapping), T,
+            weights[0].shape[1], dt)
 
 
 def causal_conv1d_varlen_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],

@@ -236,6 +236,48 @@ int sconv_fused_insert_conv_streams(const sconv_stream_t* streams, int32_t num_s
                                     int32_t dtype, hipStream_t stream);
 
 /*
+ * sconv_fused_plan_t / sconv_fused_plan -- the launch a fused call would
+ * make, without making it.
+ *
+ * For callers that size, tune or check launches ahead of time (and for the
+ * library's own host tests): sconv_fused_plan takes exactly the arguments of
+ * sconv_fused_insert_conv_streams (without the stream), runs the same host
+ * checks with the same error codes, and on success fills *plan with the
+ * kernel configuration and grid that call would enqueue.  Nothing is
+ * launched and no pointer is dereferenced, so stand-in addresses of the
+ * right alignment suffice.  The single-stream entry points plan like one
+ * stream of it (sconv_fused_insert_conv: seq_idx and query_start;
+ * sconv_fused_insert_conv_qsl: query_start_loc).  T == 0 gives an all-zero
+ * plan (nothing to launch).
+ */
+typedef struct sconv_fused_plan {
+  int32_t lane_elems;        /* channels per lane: 16 bytes' worth, or 1 */
+  int32_t rows_per_tile;     /* consecutive rows of one wave's tile */
+  int32_t request_mode;      /* 0 per-row buffers, 1 offsets in registers,
+                                2 device-memory search, 3 request guess */
+  int32_t rows_per_request;  /* rows per request the guess assumes */
+  int32_t bt_row_entries;    /* block-table entries of the guessed row read
+                                ahead per wave (0: none); >= 1 whenever
+                                request_mode == 3 and rows_per_tile == 1 */
+  int32_t stream_x_loads;    /* input rows loaded as streaming reads */
+  int32_t stream_hist_loads; /* history rows loaded as streaming reads */
+  int32_t tile_major;        /* wave order: 0 slab-major, 1 tile-major */
+  int32_t wg_threads;        /* workgroup size */
+  int32_t reserved;
+  int64_t waves;             /* tiles x slabs */
+  int64_t workgroups;        /* grid size */
+} sconv_fused_plan_t;
+
+int sconv_fused_plan(const sconv_stream_t* streams, int32_t num_streams, void* cache,
+                     int64_t num_blocks, int32_t H, int32_t N, int32_t D, int64_t cs0,
+                     int64_t cs1, int64_t cs2, const int64_t* positions,
+                     const int32_t* block_table, int64_t bt_row_stride, int32_t max_blocks,
+                     const int32_t* seq_idx, const int32_t* query_start,
+                     const int32_t* query_start_loc, int32_t num_reqs,
+                     const int64_t* slot_mapping, int64_t T, int32_t W, int32_t dtype,
+                     sconv_fused_plan_t* plan);
+
+/*
  * causal_conv1d_varlen_fwd -- causal depthwise conv over packed
  * variable-length sequences, with a slot-indexed state pool.
  *

@@ -105,3 +105,12 @@ def dtype_name(t: torch.dtype) -> str:
 
 def live_rows(case) -> np.ndarray:
     return to_np(case.slot_mapping) >= 0
+
+
+def written_cache_values(cache: np.ndarray, slot_mapping: np.ndarray, block_size: int,
+                         off_s: int, ws: int) -> np.ndarray:
+    """The cache columns [off_s, off_s + ws) of every head at the slots of
+    the non-PAD rows: what an insert writes."""
+    sm = np.asarray(slot_mapping)
+    live = sm[sm >= 0]
+    return cache[live // block_size, :, live % block_size, off_s:off_s + ws]

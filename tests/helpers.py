@@ -61,17 +61,37 @@ TOL = {
 
 
 def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "", mask=None):
+    """Every compared value finite on both sides and within the dtype's
+    tolerance.  Live outputs come from finite inputs, so a NaN or an
+    infinity on either side is a failure: the generators fill every cache
+    and state position an op must not read with NaN, and a stray read must
+    not pass by showing up on both sides."""
     g, r = as_float(got), as_float(ref)
     if mask is not None:
         g, r = g[mask], r[mask]
     tol = TOL[dtype]
     assert g.shape == r.shape, (what, g.shape, r.shape)
-    both_nan = np.isnan(g) & np.isnan(r)
+    for side, v in (("got", g), ("reference", r)):
+        nf = ~np.isfinite(v)
+        if nf.any():
+            i = np.flatnonzero(nf)[0]
+            raise AssertionError(f"{what}: {int(nf.sum())}/{v.size} non-finite values in the "
+                                 f"{side} side; first flat index {i}: {v.flat[i]!r}")
     err = np.abs(g - r)
     lim = tol["atol"] + tol["rtol"] * np.abs(r)
-    bad = ~(both_nan | (err <= lim))
+    bad = ~(err <= lim)
     if bad.any():
         i = np.flatnonzero(bad)[0]
         raise AssertionError(
             f"{what}: {int(bad.sum())}/{bad.size} outside atol={tol['atol']} rtol={tol['rtol']}; "
             f"first flat index {i}: got {g.flat[i]!r} want {r.flat[i]!r}")
+
+
+def assert_finite(a: np.ndarray, what: str = ""):
+    """Values (float32/float64 or bf16 bits) are all finite."""
+    v = as_float(np.asarray(a)) if np.asarray(a).dtype != np.float64 else np.asarray(a)
+    nf = ~np.isfinite(v)
+    if nf.any():
+        i = np.flatnonzero(nf)[0]
+        raise AssertionError(f"{what}: {int(nf.sum())}/{v.size} non-finite values; first flat "
+                             f"index {i}: {v.flat[i]!r}")

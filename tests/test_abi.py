@@ -51,11 +51,11 @@ NULL = None
 
 def test_metadata_rejects_bad_scalars(lib):
     rc = lib.sconv_seq_metadata(NULL, 1, 10, 5, NULL, 10, NULL, 10, NULL)
-    assert rc == 1 and b"cover" in lib.sconv_last_error()
+    assert rc == 1 and b"is below num_actual_tokens" in lib.sconv_last_error()
     rc = lib.sconv_seq_metadata(NULL, 1, 4, 8, NULL, 7, NULL, 8, NULL)
-    assert rc == 1 and b"seq_idx_out is too small" in lib.sconv_last_error()
+    assert rc == 1 and b"seq_idx_out holds 7 entries, 8 rows" in lib.sconv_last_error()
     rc = lib.sconv_seq_metadata(NULL, 1, 4, 8, NULL, 8, NULL, 6, NULL)
-    assert rc == 1 and b"query_start_out is too small" in lib.sconv_last_error()
+    assert rc == 1 and b"query_start_out holds 6 entries, 8 rows" in lib.sconv_last_error()
     rc = lib.sconv_seq_metadata(NULL, 0, 4, 8, NULL, 8, NULL, 8, NULL)
     assert rc == 1
     # nothing to do is a success and launches nothing
@@ -306,3 +306,74 @@ def test_host_paths_reach_the_launch(tmp_path):
     assert len(lines) >= 40
     bad = [(n, rc) for n, rc in lines if rc != "3"]
     assert not bad, f"expected the launch error (3) everywhere, got {bad}"
+
+
+def _plan(lib, T, num_reqs, H=32, ws=32, D=128, N=16, max_blocks=257, folded=True, W=4,
+          streams=1, dt=1):
+    """sconv_fused_plan on stand-in host addresses (16-byte aligned, never
+    dereferenced): returns (rc, plan)."""
+    from depthwise_causal_conv1d_amd import _lib
+    es = 2 if dt == 1 else 4
+    C = H * ws
+    big = (ctypes.c_uint8 * (1 << 16))()
+    base = (ctypes.addressof(big) + 15) & ~15
+    # x, out of each stream and the cache at distant stand-in addresses
+    arr = (_lib.StreamT * streams)()
+    for s in range(streams):
+        arr[s] = _lib.StreamT(base + (s + 1) * (1 << 40), C, base, W, 1,
+                              base + (s + 1) * (1 << 40) + (1 << 39), C, s * ws, ws, 1, 1)
+    cache = base + (1 << 44)
+    plan = _lib.FusedPlan()
+    meta = (None, None, base, num_reqs) if folded else (base, base, None, 0)
+    rc = lib.sconv_fused_plan(arr, streams, cache, 1 << 16, H, N, D, H * N * D, N * D, D, base,
+                              base, max_blocks, max_blocks, *meta, base, T, W, dt,
+                              ctypes.byref(plan))
+    return rc, plan
+
+
+def test_plan_guessed_one_row_tiles_read_inside_the_table(lib):
+    """Guessed one-row tiles read block-table row t ahead in the kernel; the
+    plan must give them at least one entry (an empty read-ahead would index
+    the entry before the row) and never more than the row holds."""
+    cases = []
+    for T, R in [(256, 256), (48, 48), (200, 50), (64, 16), (120, 40), (8, 8), (4096, 4096),
+                 (2048, 512), (9, 3)]:
+        for mb in (1, 3, 100, 257, 4097):
+            for H, ws in ((32, 32), (2, 8), (64, 64)):
+                cases.append((T, R, mb, H, ws))
+    seen_guess_row = 0
+    for T, R, mb, H, ws in cases:
+        rc, plan = _plan(lib, T, R, H=H, ws=ws, D=max(ws, 128), max_blocks=mb)
+        assert rc == 0, lib.sconv_last_error()
+        if plan.request_mode == 3 and plan.rows_per_tile == 1:
+            seen_guess_row += 1
+            assert 1 <= plan.bt_row_entries <= min(mb, 256), (T, R, mb, plan.bt_row_entries)
+            if plan.rows_per_request > 1:
+                assert plan.bt_row_entries == 1
+        else:
+            assert plan.bt_row_entries == 0, (T, R, mb)
+    assert seen_guess_row > 20
+
+
+def test_plan_shapes_of_the_benchmarked_launches(lib):
+    """The decode, spec-decode and prefill shapes plan the kernels their
+    tuning chose: one-row guessed tiles reading 256 entries ahead for
+    decode, four-row guessed tiles for speculative decode, four-row tiles
+    with per-row buffers for the prefill; and the per-row form never
+    guesses."""
+    rc, p = _plan(lib, 256, 256)
+    assert rc == 0 and (p.request_mode, p.rows_per_tile, p.bt_row_entries) == (3, 1, 256)
+    assert p.lane_elems == 8 and p.stream_hist_loads == 1 and p.waves == 512
+    rc, p = _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097)
+    assert rc == 0 and (p.request_mode, p.rows_per_tile, p.rows_per_request) == (3, 4, 4)
+    assert p.bt_row_entries == 0 and p.stream_x_loads == 1
+    rc, p = _plan(lib, 20450, 16, H=32, ws=128, D=512, max_blocks=641, folded=False)
+    assert rc == 0 and (p.request_mode, p.rows_per_tile, p.tile_major) == (0, 4, 0)
+    assert p.waves == 8 * ((20450 + 3) // 4) and p.wg_threads == 256
+    rc, p = _plan(lib, 256, 256, folded=False)
+    assert rc == 0 and p.request_mode == 0 and p.bt_row_entries == 0
+    rc, p = _plan(lib, 256, 256, streams=4)
+    assert rc == 0 and p.tile_major == 1 and p.waves == 4 * 256 * 2
+    rc, p = _plan(lib, 0, 1)
+    assert rc == 0 and p.waves == 0 and p.workgroups == 0
+    assert _plan(lib, 10, 2, W=5)[0] == 1 and b"W=5" in lib.sconv_last_error()

@@ -15,8 +15,8 @@ import torch
 
 import workloads
 from tests.gpu_util import (SENTINEL, dtype_name, gpu_fused, gpu_fused_streams, live_rows,
-                            oracle_fused, oracle_fused_streams)
-from tests.helpers import assert_bits_equal, assert_close, to_np
+                            oracle_fused, oracle_fused_streams, written_cache_values)
+from tests.helpers import assert_bits_equal, assert_close, assert_finite, to_np
 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("oracle_lib")]
 
@@ -63,9 +63,9 @@ def test_seq_metadata_errors():
     import depthwise_causal_conv1d_amd as lib
     qsl = torch.tensor([0, 4], dtype=torch.int32, device=DEV)
     buf = torch.zeros(4, dtype=torch.int32, device=DEV)
-    with pytest.raises(ValueError, match="cover"):
+    with pytest.raises(ValueError, match="is below num_actual_tokens"):
         lib.sconv_seq_metadata(qsl, 1, 4, buf, buf.clone(), 3)
-    with pytest.raises(ValueError, match="too small"):
+    with pytest.raises(ValueError, match="holds 3 entries"):
         lib.sconv_seq_metadata(qsl, 1, 4, buf[:3], buf.clone(), 4)
 
 
@@ -76,11 +76,13 @@ def check_fused(case, what, cache_compare="full", fold=False):
     say(f"fused {what}: T={case.T} C={case.C} W={case.W} N={case.block_size} "
         f"dtype={case.x.dtype} off_s={case.off_s} folded={fold}")
     out_g, cache_g, si_g, qs_g = gpu_fused(case, fold=fold)
+    sm_h = to_np(case.slot_mapping)
     if cache_compare == "full":
         out_r, cache_r, si_r, qs_r = oracle_fused(case)
         cache_gh = to_np(cache_g)
     else:  # compact both sides to the referenced blocks
         cc, bt, sm = case.compact()
+        sm_h = to_np(sm)
         out_r, cache_r, si_r, qs_r = oracle_fused(case, cache=cc, block_table=bt, slot_mapping=sm)
         ids = case.used_blocks.to(cache_g.device)
         cache_gh = to_np(cache_g[ids])
@@ -97,6 +99,8 @@ def check_fused(case, what, cache_compare="full", fold=False):
     assert_close(out_gh, out_r, dtype_name(case.x.dtype), f"{what} out", mask=live)
     assert_bits_equal(out_gh[~live], out_r[~live], f"{what} PAD rows untouched")
     assert_bits_equal(cache_gh, cache_r, f"{what} cache")
+    assert_finite(written_cache_values(cache_gh, sm_h, case.block_size, case.off_s, case.ws),
+                  f"{what} inserted cache slots")
     return out_g, cache_g
 
 
@@ -407,6 +411,7 @@ def check_streams(cases, what, fold, cache_compare="full"):
     say(f"streams {what}: {len(cases)} streams T={c0.T} ws={[c.ws for c in cases]} "
         f"off_s={[c.off_s for c in cases]} dtype={c0.x.dtype} folded={fold}")
     outs_g, cache_g = gpu_fused_streams(cases, fold=fold)
+    sm_h = to_np(c0.slot_mapping)
     if cache_compare == "full":
         if what not in _STREAMS_ORACLE:  # the same inputs serve both metadata forms
             _STREAMS_ORACLE[what] = oracle_fused_streams(cases)
@@ -414,6 +419,7 @@ def check_streams(cases, what, fold, cache_compare="full"):
         cache_gh = to_np(cache_g)
     else:
         cc, bt, sm = c0.compact()
+        sm_h = to_np(sm)
         outs_r, cache_r = oracle_fused_streams(cases, cache=cc, block_table=bt, slot_mapping=sm)
         cache_gh = to_np(cache_g[c0.used_blocks.to(cache_g.device)])
     live = live_rows(c0)
@@ -422,6 +428,9 @@ def check_streams(cases, what, fold, cache_compare="full"):
         assert_close(ogh, orf, dtype_name(c0.x.dtype), f"{what} stream {i} out", mask=live)
         assert_bits_equal(ogh[~live], orf[~live], f"{what} stream {i} PAD rows untouched")
     assert_bits_equal(cache_gh, cache_r, f"{what} cache")
+    for c in cases:
+        assert_finite(written_cache_values(cache_gh, sm_h, c0.block_size, c.off_s, c.ws),
+                      f"{what} inserted cache slots, columns {c.off_s}+{c.ws}")
 
 
 STREAM_SPECS = [
@@ -526,7 +535,11 @@ def test_config_mixed_prefill_four_streams():
         assert_close(out_h, out_r, "bf16", f"stream {s}", mask=live)
         assert (out_h[~live] == 0xC442).all()   # bf16 bits of -777
         say(f"  stream {s} ok")
-    assert_bits_equal(to_np(cache_g), cache_r, "shared cache after four streams")
+    cache_h = to_np(cache_g)
+    assert_bits_equal(cache_h, cache_r, "shared cache after four streams")
+    for case in streams:
+        assert_finite(written_cache_values(cache_h, to_np(base.slot_mapping), base.block_size,
+                                           case.off_s, case.ws), f"stream at {case.off_s} inserts")
 
 
 @pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
@@ -604,6 +617,8 @@ def test_graph_replay_folded_decode_layouts():
         assert_close(got, out_r, "bf16", f"{name} out", mask=live)
         assert_bits_equal(got[~live], out_r[~live], f"{name} PAD rows untouched")
         assert_bits_equal(to_np(cache_b), cache_r, f"{name} cache")
+        assert_finite(written_cache_values(to_np(cache_b), to_np(c.slot_mapping), N, 0, ws),
+                      f"{name} inserted cache slots")
         say(f"  replay '{name}' ok")
 
 
@@ -670,6 +685,72 @@ def test_graph_replay_decode_steps(fold):
         assert_close(to_np(out_b), ref_out[rows(s).numpy()], "bf16", f"replay {s}")
         say(f"  replay {s} ok")
     assert_bits_equal(to_np(cache), ref_cache, "cache after replays")
+    assert_finite(written_cache_values(to_np(cache), to_np(case.slot_mapping), case.block_size,
+                                       case.off_s, case.ws), "inserted cache slots")
+
+
+def test_graph_replay_batched_decode_full_size():
+    """The benchmarked decode step at full size, captured once and replayed
+    on three batches written into its buffers in place: 256 requests x 1
+    token, histories uniform in [1, 4096], H=32, D=128, ws=32 (C=1024), N=16,
+    bf16, SiLU and residual, request search folded into the launch.  The
+    three batches own disjoint blocks of one shared pool.  After each replay
+    the outputs equal the oracle within tolerance and every block the batch
+    references equals it bit for bit; after the last, every block no batch
+    references is still NaN poison."""
+    import depthwise_causal_conv1d_amd as lib
+    B, NB = 256, 3
+    full = workloads.batched_decode(device=DEV, num_reqs=B * NB,
+                                    pool_blocks=int(B * NB * 2 * 1.25) + 1)
+    say(f"full-size decode graph: {NB} batches of {B}, pool {full.cache.shape[0]} blocks")
+    cache = full.cache                       # device, shared by the batches
+    x_b = torch.zeros(B, full.C, dtype=torch.bfloat16, device=DEV)
+    pos_b = torch.zeros(B, dtype=torch.int64, device=DEV)
+    sm_b = torch.full((B,), -1, dtype=torch.int64, device=DEV)
+    bt_b = torch.zeros(B, full.block_table.shape[1], dtype=torch.int32, device=DEV)
+    qsl_b = torch.arange(B + 1, dtype=torch.int32, device=DEV)
+    out_b = torch.zeros_like(x_b)
+    w = full.weight.to(DEV)
+
+    def step():
+        lib.sconv_fused_insert_conv_qsl(x_b, w, cache, pos_b, bt_b, qsl_b, B, sm_b, full.off_s,
+                                        full.ws, full.block_size, "silu", True, out=out_b)
+
+    # warm-up launch on all-PAD rows (nothing is written), then capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    assert torch.isnan(cache.float()).sum() > 0
+    for i in range(NB):
+        rows = slice(i * B, (i + 1) * B)
+        sub = full.select(rows, rows)
+        cc, bt_c, sm_c = sub.compact()
+        out_r, cache_r, _, _ = oracle_fused(sub, cache=cc, block_table=bt_c, slot_mapping=sm_c)
+        x_b.copy_(sub.x.to(DEV))
+        pos_b.copy_(sub.positions.to(DEV))
+        sm_b.copy_(sub.slot_mapping.to(DEV))
+        bt_b.copy_(sub.block_table.to(DEV))
+        out_b.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_close(to_np(out_b), out_r, "bf16", f"batch {i} out")
+        got = to_np(cache[sub.used_blocks.to(DEV)])
+        assert_bits_equal(got, cache_r, f"batch {i} referenced blocks")
+        assert_finite(written_cache_values(got, to_np(sm_c), sub.block_size, 0, sub.ws),
+                      f"batch {i} inserted slots")
+        say(f"  replay of batch {i} ok")
+    untouched = torch.ones(cache.shape[0], dtype=torch.bool, device=DEV)
+    untouched[full.used_blocks.to(DEV)] = False
+    assert untouched.any()
+    assert torch.isnan(cache[untouched].float()).all(), "write outside the referenced blocks"
 
 
 # ------------------------------------------------------------------ SSM-style ops
@@ -736,6 +817,7 @@ def test_varlen_sweep(spec):
         if not inplace:
             assert_bits_equal(og[~mask], out_r[~mask], "PAD sequences untouched")
         assert_bits_equal(to_np(st_g), st_r, f"{name} states inplace={inplace}")
+        assert_finite(to_np(st_g)[ci[ci != case.pad_slot_id]], f"{name} written states")
 
 
 def test_varlen_transposed_view_and_null_options():
@@ -771,6 +853,7 @@ def test_config_ssm_varlen_and_updates():
     out_g, st_g = gpu_varlen(case)
     assert_close(to_np(out_g), out_r, "bf16", "ssm varlen out")
     assert_bits_equal(to_np(st_g), st_r, "ssm varlen states")
+    assert_finite(to_np(st_g)[to_np(case.cache_indices)], "ssm varlen written states")
     out_i, st_i = gpu_varlen(case, inplace=True)
     assert_bits_equal(to_np(out_i), to_np(out_g), "in-place == out-of-place")
     assert_bits_equal(to_np(st_i), to_np(st_g), "in-place states")
@@ -781,13 +864,44 @@ def test_config_ssm_varlen_and_updates():
     w, b = case.weight, case.bias
     st_cpu = st_r
     wd, bd, cid = w.to(DEV), b.to(DEV), ci.to(DEV)
+    y_ref = []
     for s, xs_s in enumerate(xs):
         y_r, st_cpu = oracle.causal_conv1d_update(to_np(xs_s), st_cpu, to_np(w), to_np(b), "silu",
                                                   to_np(ci), -1)
+        y_ref.append(y_r)
         y_g = lib.causal_conv1d_update(xs_s.to(DEV), st_g, wd, bd, True, None, cid, -1,
                                        out=torch.empty(8, 8192, dtype=torch.bfloat16, device=DEV))
         assert_close(to_np(y_g), y_r, "bf16", f"update step {s}")
     assert_bits_equal(to_np(st_g), st_cpu, "states after 64 updates")
+    assert_finite(to_np(st_g)[to_np(ci)], "live states after 64 updates")
+
+    # The same 64 steps captured as one hipGraph, replayed on the pool as the
+    # prefill left it: every step's output and the final pool as above.
+    say("ssm updates: 64 steps in one graph")
+    st_p = np.ascontiguousarray(st_r)
+    pool = torch.from_numpy(st_p.view(np.int16)).view(torch.bfloat16).to(DEV)
+    x_all = torch.stack(xs).to(DEV)
+    y_all = torch.full_like(x_all, SENTINEL)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a scratch copy of the pool
+        scratch = pool.clone()
+        lib.causal_conv1d_update(x_all[0], scratch, wd, bd, True, None, cid, -1,
+                                 out=torch.empty_like(x_all[0]))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del scratch
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(len(xs)):
+            lib.causal_conv1d_update(x_all[s], pool, wd, bd, True, None, cid, -1, out=y_all[s])
+    torch.cuda.synchronize()
+    assert_bits_equal(to_np(pool), st_p, "pool untouched by the capture")
+    graph.replay()
+    torch.cuda.synchronize()
+    for s in range(len(xs)):
+        assert_close(to_np(y_all[s]), y_ref[s], "bf16", f"graph step {s}")
+    assert_bits_equal(to_np(pool), st_cpu, "states after the 64-step graph")
 
 
 @pytest.mark.parametrize("dt,W,dim,idx,inplace", [
@@ -824,6 +938,7 @@ def test_update_sweep(dt, W, dim, idx, inplace):
     if not inplace and ci is not None:
         assert_bits_equal(to_np(out)[3], out_r[3], "PAD row untouched")
     assert_bits_equal(to_np(std), st_r, "states")
+    assert_finite(to_np(std), "states")
 
 
 # ------------------------------------------------------------------ gather
@@ -842,6 +957,7 @@ def test_config_spec_gather(real_count):
     lib.gather_intermediate_conv_window(gc.src.to(DEV), gc.abs_positions.to(DEV), rc, out_g,
                                         gc.d_conv)
     assert_bits_equal(to_np(out_g), out_r, "gathered windows")
+    assert_finite(to_np(out_g)[:max(0, min(real_count, 512))], "live gathered windows")
 
 
 @pytest.mark.parametrize("dt,conv_dim,d_conv,seq_len", [
@@ -1067,6 +1183,7 @@ def check_update_tokens(name, dt, W, L, T, ring, layout, in_place, has_bias, has
     assert_close(got[live], out_r[live], dtype_name(dt), f"{name} out")
     assert_bits_equal(got[~live], out_r[~live], f"{name} PAD rows untouched")
     assert_bits_equal(to_np(stg), st_r, f"{name} state pool")
+    assert_finite(to_np(stg)[live_slots.numpy()], f"{name} live states")
 
 
 def test_config_ssm_spec_decode():
@@ -1097,6 +1214,7 @@ def test_config_ssm_spec_decode():
                                         seqlens.to(DEV), ci_g, -1, out=out_g.permute(0, 2, 1))
         assert_close(to_np(out_g.permute(0, 2, 1).contiguous()), out_r, "bf16", f"step {step} out")
         assert_bits_equal(to_np(pool_g), pool_r, f"step {step} pool")
+        assert_finite(to_np(pool_g)[to_np(ci)], f"step {step} live states")
 
 
 def test_update_ring_form_equals_tokens_entry():
@@ -1117,6 +1235,7 @@ def test_update_ring_form_equals_tokens_entry():
                                    seqlens.to(DEV), None, -1, out=torch.empty_like(x, device=DEV))
     assert_close(to_np(out), out_r[:, :, 0], "bf16", "ring update out")
     assert_bits_equal(to_np(stg), st_r, "ring update state")
+    assert_finite(to_np(stg), "ring update state")
 
 
 # ------------------------------------------------------------------ random SSM-side sweep

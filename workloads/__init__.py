@@ -60,6 +60,23 @@ class FusedCase:
     def C(self) -> int:
         return self.x.shape[1]
 
+    def select(self, rows: slice, reqs: slice) -> "FusedCase":
+        """Requests ``reqs`` (whose rows are ``rows``) of a multi-batch case
+        as a case of their own: their rows, block-table rows and request
+        offsets (rebased to 0), over the same cache."""
+        bt = self.block_table[reqs]
+        u = torch.unique(bt.long())
+        if not (u == self.poison_block).any():
+            u = torch.cat([u, torch.tensor([self.poison_block])])
+        qsl = self.query_start_loc[reqs.start:reqs.stop + 1] - self.query_start_loc[reqs.start]
+        return FusedCase(**{**self.__dict__, "x": self.x[rows],
+                            "positions": self.positions[rows], "block_table": bt,
+                            "slot_mapping": self.slot_mapping[rows],
+                            "query_start_loc": qsl.to(torch.int32),
+                            "num_reqs": reqs.stop - reqs.start,
+                            "num_actual": rows.stop - rows.start,
+                            "used_blocks": torch.sort(u).values})
+
     def compact(self):
         """(cache, block_table, slot_mapping) restricted to the referenced
         blocks, renumbered 0..n-1: the same logical content in a small host
