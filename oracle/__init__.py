@@ -45,7 +45,7 @@ def build(force: bool = False) -> str:
     ):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-pthread",
              "-o", tmp, _SRC, "-lm"]
         )
         os.replace(tmp, _LIB_PATH)
@@ -146,13 +146,15 @@ def seq_metadata(query_start_loc, num_reqs: int, num_actual: int, num_padded: in
 
 def fused_insert_conv(x, weight, cache, positions, block_table, seq_idx, slot_mapping,
                       query_start, off_s: int, ws: int, block_size: int,
-                      activation=None, use_residual: bool = True, out_init=None):
+                      activation=None, use_residual: bool = True, out_init=None,
+                      threads: int = 1):
     """Returns (out, cache_after).  ``cache`` itself is not modified.
 
     x [T, H*ws], weight [H*ws, W], cache [num_blocks, H, N, D],
     positions int64 [T], block_table int32 [num_reqs, max_blocks],
     seq_idx / query_start int32 [T], slot_mapping int64 [T].
     ``out_init`` (default zeros) supplies the values PAD rows keep.
+    ``threads`` > 1 splits the rows over that many host threads (same bits).
     """
     lib = _load()
     x = _c(x)
@@ -175,14 +177,17 @@ def fused_insert_conv(x, weight, cache, positions, block_table, seq_idx, slot_ma
     qs = _c(query_start, np.int32)
     if not (pos.shape[0] >= T and si.shape[0] >= T and sm.shape[0] >= T and qs.shape[0] >= T):
         raise ValueError("per-token arrays shorter than T")
-    rc = lib.oracle_fused_insert_conv(
-        _p(x), I64(_es(x, 0)), _p(w), I64(_es(w, 0)), I64(_es(w, 1)),
-        _p(cache_in), _p(cache_out), I64(nb), I32(H), I32(N), I32(D),
-        I64(_es(cache_in, 0)), I64(_es(cache_in, 1)), I64(_es(cache_in, 2)),
-        _p(pos), _p(bt), I64(_es(bt, 0)), I32(bt.shape[0]), I32(bt.shape[1]),
-        _p(si), _p(sm), _p(qs),
-        _p(out), I64(_es(out, 0)), I64(T), I32(off_s), I32(ws), I32(w.shape[1]),
-        dt, _act(activation), int(bool(use_residual)))
+    args = (_p(x), I64(_es(x, 0)), _p(w), I64(_es(w, 0)), I64(_es(w, 1)),
+            _p(cache_in), _p(cache_out), I64(nb), I32(H), I32(N), I32(D),
+            I64(_es(cache_in, 0)), I64(_es(cache_in, 1)), I64(_es(cache_in, 2)),
+            _p(pos), _p(bt), I64(_es(bt, 0)), I32(bt.shape[0]), I32(bt.shape[1]),
+            _p(si), _p(sm), _p(qs),
+            _p(out), I64(_es(out, 0)), I64(T), I32(off_s), I32(ws), I32(w.shape[1]),
+            dt, _act(activation), int(bool(use_residual)))
+    if threads > 1:
+        rc = lib.oracle_fused_insert_conv_mt(*args, I32(threads))
+    else:
+        rc = lib.oracle_fused_insert_conv(*args)
     _check(rc, "fused_insert_conv")
     return out, cache_out
 
@@ -212,8 +217,9 @@ def fused_insert_conv_streams(streams, cache, positions, block_table, seq_idx, s
 
 def causal_conv1d_varlen_fwd(x, weight, bias, conv_states, query_start_loc, cache_indices,
                              has_initial_state, activation, pad_slot_id: int = -1,
-                             out_init=None):
-    """Returns (out, conv_states_after).
+                             out_init=None, threads: int = 1):
+    """Returns (out, conv_states_after).  ``threads`` > 1 splits the
+    channels over that many host threads (same bits).
 
     x [dim, total_T] (channel-major), weight [dim, W], bias [dim] or None,
     conv_states [num_slots, dim, W-1], query_start_loc int32 [batch+1],
@@ -232,12 +238,15 @@ def causal_conv1d_varlen_fwd(x, weight, bias, conv_states, query_start_loc, cach
     hi = None if has_initial_state is None else _c(np.asarray(has_initial_state).astype(np.uint8))
     dim, total_T = x.shape
     out = np.zeros_like(x) if out_init is None else np.array(out_init, dtype=x.dtype, copy=True)
-    rc = lib.oracle_causal_conv1d_varlen_fwd(
-        _p(x), I64(_es(x, 0)), I64(_es(x, 1)), _p(w), I64(_es(w, 0)), I64(_es(w, 1)), _p(b),
-        _p(st_in), _p(st_out), I64(st_in.shape[0]),
-        I64(_es(st_in, 0)), I64(_es(st_in, 1)), I64(_es(st_in, 2)),
-        _p(qsl), I32(batch), _p(ci), _p(hi), _p(out), I64(_es(out, 0)), I64(_es(out, 1)),
-        I32(dim), I64(total_T), I32(w.shape[1]), dt, _act(activation), I32(pad_slot_id))
+    args = (_p(x), I64(_es(x, 0)), I64(_es(x, 1)), _p(w), I64(_es(w, 0)), I64(_es(w, 1)), _p(b),
+            _p(st_in), _p(st_out), I64(st_in.shape[0]),
+            I64(_es(st_in, 0)), I64(_es(st_in, 1)), I64(_es(st_in, 2)),
+            _p(qsl), I32(batch), _p(ci), _p(hi), _p(out), I64(_es(out, 0)), I64(_es(out, 1)),
+            I32(dim), I64(total_T), I32(w.shape[1]), dt, _act(activation), I32(pad_slot_id))
+    if threads > 1:
+        rc = lib.oracle_causal_conv1d_varlen_fwd_mt(*args, I32(threads))
+    else:
+        rc = lib.oracle_causal_conv1d_varlen_fwd(*args)
     _check(rc, "causal_conv1d_varlen_fwd")
     return out, st_out
 

@@ -11,6 +11,7 @@
 #include "sconv_oracle.h"
 
 #include <math.h>
+#include <pthread.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------ */
@@ -125,21 +126,22 @@ int oracle_seq_metadata(const int32_t* qsl, int32_t num_reqs, int64_t num_actual
 /* fused insert + depthwise causal conv over the paged cache           */
 /* ------------------------------------------------------------------ */
 
-int oracle_fused_insert_conv(const void* x, int64_t x_rs, const void* w, int64_t w_sc,
-                             int64_t w_sk, const void* cache_in, void* cache_out,
-                             int64_t num_blocks, int32_t H, int32_t N, int32_t D,
-                             int64_t cs0, int64_t cs1, int64_t cs2,
-                             const int64_t* positions, const int32_t* block_table,
-                             int64_t bt_rs, int32_t num_reqs, int32_t max_blocks,
-                             const int32_t* seq_idx, const int64_t* slot_mapping,
-                             const int32_t* query_start, void* out, int64_t out_rs,
-                             int64_t T, int32_t off_s, int32_t ws, int32_t W,
-                             int dtype, int act, int residual) {
-  if (!valid_dtype(dtype) || T < 0 || H < 1 || N < 1 || ws < 1 || W < 1 ||
-      off_s < 0 || off_s + ws > D)
-    return ORC_ERR_ARGS;
-
-  for (int64_t t = 0; t < T; ++t) {
+/* Rows [t_begin, t_end) of oracle_fused_insert_conv (arguments checked by
+ * the caller).  Each row reads only x, the snapshot cache_in and its own
+ * metadata, and writes only its own out row and its own slot, so disjoint
+ * row ranges are independent. */
+static int fused_rows(const void* x, int64_t x_rs, const void* w, int64_t w_sc,
+                      int64_t w_sk, const void* cache_in, void* cache_out,
+                      int64_t num_blocks, int32_t H, int32_t N, int32_t D,
+                      int64_t cs0, int64_t cs1, int64_t cs2,
+                      const int64_t* positions, const int32_t* block_table,
+                      int64_t bt_rs, int32_t num_reqs, int32_t max_blocks,
+                      const int32_t* seq_idx, const int64_t* slot_mapping,
+                      const int32_t* query_start, void* out, int64_t out_rs,
+                      int64_t T, int32_t off_s, int32_t ws, int32_t W,
+                      int dtype, int act, int residual, int64_t t_begin, int64_t t_end) {
+  (void)D;
+  for (int64_t t = t_begin; t < t_end; ++t) {
     const int64_t slot = slot_mapping[t];
     /* Reading: a negative slot is PAD -- no cache write and no output. */
     if (slot < 0) continue;
@@ -197,21 +199,43 @@ int oracle_fused_insert_conv(const void* x, int64_t x_rs, const void* w, int64_t
   return ORC_OK;
 }
 
+int oracle_fused_insert_conv(const void* x, int64_t x_rs, const void* w, int64_t w_sc,
+                             int64_t w_sk, const void* cache_in, void* cache_out,
+                             int64_t num_blocks, int32_t H, int32_t N, int32_t D,
+                             int64_t cs0, int64_t cs1, int64_t cs2,
+                             const int64_t* positions, const int32_t* block_table,
+                             int64_t bt_rs, int32_t num_reqs, int32_t max_blocks,
+                             const int32_t* seq_idx, const int64_t* slot_mapping,
+                             const int32_t* query_start, void* out, int64_t out_rs,
+                             int64_t T, int32_t off_s, int32_t ws, int32_t W,
+                             int dtype, int act, int residual) {
+  if (!valid_dtype(dtype) || T < 0 || H < 1 || N < 1 || ws < 1 || W < 1 ||
+      off_s < 0 || off_s + ws > D)
+    return ORC_ERR_ARGS;
+  return fused_rows(x, x_rs, w, w_sc, w_sk, cache_in, cache_out, num_blocks, H, N, D, cs0, cs1,
+                    cs2, positions, block_table, bt_rs, num_reqs, max_blocks, seq_idx,
+                    slot_mapping, query_start, out, out_rs, T, off_s, ws, W, dtype, act,
+                    residual, 0, T);
+}
+
 /* ------------------------------------------------------------------ */
 /* varlen causal conv1d with a state pool                              */
 /* ------------------------------------------------------------------ */
 
-int oracle_causal_conv1d_varlen_fwd(const void* x, int64_t x_sc, int64_t x_st,
-                                    const void* w, int64_t w_sc, int64_t w_sk,
-                                    const void* bias, const void* st_in, void* st_out,
-                                    int64_t num_slots, int64_t ss_slot, int64_t ss_c,
-                                    int64_t ss_k, const int32_t* qsl, int32_t batch,
-                                    const int32_t* cache_indices,
-                                    const uint8_t* has_init, void* out, int64_t o_sc,
-                                    int64_t o_st, int32_t dim, int64_t total_T,
-                                    int32_t W, int dtype, int act, int32_t pad_slot_id) {
-  if (!valid_dtype(dtype) || batch < 0 || dim < 0 || W < 1 || total_T < 0)
-    return ORC_ERR_ARGS;
+/* Channels [c_begin, c_end) of oracle_causal_conv1d_varlen_fwd, for every
+ * sequence (arguments checked by the caller).  A (sequence, channel) pair
+ * reads only its own inputs and state row and writes only its own outputs
+ * and state row, so disjoint channel ranges are independent. */
+static int varlen_channels(const void* x, int64_t x_sc, int64_t x_st,
+                           const void* w, int64_t w_sc, int64_t w_sk,
+                           const void* bias, const void* st_in, void* st_out,
+                           int64_t num_slots, int64_t ss_slot, int64_t ss_c,
+                           int64_t ss_k, const int32_t* qsl, int32_t batch,
+                           const int32_t* cache_indices,
+                           const uint8_t* has_init, void* out, int64_t o_sc,
+                           int64_t o_st, int64_t total_T,
+                           int32_t W, int dtype, int act, int32_t pad_slot_id,
+                           int32_t c_begin, int32_t c_end) {
   const int32_t S = W - 1; /* state length */
 
   for (int32_t b = 0; b < batch; ++b) {
@@ -225,7 +249,7 @@ int oracle_causal_conv1d_varlen_fwd(const void* x, int64_t x_sc, int64_t x_st,
      * slot is not read. */
     const int init = has_init ? (has_init[b] != 0) : 0;
 
-    for (int32_t c = 0; c < dim; ++c) {
+    for (int32_t c = c_begin; c < c_end; ++c) {
       /* Logical input u(i): x for i >= 0, the initial state (oldest first)
        * for -S <= i < 0. */
 #define U_VAL(i)                                                                  \
@@ -257,6 +281,22 @@ int oracle_causal_conv1d_varlen_fwd(const void* x, int64_t x_sc, int64_t x_st,
     }
   }
   return ORC_OK;
+}
+
+int oracle_causal_conv1d_varlen_fwd(const void* x, int64_t x_sc, int64_t x_st,
+                                    const void* w, int64_t w_sc, int64_t w_sk,
+                                    const void* bias, const void* st_in, void* st_out,
+                                    int64_t num_slots, int64_t ss_slot, int64_t ss_c,
+                                    int64_t ss_k, const int32_t* qsl, int32_t batch,
+                                    const int32_t* cache_indices,
+                                    const uint8_t* has_init, void* out, int64_t o_sc,
+                                    int64_t o_st, int32_t dim, int64_t total_T,
+                                    int32_t W, int dtype, int act, int32_t pad_slot_id) {
+  if (!valid_dtype(dtype) || batch < 0 || dim < 0 || W < 1 || total_T < 0)
+    return ORC_ERR_ARGS;
+  return varlen_channels(x, x_sc, x_st, w, w_sc, w_sk, bias, st_in, st_out, num_slots,
+                         ss_slot, ss_c, ss_k, qsl, batch, cache_indices, has_init, out, o_sc,
+                         o_st, total_T, W, dtype, act, pad_slot_id, 0, dim);
 }
 
 /* ------------------------------------------------------------------ */
@@ -421,4 +461,118 @@ int oracle_gather_ssm_state(const void* states, int64_t num_chunks, int64_t stat
       copy_elem(out, i * out_rs + e, states, r * states_rs + e, dtype);
   }
   return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* The same two ops split across host threads (CPU baseline only)      */
+/* ------------------------------------------------------------------ */
+
+/* The bodies above, unchanged, run on disjoint ranges of their outer loop:
+ * rows for the fused op, channels for the varlen op.  Each range touches
+ * only its own outputs (see fused_rows and varlen_channels), so the result
+ * equals the single-threaded call bit for bit.  The first failing range's
+ * code is returned. */
+#define ORC_MAX_THREADS 256
+
+typedef struct {
+  const void* x; int64_t x_rs; const void* w; int64_t w_sc, w_sk;
+  const void* cache_in; void* cache_out; int64_t num_blocks; int32_t H, N, D;
+  int64_t cs0, cs1, cs2; const int64_t* positions; const int32_t* block_table;
+  int64_t bt_rs; int32_t num_reqs, max_blocks; const int32_t* seq_idx;
+  const int64_t* slot_mapping; const int32_t* query_start; void* out; int64_t out_rs, T;
+  int32_t off_s, ws, W; int dtype, act, residual;
+  int64_t lo, hi; int rc;
+} fused_job;
+
+static void* fused_worker(void* arg) {
+  fused_job* j = (fused_job*)arg;
+  j->rc = fused_rows(j->x, j->x_rs, j->w, j->w_sc, j->w_sk, j->cache_in, j->cache_out,
+                     j->num_blocks, j->H, j->N, j->D, j->cs0, j->cs1, j->cs2, j->positions,
+                     j->block_table, j->bt_rs, j->num_reqs, j->max_blocks, j->seq_idx,
+                     j->slot_mapping, j->query_start, j->out, j->out_rs, j->T, j->off_s, j->ws,
+                     j->W, j->dtype, j->act, j->residual, j->lo, j->hi);
+  return NULL;
+}
+
+int oracle_fused_insert_conv_mt(const void* x, int64_t x_rs, const void* w, int64_t w_sc,
+                                int64_t w_sk, const void* cache_in, void* cache_out,
+                                int64_t num_blocks, int32_t H, int32_t N, int32_t D,
+                                int64_t cs0, int64_t cs1, int64_t cs2,
+                                const int64_t* positions, const int32_t* block_table,
+                                int64_t bt_rs, int32_t num_reqs, int32_t max_blocks,
+                                const int32_t* seq_idx, const int64_t* slot_mapping,
+                                const int32_t* query_start, void* out, int64_t out_rs,
+                                int64_t T, int32_t off_s, int32_t ws, int32_t W,
+                                int dtype, int act, int residual, int32_t nthreads) {
+  if (!valid_dtype(dtype) || T < 0 || H < 1 || N < 1 || ws < 1 || W < 1 ||
+      off_s < 0 || off_s + ws > D || nthreads < 1 || nthreads > ORC_MAX_THREADS)
+    return ORC_ERR_ARGS;
+  fused_job jobs[ORC_MAX_THREADS];
+  pthread_t tid[ORC_MAX_THREADS];
+  int started[ORC_MAX_THREADS];
+  for (int32_t i = 0; i < nthreads; ++i) {
+    fused_job j = {x, x_rs, w, w_sc, w_sk, cache_in, cache_out, num_blocks, H, N, D,
+                   cs0, cs1, cs2, positions, block_table, bt_rs, num_reqs, max_blocks,
+                   seq_idx, slot_mapping, query_start, out, out_rs, T, off_s, ws, W,
+                   dtype, act, residual, T * i / nthreads, T * (i + 1) / nthreads, ORC_OK};
+    jobs[i] = j;
+    started[i] = pthread_create(&tid[i], NULL, fused_worker, &jobs[i]) == 0;
+    if (!started[i]) fused_worker(&jobs[i]); /* no thread: run the range here */
+  }
+  int rc = ORC_OK;
+  for (int32_t i = 0; i < nthreads; ++i) {
+    if (started[i]) pthread_join(tid[i], NULL);
+    if (rc == ORC_OK) rc = jobs[i].rc;
+  }
+  return rc;
+}
+
+typedef struct {
+  const void* x; int64_t x_sc, x_st; const void* w; int64_t w_sc, w_sk;
+  const void* bias; const void* st_in; void* st_out; int64_t num_slots, ss_slot, ss_c, ss_k;
+  const int32_t* qsl; int32_t batch; const int32_t* cache_indices; const uint8_t* has_init;
+  void* out; int64_t o_sc, o_st, total_T; int32_t W; int dtype, act; int32_t pad_slot_id;
+  int32_t lo, hi; int rc;
+} varlen_job;
+
+static void* varlen_worker(void* arg) {
+  varlen_job* j = (varlen_job*)arg;
+  j->rc = varlen_channels(j->x, j->x_sc, j->x_st, j->w, j->w_sc, j->w_sk, j->bias, j->st_in,
+                          j->st_out, j->num_slots, j->ss_slot, j->ss_c, j->ss_k, j->qsl,
+                          j->batch, j->cache_indices, j->has_init, j->out, j->o_sc, j->o_st,
+                          j->total_T, j->W, j->dtype, j->act, j->pad_slot_id, j->lo, j->hi);
+  return NULL;
+}
+
+int oracle_causal_conv1d_varlen_fwd_mt(const void* x, int64_t x_sc, int64_t x_st,
+                                       const void* w, int64_t w_sc, int64_t w_sk,
+                                       const void* bias, const void* st_in, void* st_out,
+                                       int64_t num_slots, int64_t ss_slot, int64_t ss_c,
+                                       int64_t ss_k, const int32_t* qsl, int32_t batch,
+                                       const int32_t* cache_indices,
+                                       const uint8_t* has_init, void* out, int64_t o_sc,
+                                       int64_t o_st, int32_t dim, int64_t total_T,
+                                       int32_t W, int dtype, int act, int32_t pad_slot_id,
+                                       int32_t nthreads) {
+  if (!valid_dtype(dtype) || batch < 0 || dim < 0 || W < 1 || total_T < 0 || nthreads < 1 ||
+      nthreads > ORC_MAX_THREADS)
+    return ORC_ERR_ARGS;
+  varlen_job jobs[ORC_MAX_THREADS];
+  pthread_t tid[ORC_MAX_THREADS];
+  int started[ORC_MAX_THREADS];
+  for (int32_t i = 0; i < nthreads; ++i) {
+    varlen_job j = {x, x_sc, x_st, w, w_sc, w_sk, bias, st_in, st_out, num_slots, ss_slot,
+                    ss_c, ss_k, qsl, batch, cache_indices, has_init, out, o_sc, o_st, total_T,
+                    W, dtype, act, pad_slot_id, (int32_t)((int64_t)dim * i / nthreads),
+                    (int32_t)((int64_t)dim * (i + 1) / nthreads), ORC_OK};
+    jobs[i] = j;
+    started[i] = pthread_create(&tid[i], NULL, varlen_worker, &jobs[i]) == 0;
+    if (!started[i]) varlen_worker(&jobs[i]);
+  }
+  int rc = ORC_OK;
+  for (int32_t i = 0; i < nthreads; ++i) {
+    if (started[i]) pthread_join(tid[i], NULL);
+    if (rc == ORC_OK) rc = jobs[i].rc;
+  }
+  return rc;
 }

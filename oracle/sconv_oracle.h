@@ -168,6 +168,33 @@ int oracle_gather_ssm_state(const void* states, int64_t num_chunks, int64_t stat
                             int32_t real_count, int32_t max_count, void* out, int64_t out_rs,
                             int dtype);
 
+/*
+ * The fused op and the varlen op with their outer loop split over
+ * `nthreads` host threads (1..256): rows for the fused op, channels for the
+ * varlen op.  Same arguments, same results bit for bit; used to time the
+ * oracle on every host core.
+ */
+int oracle_fused_insert_conv_mt(const void* x, int64_t x_rs, const void* w, int64_t w_sc,
+                                int64_t w_sk, const void* cache_in, void* cache_out,
+                                int64_t num_blocks, int32_t H, int32_t N, int32_t D,
+                                int64_t cs0, int64_t cs1, int64_t cs2,
+                                const int64_t* positions, const int32_t* block_table,
+                                int64_t bt_rs, int32_t num_reqs, int32_t max_blocks,
+                                const int32_t* seq_idx, const int64_t* slot_mapping,
+                                const int32_t* query_start, void* out, int64_t out_rs,
+                                int64_t T, int32_t off_s, int32_t ws, int32_t W,
+                                int dtype, int act, int residual, int32_t nthreads);
+int oracle_causal_conv1d_varlen_fwd_mt(const void* x, int64_t x_sc, int64_t x_st,
+                                       const void* w, int64_t w_sc, int64_t w_sk,
+                                       const void* bias, const void* st_in, void* st_out,
+                                       int64_t num_slots, int64_t ss_slot, int64_t ss_c,
+                                       int64_t ss_k, const int32_t* qsl, int32_t batch,
+                                       const int32_t* cache_indices,
+                                       const uint8_t* has_init, void* out, int64_t o_sc,
+                                       int64_t o_st, int32_t dim, int64_t total_T,
+                                       int32_t W, int dtype, int act, int32_t pad_slot_id,
+                                       int32_t nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -674,3 +674,34 @@ def test_named_workloads_are_well_formed():
                 first = int(case.positions[qsl[r]])
                 for q in range(max(0, first - 3), first):
                     assert int(case.block_table[r, q // N]) * N + q % N not in live
+
+
+# ------------------------------------------------------------------ threaded forms
+
+@pytest.mark.parametrize("threads", [2, 3, 8])
+def test_threaded_oracle_equals_single_threaded(threads):
+    """The row-split fused op and the channel-split varlen op (used to time
+    the oracle on every host core) give the single-threaded bits, outputs
+    and cache or states, including ranges that cut a request in two."""
+    o = orc()
+    from tests.gpu_util import oracle_fused
+    case = workloads.fused_case(91, [9, 1, 30, 4, 17], [0, 21, 5, 40, 3], H=4, D=64, ws=16,
+                                off_s=16, block_size=16, W=4, dtype="bf16", pad_count=4,
+                                tail_pad=3)
+    out1, cache1, si, qs = oracle_fused(case)
+    out_n, cache_n = o.fused_insert_conv(
+        to_np(case.x), to_np(case.weight), to_np(case.cache), to_np(case.positions),
+        to_np(case.block_table), si, to_np(case.slot_mapping), qs, case.off_s, case.ws,
+        case.block_size, "silu", True, out_init=to_np(torch.full_like(case.x, -777.0)),
+        threads=threads)
+    assert_bits_equal(out_n, out1, "fused out")
+    assert_bits_equal(cache_n, cache1, "fused cache")
+    v = workloads.varlen_case(92, [13, 1, 0, 70, 2], dim=24, num_slots=9, W=4, dtype="bf16",
+                              init_count=2, pad_seqs=1)
+    args = (to_np(v.x), to_np(v.weight), to_np(v.bias), to_np(v.conv_states),
+            to_np(v.query_start_loc), to_np(v.cache_indices), to_np(v.has_initial_state),
+            "silu", -1)
+    a_out, a_st = o.causal_conv1d_varlen_fwd(*args)
+    b_out, b_st = o.causal_conv1d_varlen_fwd(*args, threads=threads)
+    assert_bits_equal(b_out, a_out, "varlen out")
+    assert_bits_equal(b_st, a_st, "varlen states")
