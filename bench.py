@@ -1,20 +1,25 @@
 """Benchmark of the paged short-convolution hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --probe          (machine ceilings, one JSON line)
 
-Default workload (the headline): batched decode -- 256 requests x 1 token,
-history lengths uniform in [1, 4096], H=32, D=128, ws=32 (C=1024), W=4,
-N=16, bf16, SiLU and residual.  One step is one pass of the hot path over one
-decode batch, replayed from a hipGraph: by default one launch of
-sconv_fused_insert_conv_qsl (request search, insert and conv);
-`--metadata separate` runs sconv_seq_metadata + sconv_fused_insert_conv.
-Other workloads (same JSON shape, one line each):
+Default (the headline): batched decode -- 256 requests x 1 token, history
+lengths uniform in [1, 4096], H=32, D=128, ws=32 (C=1024), W=4, N=16, bf16,
+SiLU and residual; one step is one launch of sconv_fused_insert_conv_qsl
+(request search, insert and conv) replayed from a hipGraph.  The same line
+carries a `prefill` object for the mixed varlen prefill -- 16 requests,
+~20k rows, four streams of C=4096 over one shared cache, 10% PAD rows; one
+step is sconv_seq_metadata + four sconv_fused_insert_conv launches -- so
+that one run measures the metric's decode and prefill halves.
+
+`--workload NAME` prints one line for one workload instead:
+  batched_decode    the headline decode step alone
   decode_layer      the decode batch with all four streams of a layer
                     (ws=32 each) in one sconv_fused_insert_conv_streams launch
-  mixed_prefill     16 requests, ~17-20k rows, 4 streams of C=4096 over one
-                    cache, 10% PAD rows; step = metadata + 4 fused launches
+  mixed_prefill     the prefill step alone
   spec_decode       512 requests x 4 draft rows, C=4096, N=32; step = folded
-                    fused launch + conv-window gather (device real_count)
+                    fused launch + conv-window gather, each replica with its
+                    own device-side real_count uniform in [0, 512]
   ssm_prefill       8 x 4096 tokens, dim 8192, channel-major, state pool of
                     1024 slots; step = causal_conv1d_varlen_fwd
   ssm_decode        8 rows x dim 8192 against the same pool; step =
@@ -29,11 +34,25 @@ inputs (own inputs, outputs, tables and cache blocks) so that at least
 ~512 MB separate two visits of the same bytes: every step reads HBM, not the
 L2s or the 256 MB MALL.
 
-Prints one JSON line.  `value` is tokens per second over the K timed steps
-(wall clock between two device synchronizations).  `roofline` describes the
-workload's dominant kernel: algorithmic bytes per launch divided by its
-average launch duration, timed with HIP events on the stream it runs on.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Timing.  The library's code is loaded first (sconv_init), then the timed
+steps, the warm-up steps and the dominant kernel alone are captured into
+hipGraphs and uploaded; nothing runs before the warm-up.  Exactly W warm-up
+steps run, then exactly K timed steps, bracketed by device synchronizations.
+HIP events on the stream the steps run on bracket the K steps; a spin
+kernel queued ahead of the first event keeps the host's graph submission
+out of the interval.  `ms_per_step` and `value` (tokens per second) come
+from those events; `wall_ms_per_step` is the host clock around the same
+region, submission included.
+
+`roofline` describes the workload's dominant kernel: algorithmic bytes per
+launch divided by its average launch duration.  `frac` takes the duration
+from HIP events around replays of a graph holding only that kernel (the
+headline figure); `frac_trace` takes it from the committed rocprofv3 kernel
+trace of the same command (profiles/), where tracing adds its own handling
+to every dispatch, and is null once the kernel sources have changed since.
+`cpu_baseline` times the oracle on a bounded sample of the same workload,
+on every host core the process may use (rows or channels split across
+threads) and single-threaded.
 """
 from __future__ import annotations
 
@@ -90,6 +109,42 @@ def stored_traffic(workload: str):
     if not m or not t or m.group(1) != kernel_source_digest():
         return None
     return float(t.group(1))
+
+
+def stored_trace(kernel: str, workload: str):
+    """Average duration (us) of the dominant kernel in the committed
+    rocprofv3 kernel-trace summary, if it was taken on the current sources."""
+    path = os.path.join(PROFILES, f"{kernel.replace('_kernel', '')}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_sources:\s*([0-9a-f]+)", text)
+    t = re.search(r"trace_avg_us:\s*([0-9.]+)", text)
+    if not m or not t or m.group(1) != kernel_source_digest():
+        return None
+    return float(t.group(1))
+
+
+# ---------------------------------------------------------------- host facts
+
+def cpu_threads() -> int:
+    """Host threads this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when set (the share of a shared host it is given)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, min(n, 256))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ---------------------------------------------------------------- accounting
@@ -193,8 +248,11 @@ def repeat_until(budget, once):
     return tokens, spent, n
 
 
-def time_oracle_fused(case, activation="silu"):
-    """Seconds the oracle spends on one fused launch of `case` (compact cache)."""
+def time_oracle_fused(case, activation="silu", threads=1):
+    """Seconds the oracle spends on one fused launch of `case` (compact
+    cache), its rows split over `threads` host threads.  The timed call
+    includes its own marshalling: a copy of the compact cache it writes
+    into."""
     import oracle
     from tests.helpers import to_np
     cache, bt, sm = case.compact()
@@ -204,7 +262,7 @@ def time_oracle_fused(case, activation="silu"):
             si, to_np(sm), qs, case.off_s, case.ws, case.block_size, activation,
             case.use_residual)
     t0 = time.perf_counter()
-    oracle.fused_insert_conv(*args)
+    oracle.fused_insert_conv(*args, threads=threads)
     return time.perf_counter() - t0
 
 
@@ -214,12 +272,16 @@ class Workload:
     kernel_name = "fused_insert_conv_kernel"
     bound = "hbm"
     dtype = "bf16"
+    oracle_split = True   # the oracle op of its CPU baseline has a threaded form
 
     def kernel(self, i):          # the dominant kernel alone
         raise NotImplementedError
 
     def kernels_per_call(self):   # launches of it per kernel(i)
         return 1
+
+    def step_is_kernel(self):     # a step is one launch of the kernel, nothing more
+        return self.step == self.kernel
 
 
 class DecodeBench(Workload):
@@ -270,6 +332,9 @@ class DecodeBench(Workload):
             self.lib.sconv_seq_metadata(self.qsl, self.B, self.B, self.si, self.qs, self.B)
         self.kernel(i)
 
+    def step_is_kernel(self):
+        return self.fold
+
     def config(self):
         return {"workload": "batched_decode", "requests": self.B, "tokens_per_step": self.B,
                 "metadata": "folded into the fused launch" if self.fold else "separate launch",
@@ -277,13 +342,13 @@ class DecodeBench(Workload):
                 "W": 4, "block_size": 16, "activation": "silu", "residual": True,
                 "graph": "hipGraph", "replicas": self.R}
 
-    def oracle_sample(self, budget):
+    def oracle_sample(self, budget, threads=1):
         # Whole sub-batches of 256 requests, cycled, until the budget is spent.
         n_sub = self.R * self.B // 256
 
         def once(n):
             rows = slice(256 * (n % n_sub), 256 * (n % n_sub + 1))
-            return 256, time_oracle_fused(sub_case(self.case, rows, rows, self.case.poison_block))
+            return 256, time_oracle_fused(sub_case(self.case, rows, rows), threads=threads)
         done, spent, n = repeat_until(budget, once)
         return (done / spent, f"{n} decode sub-batches of 256 requests ({done} tokens, cycling "
                 f"the {n_sub} distinct ones)", spent)
@@ -348,6 +413,9 @@ class DecodeLayerBench(Workload):
     def step(self, i):
         self.kernel(i)
 
+    def step_is_kernel(self):
+        return self.one_launch
+
     def config(self):
         return {"workload": "decode_layer", "requests": self.B, "tokens_per_step": self.B,
                 "streams": 4, "stream_launches": "one launch for all 4 streams"
@@ -356,14 +424,14 @@ class DecodeLayerBench(Workload):
                 "H": 32, "D": 128, "ws": 32, "C_per_stream": 1024, "W": 4, "block_size": 16,
                 "activation": "silu", "residual": True, "graph": "hipGraph", "replicas": self.R}
 
-    def oracle_sample(self, budget):
+    def oracle_sample(self, budget, threads=1):
         # Whole sub-batches of 256 requests x 4 streams, cycled, until the
         # budget is spent.
         n_sub = self.R * self.B // 256
 
         def once(n):
             rows = slice(256 * (n % n_sub), 256 * (n % n_sub + 1))
-            return 256, sum(time_oracle_fused(sub_case(k, rows, rows, k.poison_block))
+            return 256, sum(time_oracle_fused(sub_case(k, rows, rows), threads=threads)
                             for k in self.cases)
         done, spent, n = repeat_until(budget, once)
         return (done / spent, f"{n} decode sub-batches of 256 requests x 4 streams ({done} tokens, "
@@ -439,11 +507,12 @@ class MixedPrefillBench(Workload):
                 "C": 4096, "W": 4, "block_size": 16, "pad_fraction": 0.1,
                 "activation": "silu", "residual": True}
 
-    def oracle_sample(self, budget):
+    def oracle_sample(self, budget, threads=1):
         # Whole streams (all rows), in turn, until the budget is spent; a
         # token counts once for its four streams.
         done, spent, n = repeat_until(
-            budget, lambda n: (self.live / 4, time_oracle_fused(self.streams[n % 4])))
+            budget, lambda n: (self.live / 4,
+                               time_oracle_fused(self.streams[n % 4], threads=threads)))
         return done / spent, f"{n} whole-stream passes over all {self.live} live rows", spent
 
 
@@ -476,10 +545,15 @@ class SpecDecodeBench(Workload):
         self.qs = torch.empty(self.B, dtype=torch.int32, device=dev)
         gc = workloads.spec_gather(first)
         self.gpos = gc.abs_positions.to(dev)
-        self.rc = torch.tensor([gc.real_count], dtype=torch.int32, device=dev)
+        # Each replica's gather reads its own live count, uniform in
+        # [0, 512], from a fixed device buffer (as a replayed step would find
+        # it rewritten on the device).
+        g = torch.Generator().manual_seed(1004)
+        self.counts = torch.randint(0, 513, (self.R,), generator=g).to(torch.int32)
+        self.rcs = self.counts.to(dev)
         self.gout = torch.empty(self.R, 512, c.C, 3, dtype=torch.bfloat16, device=dev)
-        self.real_count = gc.real_count
         self.tokens_per_step = self.B
+        self.sweep = None
 
     def rows(self, i):
         return slice(i * self.B, (i + 1) * self.B)
@@ -500,24 +574,44 @@ class SpecDecodeBench(Workload):
         if not self.fold:
             self.lib.sconv_seq_metadata(self.qsl, 512, self.B, self.si, self.qs, self.B)
         self.kernel(i)
+        self.gather(i, self.rcs[i:i + 1])
+
+    def gather(self, i, count):
         self.lib.gather_intermediate_conv_window(self.x[self.rows(i)].view(1, self.B, -1),
-                                                 self.gpos, self.rc, self.gout[i], 3)
+                                                 self.gpos, count, self.gout[i], 3)
+
+    def extra(self, stream, reps):
+        """The window gather alone at fixed live counts (0, 128, 256, 512 of
+        512 slots), us per launch from HIP events around graph replays: what
+        a dead slot costs next to a live one."""
+        import torch
+        out = {}
+        for n in (0, 128, 256, 512):
+            rc = torch.tensor([n], dtype=torch.int32, device="cuda")
+            g = capture(lambda i: self.gather(i, rc), range(self.R), stream)
+            us = time_graph(g, reps, stream) * 1e3 / (reps * self.R)
+            out[str(n)] = {"us": round(us, 3),
+                           # 2 x 4096 channels x 3 rows x 2 bytes + 4 per live slot
+                           "GB/s": round(49156 * n / (us * 1e-6) / 1e9, 1) if n else None}
+        self.sweep = out
+        return {"gather_real_count_sweep": out}
 
     def config(self):
         return {"workload": "spec_decode", "requests": 512, "drafts": 4, "tokens_per_step": 2048,
                 "metadata": "folded into the fused launch" if self.fold else "separate launch",
                 "positions": "uniform[1,131072)", "H": 64, "D": 64, "ws": 64, "C": 4096,
-                "W": 4, "block_size": 32, "gather": {"max_count": 512, "d_conv": 3,
-                                                     "real_count": self.real_count},
+                "W": 4, "block_size": 32,
+                "gather": {"max_count": 512, "d_conv": 3,
+                           "real_count": "uniform[0,512] per replica, on the device",
+                           "mean_real_count": round(float(self.counts.float().mean()), 1)},
                 "activation": "silu", "residual": True, "graph": "hipGraph",
                 "replicas": self.R}
 
-    def oracle_sample(self, budget):
+    def oracle_sample(self, budget, threads=1):
         def once(n):
             i = n % self.R
-            sub = sub_case(self.case, self.rows(i), slice(512 * i, 512 * (i + 1)),
-                           self.case.poison_block)
-            return self.B, time_oracle_fused(sub)
+            sub = sub_case(self.case, self.rows(i), slice(512 * i, 512 * (i + 1)))
+            return self.B, time_oracle_fused(sub, threads=threads)
         done, spent, n = repeat_until(budget, once)
         return (done / spent, f"fused conv of {n} whole spec batches ({done} tokens, cycling the "
                 f"{self.R} distinct ones)", spent)
@@ -561,7 +655,7 @@ class SsmPrefillBench(Workload):
                 "W": 4, "layout": "channel-major", "state_slots": 1024, "with_state": 4,
                 "activation": "silu", "bias": True}
 
-    def oracle_sample(self, budget):
+    def oracle_sample(self, budget, threads=1):
         import oracle
         from tests.helpers import to_np
         c = self.case
@@ -580,7 +674,7 @@ class SsmPrefillBench(Workload):
             x2 = np.ascontiguousarray(np.concatenate([xs[:, k * L:(k + 1) * L] for k in keep], 1))
             t0 = time.perf_counter()
             oracle.causal_conv1d_varlen_fwd(x2, w, b, st, np.array([0, L, 2 * L], np.int32),
-                                            ci[keep], hi[keep], "silu", -1)
+                                            ci[keep], hi[keep], "silu", -1, threads=threads)
             return 2 * L, time.perf_counter() - t0
         done, spent, n = repeat_until(budget, once)
         return (done / spent, f"{n} pairs of 4096-token sequences, one with a state and one "
@@ -589,6 +683,7 @@ class SsmPrefillBench(Workload):
 
 class SsmDecodeBench(Workload):
     kernel_name = "update_kernel"
+    oracle_split = False
 
     def __init__(self, dev="cuda"):
         import torch
@@ -619,7 +714,7 @@ class SsmDecodeBench(Workload):
                 "state_slots": 1024, "activation": "silu", "bias": True,
                 "graph": "hipGraph", "steps_per_graph": 64}
 
-    def oracle_sample(self, budget):
+    def oracle_sample(self, budget, threads=1):
         import oracle
         from tests.helpers import to_np
         c = self.case
@@ -641,6 +736,7 @@ class SsmSpecDecodeBench(Workload):
     uniform[0, 4096)), through causal_conv1d_update_tokens; 64 steps per
     graph, each with its own inputs and outputs."""
     kernel_name = "update_tokens_vec_kernel"
+    oracle_split = False
     B, T, DIM, W, STEPS = 8, 4, 8192, 4, 64
 
     def __init__(self, dev="cuda"):
@@ -679,7 +775,7 @@ class SsmSpecDecodeBench(Workload):
                 "positions": "uniform[0,4096)", "state_slots": 1024, "activation": "silu",
                 "bias": True, "graph": "hipGraph", "steps_per_graph": self.STEPS}
 
-    def oracle_sample(self, budget):
+    def oracle_sample(self, budget, threads=1):
         import oracle
         from tests.helpers import to_np
         c = self.case
@@ -704,6 +800,7 @@ class SsmStateGatherBench(Workload):
     not the MALL."""
     kernel_name = "gather_ssm_kernel"
     dtype = "f32"
+    oracle_split = False
     SHAPE = (64, 64, 128)
     CHUNKS, SLOTS, LIVE, R_ = 128, 128, 96, 3
 
@@ -736,7 +833,7 @@ class SsmStateGatherBench(Workload):
                 "state_shape": list(self.SHAPE), "state_dtype": "f32", "graph": "hipGraph",
                 "replicas": self.R}
 
-    def oracle_sample(self, budget):
+    def oracle_sample(self, budget, threads=1):
         import oracle
         st = self.states[0][:16].cpu().numpy()
         idx = (self.idx[0].cpu() % 16).numpy()
@@ -773,13 +870,301 @@ DEFAULT_STEPS = {"batched_decode": 19200, "decode_layer": 9600, "mixed_prefill":
 
 # ---------------------------------------------------------------- timing
 
-def capture(fn, indices):
+def capture(fn, indices, stream):
+    """One hipGraph of fn(i) for i in indices, captured on `stream`."""
     import torch
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in indices:
-            fn(i)
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in indices:
+                fn(i)
     return g
+
+
+_HIP = None
+
+
+def hip_runtime():
+    """The HIP runtime torch loaded (one per process)."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+        _HIP = ctypes.CDLL("libamdhip64.so.7")
+        _HIP.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    return _HIP
+
+
+def upload(graph, stream):
+    """Upload an instantiated graph to the device without running it, so
+    that its first replay does no set-up work."""
+    rc = hip_runtime().hipGraphUpload(graph.raw_cuda_graph_exec(), stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"hipGraphUpload failed ({rc})")
+
+
+def time_graph(graph, reps, stream):
+    """Milliseconds of `reps` back-to-back replays of an uploaded graph,
+    between HIP events on `stream`; a spin kernel queued first keeps the
+    host's submission out of the interval."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SPIN_CYCLES)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+SPIN_CYCLES = 2_000_000   # ~1 ms of spinning ahead of a timed interval
+
+
+class StepGraphs:
+    """The graphs of one workload: K timed steps, W warm-up steps (replicas
+    cycled), and R launches of the dominant kernel alone."""
+
+    def __init__(self, wl, K, Wm, stream):
+        self.wl, self.K, self.Wm, self.stream = wl, K, Wm, stream
+        R = wl.R
+        self.full = capture(wl.step, range(R), stream) if max(K, Wm) >= R else None
+        self.k_rem = capture(wl.step, range(K % R), stream) if K % R else None
+        # Warm-up steps end on replica R-1, so the timed steps, which start
+        # on replica 0, find none of their bytes left in a cache.
+        self.w_rem = (capture(wl.step, range(R - Wm % R, R), stream) if Wm % R else None)
+        self.kern = capture(wl.kernel, range(R), stream)
+        for g in (self.full, self.k_rem, self.w_rem, self.kern):
+            if g is not None:
+                upload(g, stream)
+
+    def _run(self, n, rem):
+        for _ in range(n // self.wl.R):
+            self.full.replay()
+        if rem is not None:
+            rem.replay()
+
+    def warmup(self):
+        import torch
+        with torch.cuda.stream(self.stream):
+            self._run(self.Wm, self.w_rem)
+        torch.cuda.synchronize()
+
+    def timed(self):
+        """(event ms, wall s) of exactly K steps."""
+        import torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(self.stream):
+            torch.cuda._sleep(SPIN_CYCLES)
+            e0.record(self.stream)
+            self._run(self.K, self.k_rem)
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1), wall
+
+    def kernel_us(self, reps):
+        """Average duration of one launch of the dominant kernel (us)."""
+        ms = time_graph(self.kern, reps, self.stream)
+        return ms * 1e3 / (reps * self.wl.R * self.wl.kernels_per_call())
+
+
+def cpu_baseline(wl, budget):
+    """The oracle on every host core the process may use, and alone."""
+    if budget <= 0:
+        return None
+    n = cpu_threads() if wl.oracle_split else 1
+    v, sample, spent = wl.oracle_sample(budget, threads=n)
+    out = {"value": round(v, 1), "unit": "tokens/s", "cores": n, "kind": "oracle",
+           "sample": f"{sample}; {spent:.1f} s on {n} thread{'s' if n > 1 else ''}",
+           "hardware_concurrency": os.cpu_count(), "cpu_model": cpu_model()}
+    if n > 1:
+        v1, sample1, spent1 = wl.oracle_sample(budget, threads=1)
+        out["single_thread"] = {"value": round(v1, 1), "cores": 1,
+                                "sample": f"{sample1}; {spent1:.1f} s on 1 thread"}
+    return out
+
+
+def measure(wl, name, K, Wm, reps, budget, stream):
+    """Everything one JSON line says about one workload."""
+    graphs = StepGraphs(wl, K, Wm, stream)
+    graphs.warmup()
+    ms, wall = graphs.timed()
+    kern_us = graphs.kernel_us(reps)
+    extra = wl.extra(stream, reps) if hasattr(wl, "extra") else {}
+    achieved = wl.bytes_per_launch / (kern_us * 1e-6) / 1e9
+    trace_us = stored_trace(wl.kernel_name, name)
+    roof = {"bound": wl.bound, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac_trace": (round(wl.bytes_per_launch / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                           if trace_us else None),
+            "headline": "frac: HIP events around graph replays of the kernel alone",
+            "traffic": stored_traffic(name), "kernel": wl.kernel_name,
+            "bytes_per_launch": wl.bytes_per_launch, "launch_us": round(kern_us, 3),
+            "launch_us_trace": trace_us,
+            # the same bytes over the event-timed step, where a step is one
+            # launch of the kernel and nothing else
+            "step_frac": round(wl.bytes_per_launch / (ms * 1e-3 / K) / 1e9 / HBM_PEAK_GBS, 4)
+            if wl.step_is_kernel() else None}
+    line = {
+        "value": round(wl.tokens_per_step * K / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms / K, 6),
+        "wall_ms_per_step": round(wall * 1e3 / K, 6),
+        "dtype": wl.dtype,
+        "config": wl.config(),
+        "roofline": roof,
+        "cpu_baseline": cpu_baseline(wl, budget),
+    }
+    line.update(extra)
+    return line
+
+
+# ---------------------------------------------------------------- probes
+
+PROBE_SRC = os.path.join(ROOT, "bench_probes.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_probes.so")
+
+
+def build_probes(verbose=False) -> str:
+    """Compile the measurement probes (bench_probes.hip) for gfx950."""
+    import subprocess
+
+    from depthwise_causal_conv1d_amd import build as b
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [b.hipcc(), f"--offload-arch={b.ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", tmp,
+           PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building bench_probes.so")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
+def run_probes(stream):
+    """Streaming ceilings and latency floors of this GPU (one JSON line)."""
+    import ctypes
+
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise ImportError(f"{PROBE_LIB} is missing: build it with `python -c 'import bench; "
+                          "bench.build_probes()'` (or __graft_entry__.build())")
+    P = ctypes.CDLL(PROBE_LIB)
+    V, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    P.probe_read.argtypes = [V, I64, V, I32, V]
+    P.probe_write.argtypes = [V, I64, I32, V]
+    P.probe_copy.argtypes = [V, V, I64, I32, V]
+    P.probe_read_write2.argtypes = [V, V, V, I64, I32, I32, I32, V]
+    P.probe_empty.argtypes = [I32, V]
+    P.probe_load_store.argtypes = [V, V, I32, V]
+    P.probe_chain.argtypes = [V, I32, V, V, V, I32, I32, V]
+    s = stream.cuda_stream
+    res = {"workload": "probe", "peak_GBs": HBM_PEAK_GBS}
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed ({rc})")
+
+    # Streaming ceilings: 1 GiB per stream, 32768 workgroups; each launch
+    # timed over graph replays, the buffers far larger than the MALL.
+    GiB = 1 << 30
+    n16 = GiB // 16
+    groups = 32768
+    a = torch.empty(GiB, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty(GiB, dtype=torch.uint8, device="cuda")
+    c = torch.empty(GiB, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(groups * 256 * 16, dtype=torch.uint8, device="cuda")
+    stream_cases = {
+        "read": (lambda: ok(P.probe_read(a.data_ptr(), n16, sink.data_ptr(), groups, s)), GiB),
+        "write": (lambda: ok(P.probe_write(b.data_ptr(), n16, groups, s)), GiB),
+        "copy": (lambda: ok(P.probe_copy(a.data_ptr(), b.data_ptr(), n16, groups, s)), 2 * GiB),
+        "read_write2_linear": (lambda: ok(P.probe_read_write2(
+            a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, 1024, 1024, groups, s)), 3 * GiB),
+    }
+    d = torch.empty(4 * GiB, dtype=torch.uint8, device="cuda")  # 256-byte pieces of 1 KiB rows
+    stream_cases["read_write2_pieces_256_of_1024"] = (lambda: ok(P.probe_read_write2(
+        a.data_ptr(), b.data_ptr(), d.data_ptr(), n16, 256, 1024, groups, s)), 3 * GiB)
+    for name, (fn, nbytes) in stream_cases.items():
+        g = capture(lambda i: fn(), range(1), stream)
+        upload(g, stream)
+        time_graph(g, 2, stream)
+        ms = time_graph(g, 5, stream) / 5
+        res[name] = {"TB/s": round(nbytes / (ms * 1e-3) / 1e12, 3),
+                     "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "ms": round(ms, 3), "bytes": nbytes}
+    del a, b, c, d, sink
+    torch.cuda.empty_cache()
+
+    # Latency floors at the decode launch shape: 512 waves, one per
+    # workgroup; 512 launches per graph, each on its own 512 KiB of input
+    # and output (512 MiB apart from one visit to the next).
+    waves, R = 512, 512
+    src = torch.empty(R * waves * 64 * 16, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty_like(src)
+    g = torch.Generator().manual_seed(5)
+    rows_per_launch = waves
+    table = torch.randint(0, 16384, (R * rows_per_launch, 256), generator=g).to(torch.int32)
+    table[:, 64] = 0
+    table[:, 128] = 0
+    table[:, 192] = 0
+    table = table.to("cuda")
+    meta = torch.arange(R * waves, dtype=torch.int32, device="cuda")
+    data = torch.empty(16384 * 8192 * 16, dtype=torch.uint8, device="cuda").fill_(4)
+    floors = {
+        "empty": lambda i: ok(P.probe_empty(waves, s)),
+        "load_store": lambda i: ok(P.probe_load_store(src.data_ptr() + i * waves * 1024,
+                                                      dst.data_ptr() + i * waves * 1024, waves, s)),
+        "table_row": lambda i: ok(P.probe_chain(
+            None, i * waves, table.data_ptr(), data.data_ptr(),
+            dst.data_ptr() + i * waves * 1024, waves, 0, s)),
+        "table_row_then_3_tap_rows": lambda i: ok(P.probe_chain(
+            None, i * waves, table.data_ptr(), data.data_ptr(),
+            dst.data_ptr() + i * waves * 1024, waves, 3, s)),
+        "meta_then_table_row": lambda i: ok(P.probe_chain(
+            meta.data_ptr() + i * waves * 4, 0, table.data_ptr(), data.data_ptr(),
+            dst.data_ptr() + i * waves * 1024, waves, 0, s)),
+        "meta_table_row_then_3_tap_rows": lambda i: ok(P.probe_chain(
+            meta.data_ptr() + i * waves * 4, 0, table.data_ptr(), data.data_ptr(),
+            dst.data_ptr() + i * waves * 1024, waves, 3, s)),
+    }
+    lat = {}
+    for name, fn in floors.items():
+        gr = capture(fn, range(R), stream)
+        upload(gr, stream)
+        time_graph(gr, 1, stream)
+        lat[name] = round(time_graph(gr, 3, stream) * 1e3 / (3 * R), 3)
+    res["decode_shape_floors_us"] = lat
+    res["decode_shape"] = {"waves": waves, "threads_per_workgroup": 64,
+                           "launches_per_graph": R}
+    return res
+
+
+# ---------------------------------------------------------------- main
+
+def make_workload(name, args):
+    fold = (args.metadata == "folded" or
+            (args.metadata == "auto" and name in ("batched_decode", "spec_decode")))
+    one = (args.stream_launches == "one" or
+           (args.stream_launches == "auto" and name == "decode_layer"))
+    if name == "batched_decode":
+        return DecodeBench(requests=args.requests, fold=fold)
+    if name == "decode_layer":
+        return DecodeLayerBench(requests=args.requests, one_launch=one)
+    if name == "mixed_prefill":
+        return MixedPrefillBench(fold=fold, one_launch=one)
+    if name == "spec_decode":
+        return SpecDecodeBench(fold=fold)
+    return WORKLOADS[name]()
 
 
 def main():
@@ -787,9 +1172,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="batched_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="default", choices=["default"] + sorted(WORKLOADS),
+                    help="default: batched decode, with the mixed prefill in a `prefill` "
+                         "object of the same line")
+    ap.add_argument("--probe", action="store_true",
+                    help="measure this GPU's streaming ceilings and decode-shape latency "
+                         "floors instead (one JSON line)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
-                    help="seconds of oracle time for the CPU baseline (0: skip)")
+                    help="seconds of oracle time per CPU-baseline leg (0: skip)")
     ap.add_argument("--metadata", choices=("auto", "separate", "folded"), default="auto",
                     help="per-row request search: its own sconv_seq_metadata launch per step, "
                          "or inside the fused launch (sconv_fused_insert_conv_qsl); auto picks "
@@ -821,6 +1211,10 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    if args.probe:
+        print(json.dumps(run_probes(stream)), flush=True)
+        return
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -831,99 +1225,34 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: {n} bytes read, {n} bytes written")
         del src, dst, evict
-    fold = (args.metadata == "folded" or
-            (args.metadata == "auto" and args.workload in ("batched_decode", "spec_decode")))
-    one = (args.stream_launches == "one" or
-           (args.stream_launches == "auto" and args.workload == "decode_layer"))
-    if args.workload == "batched_decode":
-        wl = DecodeBench(requests=args.requests, fold=fold)
-    elif args.workload == "decode_layer":
-        wl = DecodeLayerBench(requests=args.requests, one_launch=one)
-    elif args.workload == "mixed_prefill":
-        wl = MixedPrefillBench(fold=fold, one_launch=one)
-    elif args.workload == "spec_decode":
-        wl = WORKLOADS[args.workload](fold=fold)
-    else:
-        wl = WORKLOADS[args.workload]()
-    R = wl.R
-    K = args.steps if args.steps is not None else DEFAULT_STEPS[args.workload]
-    Wm = args.warmup if args.warmup is not None else max(R, K // 50)
 
-    # Touch every replica once eagerly, then capture on a side stream.
-    for i in range(R):
-        wl.step(i)
-    torch.cuda.synchronize()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        g_all = capture(wl.step, range(R))
-        rem = K % R
-        g_rem = capture(wl.step, range(rem)) if rem else None
-        g_kern = capture(wl.kernel, range(R))
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    import depthwise_causal_conv1d_amd as lib
+    lib.sconv_init()
+    name = "batched_decode" if args.workload == "default" else args.workload
 
-    def run_steps(n):
-        for _ in range(n // R):
-            g_all.replay()
-        if n % R:
-            g_rem.replay()
+    def counts(wname):
+        K = args.steps if args.steps is not None else DEFAULT_STEPS[wname]
+        Wm = args.warmup if args.warmup is not None else max(1, K // 50)
+        return K, Wm
 
-    run_steps(Wm - Wm % R if Wm >= R else R)
-    torch.cuda.synchronize()
+    def run(wname):
+        K, Wm = counts(wname)
+        wl = make_workload(wname, args)
+        return measure(wl, wname, K, Wm, max(3, min(200, K // wl.R)), args.cpu_budget, stream)
 
-    # Timed region: exactly K steps.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(K)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # Average duration of one launch of the dominant kernel: graphs holding
-    # only that kernel (R calls per replay), bracketed by HIP events on the
-    # stream the kernels run on.
-    reps = max(3, min(200, K // R))
-    k0 = torch.cuda.Event(enable_timing=True)
-    k1 = torch.cuda.Event(enable_timing=True)
-    k0.record(stream)
-    for _ in range(reps):
-        g_kern.replay()
-    k1.record(stream)
-    torch.cuda.synchronize()
-    launches = reps * R * wl.kernels_per_call()
-    kern_us = k0.elapsed_time(k1) * 1e3 / launches
-    achieved = wl.bytes_per_launch / (kern_us * 1e-6) / 1e9
-
-    cpu = None
-    if args.cpu_budget > 0:
-        v, sample, spent = wl.oracle_sample(args.cpu_budget)
-        cpu = {"value": round(v, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{sample}; {spent:.1f} s single-threaded"}
-
-    traffic = stored_traffic(args.workload)
-    value = wl.tokens_per_step * K / wall
-    line = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": Wm,
-        "ms_per_step": round(wall * 1e3 / K, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic",
-        "config": wl.config(),
-        "roofline": {"bound": wl.bound, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": wl.kernel_name,
-                     "bytes_per_launch": wl.bytes_per_launch, "launch_us": round(kern_us, 3)},
-        "cpu_baseline": cpu,
-        "kernel_sources": kernel_source_digest(),
-    }
+    K, Wm = counts(name)
+    head = run(name)
+    line = {"metric": METRIC, "value": head.pop("value"), "unit": "tokens/s", "n_gpus": 1,
+            "steps": K, "warmup": Wm, "ms_per_step": head.pop("ms_per_step"),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": head.pop("dtype"), "data": "synthetic"}
+    head.pop("steps")
+    head.pop("warmup")
+    line.update(head)
+    if args.workload == "default":
+        torch.cuda.empty_cache()
+        line["prefill"] = {"workload": "mixed_prefill", **run("mixed_prefill")}
+    line["kernel_sources"] = kernel_source_digest()
     print(json.dumps(line), flush=True)
 
 

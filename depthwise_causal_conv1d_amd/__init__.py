@@ -18,6 +18,7 @@ from .ops import (
     sconv_fused_insert_conv_qsl,
     sconv_fused_insert_conv_streams,
     sconv_fused_plan,
+    sconv_init,
     sconv_seq_metadata,
 )
 
@@ -33,5 +34,6 @@ __all__ = [
     "sconv_fused_insert_conv_qsl",
     "sconv_fused_insert_conv_streams",
     "sconv_fused_plan",
+    "sconv_init",
     "sconv_seq_metadata",
 ]

@@ -22,6 +22,7 @@ ACT_NONE, ACT_SILU = 0, 1
 EXPORTS = (
     "sconv_last_error",
     "sconv_version",
+    "sconv_init",
     "sconv_seq_metadata",
     "sconv_fused_insert_conv",
     "sconv_fused_insert_conv_qsl",
@@ -55,6 +56,7 @@ class FusedPlan(ctypes.Structure):
 
 
 _SIGS = {
+    "sconv_init": [],
     "sconv_seq_metadata": [P, I32, I64, I64, P, I64, P, I64, P],
     "sconv_fused_insert_conv": [P, I64, P, I64, I64, P, I64, I32, I32, I32, I64, I64, I64,
                                 P, P, I64, I32, P, P, P, P, I64, I64, I32, I32, I32, I32,

@@ -88,3 +88,18 @@ extern "C" int sconv_seq_metadata(const int32_t* query_start_loc, int32_t num_re
                      seq_idx_out, query_start_out);
   return check_launch("sconv_seq_metadata");
 }
+
+// Load the library's GPU code on the current device.  Launches otherwise
+// load it on first use; a caller that captures its first call into a
+// hipGraph calls this beforehand so that nothing but the launch itself
+// happens inside the capture.  Asking for a kernel's attributes loads the
+// code object holding every kernel of the library.
+extern "C" int sconv_init(void) {
+  sconv::clear_error();
+  hipFuncAttributes attr;
+  const hipError_t e =
+      hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&sconv::seq_metadata_kernel));
+  if (e != hipSuccess)
+    return sconv::fail(SCONV_ERR_HIP, "sconv_init: %s", hipGetErrorString(e));
+  return SCONV_OK;
+}

@@ -54,6 +54,12 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def sconv_init() -> None:
+    """Load the library's GPU code on the current device (before a first
+    call that is captured into a graph)."""
+    _lib.check(_lib.load().sconv_init(), "sconv_init")
+
+
 def sconv_seq_metadata(query_start_loc: torch.Tensor, num_reqs: int, num_actual_tokens: int,
                        seq_idx_out: torch.Tensor, query_start_out: torch.Tensor,
                        num_padded_tokens: Optional[int] = None) -> None:

@@ -49,6 +49,15 @@ const char* sconv_last_error(void);
 const char* sconv_version(void);
 
 /*
+ * Load the library's GPU code on the current device without launching
+ * anything.  Every entry point otherwise loads it at its first launch; a
+ * caller whose first call is captured into a hipGraph calls sconv_init
+ * first, so that the capture records launches only.  Idempotent.
+ * SCONV_ERR_HIP if the runtime cannot load the code (no gfx950 device).
+ */
+int sconv_init(void);
+
+/*
  * sconv_seq_metadata -- per-token request index and request start row.
  *
  * Source: vLLM page "vllm.models.inkling.nvidia.ops.sconv", function

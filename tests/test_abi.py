@@ -280,6 +280,7 @@ for dt, es in ((0, 4), (1, 2)):
         buf(8 * 4096 * es), 8, 4096, 4096, buf(8 * 16), buf(4), 16, buf(16 * 4096 * es), 4096, dt,
         None))
 expect("metadata", lib.sconv_seq_metadata(buf(68), 16, 64, 64, buf(256), 64, buf(256), 64, None))
+expect("init", lib.sconv_init())
 for name, rc in results:
     print(name, rc)
 '''

@@ -16,10 +16,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.mark.gpu
 def test_default_bench_line():
-    print("bench.py --steps 8 --warmup 2 --cpu-budget 0.3 (batched decode)", flush=True)
+    print("bench.py --steps 8 --warmup 2 --cpu-budget 0.3 (decode + prefill)", flush=True)
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "8",
                         "--warmup", "2", "--cpu-budget", "0.3"],
-                       capture_output=True, text=True, timeout=110, cwd=ROOT)
+                       capture_output=True, text=True, timeout=170, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.strip()]
     assert len(lines) == 1, r.stdout
@@ -29,15 +29,25 @@ def test_default_bench_line():
     assert j["higher_is_better"] is True and j["scaling"] == "weak"
     assert j["vs_baseline"] is None and j["data"] == "synthetic" and j["dtype"] == "bf16"
     assert j["config"]["workload"] == "batched_decode" and j["config"]["requests"] == 256
-    assert j["value"] > 0 and j["ms_per_step"] > 0
+    assert j["value"] > 0 and j["ms_per_step"] > 0 and j["wall_ms_per_step"] >= j["ms_per_step"]
     # tokens/s over exactly the timed steps
     assert math.isclose(j["value"], 256 / (j["ms_per_step"] * 1e-3), rel_tol=1e-3)
-    rf = j["roofline"]
-    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
-    assert rf["achieved"] > 0 and math.isclose(rf["frac"], rf["achieved"] / rf["peak"],
-                                                abs_tol=1e-4)
-    assert rf["traffic"] is None or rf["traffic"] > 0
-    assert rf["bytes_per_launch"] == 3161224
-    cpu = j["cpu_baseline"]
-    assert cpu["kind"] == "oracle" and cpu["cores"] == 1 and cpu["value"] > 0
-    assert cpu["unit"] == "tokens/s" and cpu["sample"]
+    for part, nbytes in ((j, 3161224), (j["prefill"], None)):
+        rf = part["roofline"]
+        assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+        assert rf["achieved"] > 0 and math.isclose(rf["frac"], rf["achieved"] / rf["peak"],
+                                                    abs_tol=1e-4)
+        assert rf["traffic"] is None or rf["traffic"] > 0
+        assert rf["frac_trace"] is None or 0 < rf["frac_trace"] < 1
+        if nbytes:
+            assert rf["bytes_per_launch"] == nbytes
+        cpu = part["cpu_baseline"]
+        assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
+        assert cpu["unit"] == "tokens/s" and cpu["sample"] and cpu["cpu_model"]
+        if cpu["cores"] > 1:
+            assert cpu["single_thread"]["value"] > 0
+    p = j["prefill"]
+    assert p["workload"] == "mixed_prefill" and p["steps"] == 8 and p["warmup"] == 2
+    assert p["config"]["streams"] == 4 and p["value"] > 0
+    assert math.isclose(p["value"], p["config"]["non_pad_tokens"] / (p["ms_per_step"] * 1e-3),
+                        rel_tol=1e-3)
