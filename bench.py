@@ -920,6 +920,7 @@ def time_graph(graph, reps, stream):
 
 
 SPIN_CYCLES = 2_000_000   # ~1 ms of spinning ahead of a timed interval
+OTHER_LIB = None          # path of a library other than the in-tree build (--lib)
 
 
 class StepGraphs:
@@ -997,13 +998,14 @@ def measure(wl, name, K, Wm, reps, budget, stream):
     kern_us = graphs.kernel_us(reps)
     extra = wl.extra(stream, reps) if hasattr(wl, "extra") else {}
     achieved = wl.bytes_per_launch / (kern_us * 1e-6) / 1e9
-    trace_us = stored_trace(wl.kernel_name, name)
+    # Stored trace and counter figures describe the in-tree build only.
+    trace_us = None if OTHER_LIB else stored_trace(wl.kernel_name, name)
     roof = {"bound": wl.bound, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "frac_trace": (round(wl.bytes_per_launch / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                            if trace_us else None),
             "headline": "frac: HIP events around graph replays of the kernel alone",
-            "traffic": stored_traffic(name), "kernel": wl.kernel_name,
+            "traffic": None if OTHER_LIB else stored_traffic(name), "kernel": wl.kernel_name,
             "bytes_per_launch": wl.bytes_per_launch, "launch_us": round(kern_us, 3),
             "launch_us_trace": trace_us,
             # the same bytes over the event-timed step, where a step is one
@@ -1192,6 +1194,9 @@ def main():
                          "sconv_fused_insert_conv_streams launch, or one launch per stream; "
                          "auto: one for decode_layer, separate (the configured four calls) "
                          "for mixed_prefill")
+    ap.add_argument("--lib", default=None,
+                    help="measure another build of libsconv.so (one made with "
+                         "`python -m depthwise_causal_conv1d_amd.build --define ... --out PATH`)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "reference for hardware byte counters)")
@@ -1227,6 +1232,10 @@ def main():
         del src, dst, evict
 
     import depthwise_causal_conv1d_amd as lib
+    if args.lib:
+        global OTHER_LIB
+        from depthwise_causal_conv1d_amd import _lib
+        OTHER_LIB = _lib.LIB_PATH = os.path.abspath(args.lib)
     lib.sconv_init()
     name = "batched_decode" if args.workload == "default" else args.workload
 
@@ -1253,6 +1262,8 @@ def main():
         torch.cuda.empty_cache()
         line["prefill"] = {"workload": "mixed_prefill", **run("mixed_prefill")}
     line["kernel_sources"] = kernel_source_digest()
+    if OTHER_LIB:
+        line["library"] = OTHER_LIB
     print(json.dumps(line), flush=True)
 
 

@@ -152,11 +152,30 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_BT_ROW 1  // one-row tiles of decode-shaped launches guess request t
 #endif
 
-// Wave order of a launch: slab-major (consecutive waves walk consecutive
-// tiles of one slab), except for several streams in one-row tiles, which
-// run tile-major.
+#ifndef SCONV_FUSED_MS_ORDER
+#define SCONV_FUSED_MS_ORDER 0  // several streams in multi-row tiles: 0 slab-major,
+                                // 1 stream-inner, 2 tile-major
+#endif
+#ifndef SCONV_FUSED_DECODE_TILE_MAJOR
+#define SCONV_FUSED_DECODE_TILE_MAJOR 0  // one stream in one-row tiles: tile-major
+#endif
+
+// Wave orders.  Slab-major: consecutive waves walk consecutive tiles of one
+// slab.  Tile-major: consecutive waves walk the slabs of one tile.
+// Stream-inner (several streams with the same slab count): consecutive
+// waves walk the streams of one (slab within stream, tile), then the tiles.
+enum { kOrderSlabMajor = 0, kOrderTileMajor = 1, kOrderStreamInner = 2 };
+__host__ __device__ constexpr int wave_order(bool multi_stream, int rows_per_tile) {
+  return !SCONV_FUSED_SLAB_MAJOR ? kOrderTileMajor
+         : (multi_stream && rows_per_tile == 1) ? kOrderTileMajor
+         : (multi_stream && SCONV_FUSED_MS_ORDER == 1) ? kOrderStreamInner
+         : (multi_stream && SCONV_FUSED_MS_ORDER == 2) ? kOrderTileMajor
+         : (!multi_stream && rows_per_tile == 1 && SCONV_FUSED_DECODE_TILE_MAJOR)
+             ? kOrderTileMajor
+             : kOrderSlabMajor;
+}
 __host__ __device__ constexpr bool slab_major_order(bool multi_stream, int rows_per_tile) {
-  return SCONV_FUSED_SLAB_MAJOR && !(multi_stream && rows_per_tile == 1);
+  return wave_order(multi_stream, rows_per_tile) == kOrderSlabMajor;
 }
 
 // Where a row's request and request start come from (template QM).
@@ -231,13 +250,21 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // slabs of all streams for one row are then neighbours on one XCD, and
   // the streams' pieces of a cache row, which share 128-byte lines, meet
   // in one L2.
-  constexpr bool kSlabMajor = slab_major_order(MS, BT);
+  constexpr int kOrder = wave_order(MS, BT);
+  constexpr bool kSlabMajor = kOrder == kOrderSlabMajor;
   uint32_t tile;
   int slab;
   if constexpr (kSlabMajor) {
     const uint32_t slab_u = wave / (uint32_t)p.num_tiles;
     tile = wave - slab_u * (uint32_t)p.num_tiles;
     slab = (int)slab_u;
+  } else if constexpr (kOrder == kOrderStreamInner) {
+    // every stream has num_slabs / num_streams slabs (checked on the host)
+    const uint32_t S = (uint32_t)p.num_streams;
+    const uint32_t rest = wave / S;
+    const uint32_t j = rest / (uint32_t)p.num_tiles;
+    tile = rest - j * (uint32_t)p.num_tiles;
+    slab = (int)((wave - rest * S) * ((uint32_t)p.num_slabs / S) + j);
   } else {
     tile = wave / (uint32_t)p.num_slabs;
     slab = (int)(wave - tile * (uint32_t)p.num_slabs);
@@ -938,6 +965,13 @@ static int fused_launch(
   }
   p.num_slabs = (int32_t)slabs;
   const int bt = pick_bt(T, p.num_slabs);
+  if (num_streams > 1 && wave_order(true, bt) == kOrderStreamInner) {
+    for (int s = 1; s < num_streams; ++s)
+      if (p.st[s].slab0 - p.st[s - 1].slab0 != p.st[1].slab0)
+        return fail(SCONV_ERR_UNSUPPORTED, "%s: this build needs streams of equal width", fn);
+    if (slabs != (int64_t)p.st[1].slab0 * num_streams)
+      return fail(SCONV_ERR_UNSUPPORTED, "%s: this build needs streams of equal width", fn);
+  }
   p.num_tiles = cdiv(T, bt);
   // Decode-shaped launches, where every request has the same small number
   // k of rows (k = 1 when there are no more rows than requests), guess row
