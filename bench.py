@@ -17,9 +17,11 @@ that one run measures the metric's decode and prefill halves.
   decode_layer      the decode batch with all four streams of a layer
                     (ws=32 each) in one sconv_fused_insert_conv_streams launch
   mixed_prefill     the prefill step alone
-  spec_decode       512 requests x 4 draft rows, C=4096, N=32; step = folded
-                    fused launch + conv-window gather, each replica with its
-                    own device-side real_count uniform in [0, 512]
+  spec_decode       512 requests x 4 draft rows, C=4096, N=32; step = the
+                    folded conv and the conv-window gather in one launch
+                    (sconv_fused_insert_conv_gather; --gather-launch separate:
+                    two), each replica with its own device-side real_count
+                    uniform in [0, 512]
   ssm_prefill       8 x 4096 tokens, dim 8192, channel-major, state pool of
                     1024 slots; step = causal_conv1d_varlen_fwd
   ssm_decode        8 rows x dim 8192 against the same pool; step =
@@ -517,19 +519,22 @@ class MixedPrefillBench(Workload):
 
 
 class SpecDecodeBench(Workload):
-    """Speculative decode (512 x 4 drafts) plus the conv-window gather."""
+    """Speculative decode (512 x 4 drafts) plus the conv-window gather, in
+    one launch (sconv_fused_insert_conv_gather) or in two."""
 
     B = 2048
 
-    def __init__(self, dev="cuda", fold: bool = False):
+    def __init__(self, dev="cuda", fold: bool = False, one_launch: bool = True):
         import torch
 
         import depthwise_causal_conv1d_amd as lib
         import workloads
         self.lib = lib
         self.fold = fold
+        self.one_launch = one_launch
         first = workloads.spec_decode()
-        self.bytes_per_launch = fused_algorithmic_bytes(first)
+        self.conv_bytes = fused_algorithmic_bytes(first)
+        self.bytes_per_launch = self.conv_bytes
         self.R = max(2, -(-FLUSH_BYTES // self.bytes_per_launch) + 2)
         t = time.time()
         reqs = 512 * self.R
@@ -554,6 +559,12 @@ class SpecDecodeBench(Workload):
         self.gout = torch.empty(self.R, 512, c.C, 3, dtype=torch.bfloat16, device=dev)
         self.tokens_per_step = self.B
         self.sweep = None
+        if one_launch:
+            # The launch also writes each live slot's window (2 x 4096
+            # channels x 3 rows x 2 bytes) and reads its position; the
+            # windows' source rows are x rows the conv reads anyway.
+            self.bytes_per_launch = self.conv_bytes + int(
+                round(float(self.counts.double().mean()) * (4096 * 3 * 2 + 4))) + 4
 
     def rows(self, i):
         return slice(i * self.B, (i + 1) * self.B)
@@ -561,6 +572,16 @@ class SpecDecodeBench(Workload):
     def kernel(self, i):
         s, c = self.rows(i), self.case
         bt = self.bt[512 * i:512 * (i + 1)]
+        if self.one_launch:
+            meta = (dict(query_start_loc=self.qsl, num_reqs=512) if self.fold
+                    else dict(seq_idx=self.si, query_start=self.qs))
+            x = self.x[s]
+            self.lib.sconv_fused_insert_conv_gather(
+                [x], [self.w], self.cache, self.pos[s], bt, self.sm[s], [c.off_s], [c.ws],
+                c.block_size, x.view(1, self.B, -1), self.gpos, self.rcs[i:i + 1],
+                self.gout[i], 3, activation="silu", use_residual=True, outs=[self.out[s]],
+                **meta)
+            return
         if self.fold:
             self.lib.sconv_fused_insert_conv_qsl(self.x[s], self.w, self.cache, self.pos[s], bt,
                                                  self.qsl, 512, self.sm[s], c.off_s, c.ws,
@@ -574,7 +595,11 @@ class SpecDecodeBench(Workload):
         if not self.fold:
             self.lib.sconv_seq_metadata(self.qsl, 512, self.B, self.si, self.qs, self.B)
         self.kernel(i)
-        self.gather(i, self.rcs[i:i + 1])
+        if not self.one_launch:
+            self.gather(i, self.rcs[i:i + 1])
+
+    def step_is_kernel(self):
+        return self.fold and self.one_launch
 
     def gather(self, i, count):
         self.lib.gather_intermediate_conv_window(self.x[self.rows(i)].view(1, self.B, -1),
@@ -599,6 +624,8 @@ class SpecDecodeBench(Workload):
     def config(self):
         return {"workload": "spec_decode", "requests": 512, "drafts": 4, "tokens_per_step": 2048,
                 "metadata": "folded into the fused launch" if self.fold else "separate launch",
+                "gather_launch": "in the conv's launch (sconv_fused_insert_conv_gather)"
+                if self.one_launch else "its own launch after the conv's",
                 "positions": "uniform[1,131072)", "H": 64, "D": 64, "ws": 64, "C": 4096,
                 "W": 4, "block_size": 32,
                 "gather": {"max_count": 512, "d_conv": 3,
@@ -1165,7 +1192,7 @@ def make_workload(name, args):
     if name == "mixed_prefill":
         return MixedPrefillBench(fold=fold, one_launch=one)
     if name == "spec_decode":
-        return SpecDecodeBench(fold=fold)
+        return SpecDecodeBench(fold=fold, one_launch=args.gather_launch != "separate")
     return WORKLOADS[name]()
 
 
@@ -1194,6 +1221,9 @@ def main():
                          "sconv_fused_insert_conv_streams launch, or one launch per stream; "
                          "auto: one for decode_layer, separate (the configured four calls) "
                          "for mixed_prefill")
+    ap.add_argument("--gather-launch", choices=("same", "separate"), default="same",
+                    help="spec_decode: the window gather in the conv's launch "
+                         "(sconv_fused_insert_conv_gather) or in its own launch after it")
     ap.add_argument("--lib", default=None,
                     help="measure another build of libsconv.so (one made with "
                          "`python -m depthwise_causal_conv1d_amd.build --define ... --out PATH`)")

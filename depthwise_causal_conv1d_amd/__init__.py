@@ -15,6 +15,7 @@ from .ops import (
     gather_intermediate_conv_window,
     gather_intermediate_ssm_state,
     sconv_fused_insert_conv,
+    sconv_fused_insert_conv_gather,
     sconv_fused_insert_conv_qsl,
     sconv_fused_insert_conv_streams,
     sconv_fused_plan,
@@ -31,6 +32,7 @@ __all__ = [
     "gather_intermediate_conv_window",
     "gather_intermediate_ssm_state",
     "sconv_fused_insert_conv",
+    "sconv_fused_insert_conv_gather",
     "sconv_fused_insert_conv_qsl",
     "sconv_fused_insert_conv_streams",
     "sconv_fused_plan",

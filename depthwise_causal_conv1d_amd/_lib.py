@@ -28,6 +28,7 @@ EXPORTS = (
     "sconv_fused_insert_conv_qsl",
     "sconv_fused_insert_conv_streams",
     "sconv_fused_plan",
+    "sconv_fused_insert_conv_gather",
     "causal_conv1d_varlen_fwd",
     "causal_conv1d_update",
     "causal_conv1d_update_tokens",
@@ -52,7 +53,14 @@ class FusedPlan(ctypes.Structure):
     _fields_ = [("lane_elems", I32), ("rows_per_tile", I32), ("request_mode", I32),
                 ("rows_per_request", I32), ("bt_row_entries", I32), ("stream_x_loads", I32),
                 ("stream_hist_loads", I32), ("tile_major", I32), ("wg_threads", I32),
-                ("reserved", I32), ("waves", I64), ("workgroups", I64)]
+                ("gather_mode", I32), ("waves", I64), ("workgroups", I64)]
+
+
+class WindowGather(ctypes.Structure):
+    """sconv_window_gather_t of include/sconv.h (a conditional window gather)."""
+    _fields_ = [("src", P), ("seq_len", I64), ("conv_dim", I32), ("src_stride_s", I64),
+                ("src_stride_c", I64), ("abs_positions", P), ("real_count", P),
+                ("max_count", I32), ("out", P), ("out_slot_stride", I64), ("d_conv", I32)]
 
 
 _SIGS = {
@@ -69,7 +77,10 @@ _SIGS = {
                                         I32, I32, P],
     "sconv_fused_plan": [ctypes.POINTER(StreamT), I32, P, I64, I32, I32, I32, I64, I64, I64,
                          P, P, I64, I32, P, P, P, I32, P, I64, I32, I32,
-                         ctypes.POINTER(FusedPlan)],
+                         ctypes.POINTER(WindowGather), ctypes.POINTER(FusedPlan)],
+    "sconv_fused_insert_conv_gather": [ctypes.POINTER(StreamT), I32, P, I64, I32, I32, I32, I64,
+                                       I64, I64, P, P, I64, I32, P, P, P, I32, P, I64, I32, I32,
+                                       ctypes.POINTER(WindowGather), P],
     "causal_conv1d_varlen_fwd": [P, I64, I64, P, I64, I64, P, P, I64, I64, I64, I64, P, I32,
                                  P, P, P, I64, I64, I32, I64, I32, I32, I32, I32, P],
     "causal_conv1d_update": [P, I64, P, I64, I64, I64, I64, P, I64, I64, P, P, P, P, I64,

@@ -31,8 +31,11 @@
 //     rounding by v_cvt_pk_bf16_f32 (round to nearest even);
 //   * the grid depends only on T and C, so the decode path replays under a
 //     hipGraph without any data-dependent shape.
+#include "gather_window.h"
 #include "sconv_device.h"
 #include "sconv_host.h"
+
+#include <type_traits>
 
 namespace sconv {
 
@@ -78,6 +81,20 @@ struct FusedParams {
   int64_t cs0, cs1, cs2, bt_rs, T;
   int64_t num_tiles;
   FusedStream st[kMaxStreams];
+};
+
+// A fused launch that also runs a conditional window gather: workgroups
+// [0, num_groups) are the conv's, the next g_groups the gather's, one per
+// (slot, channel block) item in slot-major order.  The conv's come first:
+// its one generation of waves starts its latency chains at once, and the
+// gather's workgroups take the room its resident waves leave, then its
+// tail.  (Measured on the 512 x 4-draft step: 16.0 us per launch; gather
+// workgroups first 18.2 us; a few gather workgroups looping over the items
+// beside the conv 17.0 us; two launches 18.3 us.)
+struct FusedGatherParams : FusedParams {
+  GatherParams g;
+  int32_t g_dc;      // window length d_conv, 1..4
+  uint32_t g_groups;
 };
 
 // Request of row t: the last r in [0, n) with off[r] <= t (rows past the
@@ -204,8 +221,30 @@ static_assert(kQslRegMax <= 512, "8 offsets per lane");
 // NTX: input rows loaded as streaming (non-temporal) reads.  MS: several
 // streams, each wave finding its own (one-stream launches read entry 0).
 // NTH: history rows loaded as streaming reads.
-template <typename D, int VEC, int W, int BT, int QM, bool NTX, bool MS, bool NTH = false>
-__global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kernel(const FusedParams p) {
+// GW: the launch also runs a window gather in workgroups past the conv's
+// (parameters FusedGatherParams).
+template <typename D, int VEC, int W, int BT, int QM, bool NTX, bool MS, bool NTH = false,
+          bool GW = false>
+__global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kernel(
+    const std::conditional_t<GW, FusedGatherParams, FusedParams> p) {
+  if constexpr (GW) {
+    // Gather workgroups come after every conv workgroup, so the hardware
+    // hands them out as the conv's resident waves leave room: they fill the
+    // conv's latency gaps.  Their inputs are never written by the conv.
+    __shared__ GatherChunk g_lds[kGatherLdsChunks];
+    if (blockIdx.x >= p.num_groups) {
+      const uint32_t it = blockIdx.x - p.num_groups;
+      const uint32_t cbs = (uint32_t)p.g.cblocks;
+      const int slot = (int)(it / cbs), cb = (int)(it - (it / cbs) * cbs);
+      switch (p.g_dc) {
+        case 1: gather_window_body<D, VEC, 1>(p.g, slot, cb, g_lds); break;
+        case 2: gather_window_body<D, VEC, 2>(p.g, slot, cb, g_lds); break;
+        case 3: gather_window_body<D, VEC, 3>(p.g, slot, cb, g_lds); break;
+        default: gather_window_body<D, VEC, 4>(p.g, slot, cb, g_lds); break;
+      }
+      return;
+    }
+  }
   using S = typename D::storage;
   using P = Pack<D, VEC>;
   S* __restrict__ cache = static_cast<S*>(p.cache);
@@ -778,6 +817,47 @@ static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipS
   }
 }
 
+// Conv + window gather in one launch: built for one-generation conv launches
+// (16-byte lanes, four-row tiles, streaming input loads), where the
+// gather's workgroups can fill the conv's latency gaps.
+template <typename D, int VEC, int W, bool MS>
+static void launch_gw(const FusedGatherParams& p, uint32_t grid, uint32_t threads,
+                      hipStream_t s) {
+  if constexpr (VEC > 1) {
+    if constexpr (W > 1) {
+      if (p.guess) {
+        hipLaunchKernelGGL(
+            (fused_insert_conv_kernel<D, VEC, W, 4, kQslGuess, true, MS, false, true>),
+            dim3(grid), dim3(threads), 0, s, p);
+        return;
+      }
+    }
+    if (p.qsl && p.num_reqs <= kQslRegMax) {
+      hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, 4, kQslRegs, true, MS, false, true>),
+                         dim3(grid), dim3(threads), 0, s, p);
+    } else if (p.qsl) {
+      hipLaunchKernelGGL(
+          (fused_insert_conv_kernel<D, VEC, W, 4, kQslSearch, true, MS, false, true>),
+          dim3(grid), dim3(threads), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, 4, kQslOff, true, MS, false, true>),
+                         dim3(grid), dim3(threads), 0, s, p);
+    }
+  }
+}
+
+template <typename D, int VEC>
+static void launch_gw_w(int W, const FusedGatherParams& p, uint32_t g, uint32_t th,
+                        hipStream_t s) {
+  const bool ms = p.num_streams > 1;
+  switch (W) {
+    case 1: ms ? launch_gw<D, VEC, 1, true>(p, g, th, s) : launch_gw<D, VEC, 1, false>(p, g, th, s); break;
+    case 2: ms ? launch_gw<D, VEC, 2, true>(p, g, th, s) : launch_gw<D, VEC, 2, false>(p, g, th, s); break;
+    case 3: ms ? launch_gw<D, VEC, 3, true>(p, g, th, s) : launch_gw<D, VEC, 3, false>(p, g, th, s); break;
+    default: ms ? launch_gw<D, VEC, 4, true>(p, g, th, s) : launch_gw<D, VEC, 4, false>(p, g, th, s); break;
+  }
+}
+
 template <typename D, int VEC, int W, int BT, bool MS>
 static void launch_n(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
   // Streaming history loads are built for one-row tiles (decode).
@@ -870,7 +950,8 @@ static int fused_launch(
     const int64_t* positions, const int32_t* block_table, int64_t bt_row_stride,
     int32_t max_blocks, const int32_t* seq_idx, const int32_t* query_start, const int32_t* qsl,
     int32_t num_reqs, const int64_t* slot_mapping, int64_t T, int32_t W, int32_t dtype,
-    hipStream_t stream, sconv_fused_plan_t* plan = nullptr) {
+    hipStream_t stream, sconv_fused_plan_t* plan = nullptr,
+    const sconv_window_gather_t* gather = nullptr) {
   if (T < 0) return fail(SCONV_ERR_INVALID, "%s: T < 0", fn);
   if (!valid_dtype(dtype)) return fail(SCONV_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
   if (W < 1 || W > 4) return fail(SCONV_ERR_INVALID, "%s: W=%d outside [1, 4]", fn, W);
@@ -911,8 +992,52 @@ static int fused_launch(
           q.x_row_stride % vec16 == 0 && q.out_row_stride % vec16 == 0 && aligned16(q.x) &&
           aligned16(q.out);
   }
+  // The window gather, when one comes with the call: its own checks, and
+  // none of its bytes may meet what the conv writes (out, cache), nor may
+  // its output meet what the conv reads.
+  GatherParams gp = {};
+  int gvec = 1;
+  bool g_empty = true;
+  const int64_t es_ = elem_size(dtype);
+  if (gather) {
+    const sconv_window_gather_t& g = *gather;
+    const int rc = gather_window_setup(fn, g.src, g.seq_len, g.conv_dim, g.src_stride_s,
+                                       g.src_stride_c, g.abs_positions, g.real_count,
+                                       g.max_count, g.out, g.out_slot_stride, g.d_conv, dtype, 0,
+                                       &gp, &gvec, &g_empty);
+    if (rc != SCONV_OK) return rc;
+    if (!g_empty) {
+      const int64_t gs_bytes =
+          ((g.seq_len - 1) * g.src_stride_s + (int64_t)(g.conv_dim - 1) * g.src_stride_c + 1) * es_;
+      const int64_t go_bytes =
+          ((int64_t)(g.max_count - 1) * g.out_slot_stride + (int64_t)g.conv_dim * g.d_conv) * es_;
+      const int64_t c_bytes_ = ((num_blocks - 1) * cs0 + (H - 1) * cs1 + (N - 1) * cs2 + D) * es_;
+      bool bad = overlap(g.out, go_bytes, g.src, gs_bytes) ||
+                 (T > 0 && (overlap(g.out, go_bytes, cache, c_bytes_) ||
+                            overlap(g.src, gs_bytes, cache, c_bytes_)));
+      for (int s = 0; s < num_streams && T > 0; ++s) {
+        const int64_t x_bytes = ((T - 1) * streams[s].x_row_stride + C[s]) * es_;
+        const int64_t o_bytes = ((T - 1) * streams[s].out_row_stride + C[s]) * es_;
+        bad = bad || overlap(g.out, go_bytes, streams[s].x, x_bytes) ||
+              overlap(g.out, go_bytes, streams[s].out, o_bytes) ||
+              overlap(g.src, gs_bytes, streams[s].out, o_bytes);
+      }
+      if (bad)
+        return fail(SCONV_ERR_INVALID,
+                    "%s: the gather's output overlaps its source or the conv's buffers, or "
+                    "its source overlaps what the conv writes", fn);
+    }
+  }
   if (T == 0) {
-    if (plan) *plan = sconv_fused_plan_t{};
+    if (plan) {
+      *plan = sconv_fused_plan_t{};
+      plan->gather_mode = g_empty ? 0 : 2;
+      return SCONV_OK;
+    }
+    if (!g_empty) {
+      gather_window_launch(gp, gvec, gather->d_conv, dtype, stream);
+      return check_launch(fn);
+    }
     return SCONV_OK;
   }
   if (!cache || !positions || !block_table || !slot_mapping ||
@@ -1017,7 +1142,22 @@ static int fused_launch(
   p.nt_hist = SCONV_FUSED_NT_HIST && bt == 1 && widest * es < 128;
   p.waves_per_group = (int32_t)(threads / 64);
 
+  // The gather runs in the conv's launch when this configuration has a
+  // combined kernel: a one-generation conv in four-row tiles with 16-byte
+  // lanes, and a gather on 16-byte lanes too; otherwise it is launched
+  // right after the conv, on the same stream.
+  const bool combined = !g_empty && VEC > 1 && bt == 4 && p.nt_x && gvec == VEC;
+  if (combined) {
+    gp.threads = (int32_t)threads;
+    gp.cblocks = (int32_t)cdiv(gp.conv_dim, (int64_t)threads * VEC);
+  }
+  // One gather workgroup per (slot, channel block) item.
+  const int64_t g_groups = combined ? (int64_t)gp.cblocks * gp.max_count : 0;
+  if (grid + g_groups > INT32_MAX)
+    return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
+
   if (plan) {
+    plan->gather_mode = g_empty ? 0 : combined ? 1 : 2;
     plan->lane_elems = VEC;
     plan->rows_per_tile = bt;
     plan->request_mode = p.guess ? kQslGuess
@@ -1030,8 +1170,20 @@ static int fused_launch(
     plan->tile_major = !slab_major_order(num_streams > 1, bt);
     plan->wg_threads = (int32_t)threads;
     plan->waves = waves;
-    plan->workgroups = grid;
+    plan->workgroups = grid + g_groups;
     return SCONV_OK;
+  }
+
+  if (combined) {
+    FusedGatherParams q;
+    static_cast<FusedParams&>(q) = p;
+    q.g = gp;
+    q.g_dc = gather->d_conv;
+    q.g_groups = (uint32_t)g_groups;
+    const uint32_t all = (uint32_t)(grid + g_groups);
+    if (dtype == SCONV_BF16) launch_gw_w<Bf16, 8>(W, q, all, threads, stream);
+    else launch_gw_w<F32, 4>(W, q, all, threads, stream);
+    return check_launch(fn);
   }
 
   if (dtype == SCONV_BF16) {
@@ -1040,6 +1192,11 @@ static int fused_launch(
   } else {
     if (VEC == 4) launch_w<F32, 4>(W, bt, p, (uint32_t)grid, threads, stream);
     else launch_w<F32, 1>(W, bt, p, (uint32_t)grid, threads, stream);
+  }
+  if (!g_empty) {
+    const int rc = check_launch(fn);
+    if (rc != SCONV_OK) return rc;
+    gather_window_launch(gp, gvec, gather->d_conv, dtype, stream);
   }
   return check_launch(fn);
 }
@@ -1113,13 +1270,33 @@ extern "C" int sconv_fused_insert_conv_streams(
                              stream);
 }
 
+extern "C" int sconv_fused_insert_conv_gather(
+    const sconv_stream_t* streams, int32_t num_streams, void* cache, int64_t num_blocks,
+    int32_t H, int32_t N, int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
+    const int64_t* positions, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t max_blocks, const int32_t* seq_idx, const int32_t* query_start,
+    const int32_t* query_start_loc, int32_t num_reqs, const int64_t* slot_mapping, int64_t T,
+    int32_t W, int32_t dtype, const sconv_window_gather_t* gather, hipStream_t stream) {
+  const char* fn = "sconv_fused_insert_conv_gather";
+  sconv::clear_error();
+  if (!gather) return sconv::fail(SCONV_ERR_INVALID, "%s: NULL gather", fn);
+  const bool per_row = seq_idx || query_start;
+  if (per_row == (query_start_loc != nullptr))
+    return sconv::fail(SCONV_ERR_INVALID,
+                       "%s: give either seq_idx and query_start, or query_start_loc", fn);
+  return sconv::fused_launch(fn, streams, num_streams, cache, num_blocks, H, N, D, cs0, cs1,
+                             cs2, positions, block_table, bt_row_stride, max_blocks, seq_idx,
+                             query_start, query_start_loc, num_reqs, slot_mapping, T, W, dtype,
+                             stream, nullptr, gather);
+}
+
 extern "C" int sconv_fused_plan(
     const sconv_stream_t* streams, int32_t num_streams, void* cache, int64_t num_blocks,
     int32_t H, int32_t N, int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
     const int64_t* positions, const int32_t* block_table, int64_t bt_row_stride,
     int32_t max_blocks, const int32_t* seq_idx, const int32_t* query_start,
     const int32_t* query_start_loc, int32_t num_reqs, const int64_t* slot_mapping, int64_t T,
-    int32_t W, int32_t dtype, sconv_fused_plan_t* plan) {
+    int32_t W, int32_t dtype, const sconv_window_gather_t* gather, sconv_fused_plan_t* plan) {
   const char* fn = "sconv_fused_plan";
   sconv::clear_error();
   if (!plan) return sconv::fail(SCONV_ERR_INVALID, "%s: NULL plan", fn);
@@ -1130,5 +1307,5 @@ extern "C" int sconv_fused_plan(
   return sconv::fused_launch(fn, streams, num_streams, cache, num_blocks, H, N, D, cs0, cs1,
                              cs2, positions, block_table, bt_row_stride, max_blocks, seq_idx,
                              query_start, query_start_loc, num_reqs, slot_mapping, T, W, dtype,
-                             nullptr, plan);
+                             nullptr, plan, gather);
 }

@@ -218,17 +218,22 @@ def sconv_fused_plan(xs: Sequence[torch.Tensor], weights: Sequence[torch.Tensor]
                      query_start: Optional[torch.Tensor] = None,
                      query_start_loc: Optional[torch.Tensor] = None,
                      num_reqs: Optional[int] = None,
-                     outs: Optional[Sequence[torch.Tensor]] = None) -> dict:
-    """The launch sconv_fused_insert_conv_streams would make for these
-    arguments, as a dict of the plan's fields; nothing is launched."""
+                     outs: Optional[Sequence[torch.Tensor]] = None,
+                     gather: Optional[tuple] = None) -> dict:
+    """The launch sconv_fused_insert_conv_streams (or, with ``gather`` =
+    (src, abs_positions, real_count_gpu, out, d_conv),
+    sconv_fused_insert_conv_gather) would make for these arguments, as a
+    dict of the plan's fields; nothing is launched."""
     if outs is None:
         outs = [torch.empty_like(x) for x in xs]
     plan = _lib.FusedPlan()
     args = _streams_args(xs, weights, cache, positions, block_table, slot_mapping, off_s, ws,
                          block_size, activation, use_residual, seq_idx, query_start,
                          query_start_loc, num_reqs, outs)
+    g = None if gather is None else _window_gather(*gather)[0]
     if args is not None:
-        rc = _lib.load().sconv_fused_plan(*args, ctypes.byref(plan))
+        rc = _lib.load().sconv_fused_plan(*args, None if g is None else ctypes.byref(g),
+                                          ctypes.byref(plan))
         _lib.check(rc, "sconv_fused_plan")
     return {name: getattr(plan, name) for name, _ in _lib.FusedPlan._fields_}
 
@@ -418,6 +423,15 @@ def gather_intermediate_conv_window(src: torch.Tensor, abs_positions: torch.Tens
     """Gather length-d_conv windows of src[0] ending before abs_positions
     into out [max_count, conv_dim, d_conv] for the first real_count slots
     (count read on the device)."""
+    g, dt = _window_gather(src, abs_positions, real_count_gpu, out, d_conv)
+    rc = _lib.load().gather_intermediate_conv_window(
+        g.src, g.seq_len, g.conv_dim, g.src_stride_s, g.src_stride_c, g.abs_positions,
+        g.real_count, g.max_count, g.out, g.out_slot_stride, g.d_conv, dt, _stream(src))
+    _lib.check(rc, "gather_intermediate_conv_window")
+
+
+def _window_gather(src, abs_positions, real_count_gpu, out, d_conv):
+    """Checked sconv_window_gather_t of a window gather, and its dtype code."""
     if src.dim() != 3 or out.dim() != 3:
         raise ValueError("src [batch, seq_len, conv_dim], out [max_count, conv_dim, d_conv]")
     _dev(src, abs_positions, real_count_gpu, out)
@@ -431,10 +445,43 @@ def gather_intermediate_conv_window(src: torch.Tensor, abs_positions: torch.Tens
         raise ValueError("out slots must be dense (conv_dim, d_conv)")
     _vec(abs_positions, torch.int32, "abs_positions", max_count)
     _vec(real_count_gpu, torch.int32, "real_count_gpu", 1)
-    rc = _lib.load().gather_intermediate_conv_window(
-        _ptr(src), src.shape[1], conv_dim, src.stride(1), src.stride(2), _ptr(abs_positions),
-        _ptr(real_count_gpu), max_count, _ptr(out), out.stride(0), d_conv, dt, _stream(src))
-    _lib.check(rc, "gather_intermediate_conv_window")
+    g = _lib.WindowGather(_ptr(src), src.shape[1], conv_dim, src.stride(1), src.stride(2),
+                          _ptr(abs_positions), _ptr(real_count_gpu), max_count, _ptr(out),
+                          out.stride(0), d_conv)
+    return g, dt
+
+
+def sconv_fused_insert_conv_gather(xs: Sequence[torch.Tensor], weights: Sequence[torch.Tensor],
+                                   cache: torch.Tensor, positions: torch.Tensor,
+                                   block_table: torch.Tensor, slot_mapping: torch.Tensor,
+                                   off_s: Sequence[int], ws: Sequence[int], block_size: int,
+                                   gather_src: torch.Tensor, abs_positions: torch.Tensor,
+                                   real_count_gpu: torch.Tensor, gather_out: torch.Tensor,
+                                   d_conv: int, activation=None, use_residual=True,
+                                   seq_idx: Optional[torch.Tensor] = None,
+                                   query_start: Optional[torch.Tensor] = None,
+                                   query_start_loc: Optional[torch.Tensor] = None,
+                                   num_reqs: Optional[int] = None,
+                                   outs: Optional[Sequence[torch.Tensor]] = None
+                                   ) -> List[torch.Tensor]:
+    """sconv_fused_insert_conv_streams and gather_intermediate_conv_window
+    (gather_src, abs_positions, real_count_gpu, gather_out, d_conv) in one
+    launch.  Returns the conv outputs; gather_out is written in place."""
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    g, gdt = _window_gather(gather_src, abs_positions, real_count_gpu, gather_out, d_conv)
+    args = _streams_args(xs, weights, cache, positions, block_table, slot_mapping, off_s, ws,
+                         block_size, activation, use_residual, seq_idx, query_start,
+                         query_start_loc, num_reqs, outs)
+    if args is None:  # no rows: the gather alone
+        gather_intermediate_conv_window(gather_src, abs_positions, real_count_gpu, gather_out,
+                                        d_conv)
+        return list(outs)
+    if gdt != args[-1]:
+        raise TypeError("the gather and the conv must share one element type")
+    rc = _lib.load().sconv_fused_insert_conv_gather(*args, ctypes.byref(g), _stream(xs[0]))
+    _lib.check(rc, "sconv_fused_insert_conv_gather")
+    return list(outs)
 
 
 def gather_intermediate_ssm_state(states: torch.Tensor, chunk_indices: torch.Tensor,

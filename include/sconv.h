@@ -272,11 +272,31 @@ typedef struct sconv_fused_plan {
   int32_t stream_hist_loads; /* history rows loaded as streaming reads */
   int32_t tile_major;        /* wave order: 0 slab-major, 1 tile-major */
   int32_t wg_threads;        /* workgroup size */
-  int32_t reserved;
+  int32_t gather_mode;       /* window gather: 0 none, 1 in the conv's launch,
+                                2 its own launch right after the conv's */
   int64_t waves;             /* tiles x slabs */
-  int64_t workgroups;        /* grid size */
+  int64_t workgroups;        /* grid size (with the gather's, if in it) */
 } sconv_fused_plan_t;
 
+/*
+ * sconv_window_gather_t -- the arguments of gather_intermediate_conv_window
+ * (same names, meaning, layout and contract; the element type is the
+ * fused call's), for sconv_fused_insert_conv_gather and sconv_fused_plan.
+ */
+typedef struct sconv_window_gather {
+  const void* src;                /* [seq_len, conv_dim] rows (batch 0) */
+  int64_t seq_len;
+  int32_t conv_dim;
+  int64_t src_stride_s, src_stride_c;
+  const int32_t* abs_positions;   /* int32 [max_count] */
+  const int32_t* real_count;      /* int32 [1], read on the device */
+  int32_t max_count;
+  void* out;                      /* [max_count, conv_dim, d_conv] */
+  int64_t out_slot_stride;
+  int32_t d_conv;
+} sconv_window_gather_t;
+
+/* `gather` may be NULL (a plain fused call). */
 int sconv_fused_plan(const sconv_stream_t* streams, int32_t num_streams, void* cache,
                      int64_t num_blocks, int32_t H, int32_t N, int32_t D, int64_t cs0,
                      int64_t cs1, int64_t cs2, const int64_t* positions,
@@ -284,7 +304,45 @@ int sconv_fused_plan(const sconv_stream_t* streams, int32_t num_streams, void* c
                      const int32_t* seq_idx, const int32_t* query_start,
                      const int32_t* query_start_loc, int32_t num_reqs,
                      const int64_t* slot_mapping, int64_t T, int32_t W, int32_t dtype,
-                     sconv_fused_plan_t* plan);
+                     const sconv_window_gather_t* gather, sconv_fused_plan_t* plan);
+
+/*
+ * sconv_fused_insert_conv_gather -- a speculative-decode step in one launch:
+ * the insert + conv of sconv_fused_insert_conv_streams and the conditional
+ * window gather of gather_intermediate_conv_window.
+ *
+ * Sources: vLLM page "vllm.models.inkling.nvidia.ops.sconv", fused_sconv;
+ * Megatron-core page "core.ssm.ops.intermediate_extraction",
+ * scatter_intermediate_conv (parameters) and its kernel.  The results are
+ * exactly those of the two calls in turn: the gather reads only its source
+ * rows (usually the conv's x), which the conv never writes.
+ *
+ * The conv's workgroups come first in the grid and the gather's after them
+ * (one per live-or-dead slot and channel block, the count read on the
+ * device as in gather_intermediate_conv_window), so gather workgroups run
+ * in the room the conv's resident waves leave.  Configurations without a
+ * combined kernel (see sconv_fused_plan_t.gather_mode) launch the gather
+ * right after the conv on the same stream, with the same results.
+ *
+ *   streams ... dtype   as sconv_fused_insert_conv_streams
+ *   gather              as gather_intermediate_conv_window (host struct,
+ *                       read during the call); max_count == 0 or
+ *                       conv_dim == 0: no gather
+ *
+ * Host errors (SCONV_ERR_INVALID / _UNSUPPORTED): those of both calls; the
+ * gather's out overlapping its source or any buffer of the conv; the
+ * gather's source overlapping the cache or any stream's out.
+ */
+int sconv_fused_insert_conv_gather(const sconv_stream_t* streams, int32_t num_streams,
+                                   void* cache, int64_t num_blocks, int32_t H, int32_t N,
+                                   int32_t D, int64_t cs0, int64_t cs1, int64_t cs2,
+                                   const int64_t* positions, const int32_t* block_table,
+                                   int64_t bt_row_stride, int32_t max_blocks,
+                                   const int32_t* seq_idx, const int32_t* query_start,
+                                   const int32_t* query_start_loc, int32_t num_reqs,
+                                   const int64_t* slot_mapping, int64_t T, int32_t W,
+                                   int32_t dtype, const sconv_window_gather_t* gather,
+                                   hipStream_t stream);
 
 /*
  * causal_conv1d_varlen_fwd -- causal depthwise conv over packed

@@ -260,6 +260,13 @@ for dt, es in ((0, 4), (1, 2)):
                        lib.sconv_fused_insert_conv_streams(
                            arr, 2, cache, 64, H, 16, D, H * 16 * D, 16 * D, D, pos, bt, 300, 300,
                            None if q else si, None if q else qs, q, R, sm, T, 4, dt, None))
+        # conv + window gather over the conv's x, in one launch or two
+        g = _lib.WindowGather(x, T, C, C, 1, buf(64 * 4), buf(4), 64, buf(64 * C * 3 * es),
+                              C * 3, 3)
+        arr1 = (StreamT * 1)(StreamT(x, C, w, 4, 1, out, C, 0, ws, 1, 1))
+        expect(f"conv+gather dt{dt} T{T} R{R}", lib.sconv_fused_insert_conv_gather(
+            arr1, 1, cache, 64, H, 16, D, H * 16 * D, 16 * D, D, pos, bt, 300, 300, None, None,
+            qsl, R, sm, T, 4, dt, ctypes.byref(g), None))
     dim = 64
     xs, st = buf(dim * 4096 * es), buf(16 * dim * 3 * es)
     expect(f"varlen dt{dt}", lib.causal_conv1d_varlen_fwd(
@@ -309,15 +316,18 @@ def test_host_paths_reach_the_launch(tmp_path):
     assert not bad, f"expected the launch error (3) everywhere, got {bad}"
 
 
+# A 16-byte-aligned stand-in address: the plan query never dereferences
+# its pointers, so the buffers are placed at fixed offsets from it.
+STAND_IN = 1 << 24
+
+
 def _plan(lib, T, num_reqs, H=32, ws=32, D=128, N=16, max_blocks=257, folded=True, W=4,
-          streams=1, dt=1):
-    """sconv_fused_plan on stand-in host addresses (16-byte aligned, never
+          streams=1, dt=1, gather=None):
+    """sconv_fused_plan on stand-in addresses (16-byte aligned, never
     dereferenced): returns (rc, plan)."""
     from depthwise_causal_conv1d_amd import _lib
-    es = 2 if dt == 1 else 4
     C = H * ws
-    big = (ctypes.c_uint8 * (1 << 16))()
-    base = (ctypes.addressof(big) + 15) & ~15
+    base = STAND_IN
     # x, out of each stream and the cache at distant stand-in addresses
     arr = (_lib.StreamT * streams)()
     for s in range(streams):
@@ -328,6 +338,7 @@ def _plan(lib, T, num_reqs, H=32, ws=32, D=128, N=16, max_blocks=257, folded=Tru
     meta = (None, None, base, num_reqs) if folded else (base, base, None, 0)
     rc = lib.sconv_fused_plan(arr, streams, cache, 1 << 16, H, N, D, H * N * D, N * D, D, base,
                               base, max_blocks, max_blocks, *meta, base, T, W, dt,
+                              None if gather is None else ctypes.byref(gather),
                               ctypes.byref(plan))
     return rc, plan
 
@@ -378,3 +389,61 @@ def test_plan_shapes_of_the_benchmarked_launches(lib):
     rc, p = _plan(lib, 0, 1)
     assert rc == 0 and p.waves == 0 and p.workgroups == 0
     assert _plan(lib, 10, 2, W=5)[0] == 1 and b"W=5" in lib.sconv_last_error()
+
+
+def _gather_struct(conv_dim=4096, max_count=512, d_conv=3, seq_len=2048, src_ss=4096,
+                   src_sc=1, dt=1):
+    from depthwise_causal_conv1d_amd import _lib
+    base = STAND_IN
+    src = base + (1 << 46)          # far from every conv buffer of _plan
+    out = base + (1 << 47)
+    return _lib.WindowGather(src, seq_len, conv_dim, src_ss, src_sc, base, base, max_count,
+                             out, conv_dim * d_conv, d_conv)
+
+
+def test_plan_conv_and_gather_in_one_launch(lib):
+    """The speculative step's shape (one generation of four-row tiles,
+    16-byte lanes on both sides) runs the gather's workgroups in the conv's
+    launch, after the conv's; other shapes launch it after the conv; an
+    empty gather is no gather."""
+    rc, plain = _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097)
+    rc, p = _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097,
+                  gather=_gather_struct())
+    assert rc == 0, lib.sconv_last_error()
+    assert p.gather_mode == 1 and p.wg_threads == 256
+    # one gather workgroup per item (2 x 512: 4096 channels in 256-thread
+    # groups of 8-channel lanes)
+    assert p.workgroups == plain.workgroups + 1024 and plain.gather_mode == 0
+    rc, p = _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097,
+                  gather=_gather_struct(max_count=21))
+    assert rc == 0 and p.workgroups == plain.workgroups + 42
+    # decode shape (one-row tiles): its own launch after the conv
+    rc, p = _plan(lib, 256, 256, gather=_gather_struct(conv_dim=1024, seq_len=256, src_ss=1024))
+    assert rc == 0 and p.gather_mode == 2 and p.workgroups == 512
+    # a gather whose source rows are not 16-byte lanes: separate launch
+    rc, p = _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097,
+                  gather=_gather_struct(src_ss=4097))
+    assert rc == 0 and p.gather_mode == 2
+    # nothing to gather
+    rc, p = _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097,
+                  gather=_gather_struct(max_count=0))
+    assert rc == 0 and p.gather_mode == 0
+    # no rows: the gather alone
+    rc, p = _plan(lib, 0, 512, gather=_gather_struct())
+    assert rc == 0 and p.gather_mode == 2 and p.workgroups == 0
+
+
+def test_combined_entry_rejects_bad_gathers(lib):
+    assert _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097,
+                 gather=_gather_struct(d_conv=5))[0] == 2
+    assert b"d_conv=5" in lib.sconv_last_error()
+    assert _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097,
+                 gather=_gather_struct(seq_len=0))[0] == 1
+    # the gather writing over the conv's input rows
+    g = _gather_struct()
+    rc, plan = _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097, gather=g)
+    assert rc == 0
+    g.out = STAND_IN + (1 << 40)     # stream 0's x in _plan
+    assert _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097,
+                 gather=g)[0] == 1
+    assert b"overlaps" in lib.sconv_last_error()

@@ -1012,6 +1012,159 @@ def test_gather_graph_replay_with_device_count():
         assert_bits_equal(to_np(out), out_r, f"replay n={n}")
 
 
+# ------------------------------------------------------------------ conv + gather, one launch
+
+def check_conv_gather(cases, gc, what, fold=True, expect_mode=1):
+    """sconv_fused_insert_conv_gather against the oracle's two ops: every
+    stream's output, the cache (referenced blocks bit for bit, the others
+    still NaN), and the gathered windows bit for bit (dead slots keep their
+    sentinel).  The gather reads the first stream's x."""
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    c0 = cases[0]
+    say(f"conv+gather {what}: {len(cases)} streams T={c0.T} C={c0.C} "
+        f"real_count={gc.real_count} d_conv={gc.d_conv} folded={fold}")
+    xs = [c.x.to(DEV) for c in cases]
+    ws_ = [c.weight.to(DEV) for c in cases]
+    cache = c0.cache.to(DEV).clone()
+    pos, bt, sm = c0.positions.to(DEV), c0.block_table.to(DEV), c0.slot_mapping.to(DEV)
+    qsl = c0.query_start_loc.to(DEV)
+    outs = [torch.full_like(x, SENTINEL) for x in xs]
+    src = xs[0].view(1, c0.T, c0.C)
+    gpos = gc.abs_positions.to(DEV)
+    rc = torch.tensor([gc.real_count], dtype=torch.int32, device=DEV)
+    gout = gc.out_init.to(DEV).clone()
+    kw = dict(activation=[c.activation for c in cases],
+              use_residual=[c.use_residual for c in cases], outs=outs)
+    if fold:
+        kw.update(query_start_loc=qsl, num_reqs=c0.num_reqs)
+    else:
+        si = torch.empty(c0.T, dtype=torch.int32, device=DEV)
+        qs = torch.empty_like(si)
+        lib.sconv_seq_metadata(qsl, c0.num_reqs, c0.num_actual, si, qs, c0.T)
+        kw.update(seq_idx=si, query_start=qs)
+    args = (xs, ws_, cache, pos, bt, sm, [c.off_s for c in cases], [c.ws for c in cases],
+            c0.block_size)
+    plan = lib.sconv_fused_plan(*args, gather=(src, gpos, rc, gout, gc.d_conv), **kw)
+    assert plan["gather_mode"] == expect_mode, plan
+    lib.sconv_fused_insert_conv_gather(*args, src, gpos, rc, gout, gc.d_conv, **kw)
+    torch.cuda.synchronize()
+    cc, btc, smc = c0.compact()
+    outs_r, cache_r = oracle_fused_streams(cases, cache=cc, block_table=btc, slot_mapping=smc)
+    live = live_rows(c0)
+    for i, (og, orf) in enumerate(zip(outs, outs_r)):
+        ogh = to_np(og)
+        assert_close(ogh, orf, dtype_name(c0.x.dtype), f"{what} stream {i} out", mask=live)
+        assert_bits_equal(ogh[~live], orf[~live], f"{what} stream {i} PAD rows untouched")
+    ids = c0.used_blocks.to(DEV)
+    got = to_np(cache[ids])
+    assert_bits_equal(got, cache_r, f"{what} referenced blocks")
+    untouched = torch.ones(cache.shape[0], dtype=torch.bool, device=DEV)
+    untouched[ids] = False
+    if untouched.any():
+        assert torch.isnan(cache[untouched].float()).all(), "write outside referenced blocks"
+    g_r = oracle.gather_conv_window(to_np(gc.src), to_np(gc.abs_positions), gc.real_count,
+                                    to_np(gc.out_init), gc.d_conv)
+    g_h = to_np(gout)
+    assert_bits_equal(g_h, g_r, f"{what} gathered windows")
+    n = max(0, min(gc.real_count, gc.out_init.shape[0]))
+    assert_finite(g_h[:n], f"{what} live gathered windows")
+
+
+@pytest.mark.parametrize("real_count", [0, 1, 256, 512, 600, -4])
+def test_spec_step_in_one_launch(real_count):
+    """The benchmarked speculative step at full size (512 requests x 4
+    drafts, C=4096, N=32, bf16) with the window gather of its x (max_count
+    512, d_conv 3) in the conv's launch."""
+    case = workloads.spec_decode()
+    gc = workloads.spec_gather(case, real_count=real_count)
+    check_conv_gather([case], gc, f"spec step, {real_count} live")
+
+
+@pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
+def test_conv_gather_four_streams_f32_and_small_windows(fold):
+    """Four streams in one launch with the gather (one generation of
+    four-row tiles), and an fp32 launch with d_conv 1, 2 and 4."""
+    g = torch.Generator().manual_seed(95)
+    ctx = [int(v) for v in torch.randint(1, 2000, (512,), generator=g)]
+    cases = workloads.fused_streams_case(95, [4] * 512, ctx, H=8, D=512,
+                                         streams=[(0, 128), (128, 128), (256, 128), (384, 128)],
+                                         block_size=16, W=4, dtype=torch.bfloat16, pad_count=20)
+    gc = workloads.gather_case(96, cases[0].x.view(1, cases[0].T, cases[0].C), max_count=300,
+                               d_conv=3)
+    check_conv_gather(cases, gc, "four streams", fold=fold)
+    for dc, W in ((1, 4), (2, 3), (4, 2)):
+        # 1024 requests x 4 rows of 1024 fp32 channels: 4096 waves of four-row tiles
+        ctx = [int(v) for v in torch.randint(1, 500, (1024,), generator=g)]
+        c = workloads.fused_case(97 + dc, [4] * 1024, ctx, H=16, D=96, ws=64, off_s=16,
+                                 block_size=16, W=W, dtype=torch.float32, pad_count=9)
+        gc = workloads.gather_case(98 + dc, c.x.view(1, c.T, c.C), max_count=200, d_conv=dc)
+        check_conv_gather([c], gc, f"f32 W={W} d_conv={dc}", fold=fold)
+
+
+def test_conv_gather_falls_back_to_two_launches():
+    """Shapes without a combined kernel (one-row decode tiles; a one-channel
+    conv) launch the gather after the conv, with the same results."""
+    case = workloads.batched_decode(seed=21)
+    gc = workloads.gather_case(22, case.x.view(1, case.T, case.C), max_count=100, d_conv=3,
+                               stride=2)
+    check_conv_gather([case], gc, "decode shape", expect_mode=2)
+    c = workloads.fused_case(23, [4] * 64, [5] * 64, H=3, D=16, ws=6, off_s=2, block_size=8,
+                             W=4, dtype=torch.bfloat16)
+    gc = workloads.gather_case(24, c.x.view(1, c.T, c.C), max_count=40, d_conv=3, stride=4)
+    check_conv_gather([c], gc, "one-channel conv", expect_mode=2)
+
+
+def test_spec_step_in_one_launch_graph_replay():
+    """The one-launch speculative step captured once and replayed with new
+    live counts written into its device buffer: each replay's windows
+    equal the oracle's, and the conv's output does not depend on them."""
+    import depthwise_causal_conv1d_amd as lib
+    import oracle
+    case = workloads.spec_decode()
+    gc = workloads.spec_gather(case, real_count=0)
+    x = case.x.to(DEV)
+    w = case.weight.to(DEV)
+    cache0 = case.cache.to(DEV)
+    cache = cache0.clone()
+    pos, bt, sm = case.positions.to(DEV), case.block_table.to(DEV), case.slot_mapping.to(DEV)
+    qsl = case.query_start_loc.to(DEV)
+    out = torch.full_like(x, SENTINEL)
+    src = x.view(1, case.T, case.C)
+    gpos = gc.abs_positions.to(DEV)
+    rc = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gout = gc.out_init.to(DEV).clone()
+
+    def step():
+        lib.sconv_fused_insert_conv_gather([x], [w], cache, pos, bt, sm, [0], [case.ws],
+                                           case.block_size, src, gpos, rc, gout, 3,
+                                           activation="silu", use_residual=True,
+                                           query_start_loc=qsl, num_reqs=case.num_reqs,
+                                           outs=[out])
+    lib.sconv_init()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    cc, btc, smc = case.compact()
+    out_r, _, _, _ = oracle_fused(case, cache=cc, block_table=btc, slot_mapping=smc)
+    live = live_rows(case)
+    g = torch.Generator().manual_seed(98)
+    for n in [0, 512, 7] + [int(v) for v in torch.randint(0, 513, (3,), generator=g)]:
+        cache.copy_(cache0)
+        out.fill_(SENTINEL)
+        gout.copy_(gc.out_init.to(DEV))
+        rc.fill_(n)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_close(to_np(out), out_r, "bf16", f"replay n={n} out", mask=live)
+        g_r = oracle.gather_conv_window(to_np(gc.src), to_np(gc.abs_positions), n,
+                                        to_np(gc.out_init), 3)
+        assert_bits_equal(to_np(gout), g_r, f"replay n={n} windows")
+        say(f"  replay n={n} ok")
+
+
 # ------------------------------------------------------------------ SSM-state row gather
 
 SSM_GATHER = [
