@@ -156,6 +156,9 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #ifndef SCONV_FUSED_XCD_ORDER
 #define SCONV_FUSED_XCD_ORDER 1
 #endif
+#ifndef SCONV_FUSED_XCD_ONE_ROW
+#define SCONV_FUSED_XCD_ONE_ROW 0  // XCD runs for one-row slab-major tiles too
+#endif
 #ifndef SCONV_FUSED_WG_THREADS
 #define SCONV_FUSED_WG_THREADS 256
 #endif
@@ -267,16 +270,21 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   constexpr bool kRowAhead = kGuess && BT == 1;  // block-table row read ahead
   if constexpr (kGuess) asm volatile("" ::"s"(p.k_magic), "s"(p.k_s1), "s"(p.k_s2));
   if constexpr (kRowAhead) asm volatile("" ::"s"(p.bt), "s"(p.bt_rs), "s"(p.bt_pref));
+  constexpr int kOrder = wave_order(MS, BT);
+  constexpr bool kSlabMajor = kOrder == kOrderSlabMajor;
+  // Workgroups are renumbered so that each XCD runs one contiguous range of
+  // waves (neighbouring tiles share halo rows, streams' pieces share cache
+  // lines) -- except one-row tiles in slab-major order, where neighbours
+  // share nothing and the hardware's round-robin puts the slabs of one row,
+  // which read the same block-table row, on the same XCD.
+  constexpr bool kXcdRuns = SCONV_FUSED_XCD_ORDER && (BT > 1 || !kSlabMajor || SCONV_FUSED_XCD_ONE_ROW);
   const int lane = threadIdx.x & 63;
   // The launch geometry comes in the parameters (loaded with them in one
   // batch) rather than from the implicit arguments, which would cost a
   // second dependent round trip before any data load could start.
   // Wave counts are below 2^31 (checked on the host): 32-bit arithmetic.
-#if SCONV_FUSED_XCD_ORDER
-  uint32_t wave = xcd_contiguous(blockIdx.x, p.num_groups) * (uint32_t)p.waves_per_group +
-#else
-  uint32_t wave = blockIdx.x * (uint32_t)p.waves_per_group +
-#endif
+  uint32_t wave = (kXcdRuns ? xcd_contiguous(blockIdx.x, p.num_groups) : blockIdx.x) *
+                      (uint32_t)p.waves_per_group +
                   (uint32_t)uniform(threadIdx.x >> 6);
   // A wave past the end works on the last tile and writes nothing (no early
   // return: it would split the parameter loads around the branch).
@@ -289,8 +297,6 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // slabs of all streams for one row are then neighbours on one XCD, and
   // the streams' pieces of a cache row, which share 128-byte lines, meet
   // in one L2.
-  constexpr int kOrder = wave_order(MS, BT);
-  constexpr bool kSlabMajor = kOrder == kOrderSlabMajor;
   uint32_t tile;
   int slab;
   if constexpr (kSlabMajor) {
