@@ -145,7 +145,8 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_NT_LOADS_MAX_WAVES 5120  // streaming x loads up to this many waves
 #endif
 #ifndef SCONV_FUSED_GROUP_STORES
-#define SCONV_FUSED_GROUP_STORES 0
+#define SCONV_FUSED_GROUP_STORES 2  // stores after all rows' arithmetic: 0 never, 1 always,
+                                    // 2 in multi-generation launches (no streaming x loads)
 #endif
 #ifndef SCONV_FUSED_LDS_HALO
 #define SCONV_FUSED_LDS_HALO 1  // halo rows passed between the waves of a workgroup
@@ -234,16 +235,18 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     // Gather workgroups come after every conv workgroup, so the hardware
     // hands them out as the conv's resident waves leave room: they fill the
     // conv's latency gaps.  Their inputs are never written by the conv.
-    __shared__ GatherChunk g_lds[kGatherLdsChunks];
+    // the gather body's staging, one kGatherLdsWave slice per wave
+    __shared__ GatherChunk g_lds[(SCONV_FUSED_WG_THREADS / 64) * kGatherLdsWave];
+    constexpr bool kGNt = SCONV_FUSED_GATHER_NT_LOADS;
     if (blockIdx.x >= p.num_groups) {
       const uint32_t it = blockIdx.x - p.num_groups;
       const uint32_t cbs = (uint32_t)p.g.cblocks;
       const int slot = (int)(it / cbs), cb = (int)(it - (it / cbs) * cbs);
       switch (p.g_dc) {
-        case 1: gather_window_body<D, VEC, 1>(p.g, slot, cb, g_lds); break;
-        case 2: gather_window_body<D, VEC, 2>(p.g, slot, cb, g_lds); break;
-        case 3: gather_window_body<D, VEC, 3>(p.g, slot, cb, g_lds); break;
-        default: gather_window_body<D, VEC, 4>(p.g, slot, cb, g_lds); break;
+        case 1: gather_window_body<D, VEC, 1, kGNt>(p.g, slot, cb, g_lds); break;
+        case 2: gather_window_body<D, VEC, 2, kGNt>(p.g, slot, cb, g_lds); break;
+        case 3: gather_window_body<D, VEC, 3, kGNt>(p.g, slot, cb, g_lds); break;
+        default: gather_window_body<D, VEC, 4, kGNt>(p.g, slot, cb, g_lds); break;
       }
       return;
     }
@@ -278,6 +281,12 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // share nothing and the hardware's round-robin puts the slabs of one row,
   // which read the same block-table row, on the same XCD.
   constexpr bool kXcdRuns = SCONV_FUSED_XCD_ORDER && (BT > 1 || !kSlabMajor || SCONV_FUSED_XCD_ONE_ROW);
+  // Stores of multi-row tiles after all rows' arithmetic (in row order)
+  // rather than after each row's: measured faster in the many-generation
+  // prefill launches, slower in one-generation launches (streaming x loads),
+  // where the first row's stores then wait behind every row's history.
+  constexpr bool kGroupStores =
+      BT > 1 && (SCONV_FUSED_GROUP_STORES == 1 || (SCONV_FUSED_GROUP_STORES == 2 && !NTX));
   const int lane = threadIdx.x & 63;
   // The launch geometry comes in the parameters (loaded with them in one
   // batch) rather than from the implicit arguments, which would cost a
@@ -654,9 +663,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
       }
     }
     outv[i].from_float(y);
-#if !SCONV_FUSED_GROUP_STORES
-    store_row(i);
-#endif
+    if constexpr (!kGroupStores) store_row(i);
   };
 
 
@@ -793,11 +800,11 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     }
     finish(i, acc);
   }
-#if SCONV_FUSED_GROUP_STORES
+  if constexpr (kGroupStores) {
 #pragma unroll
-  for (int i = 0; i < BT; ++i)
-    if (slot[i] >= 0) store_row(i);
-#endif
+    for (int i = 0; i < BT; ++i)
+      if (slot[i] >= 0) store_row(i);
+  }
 }
 
 // ---------------------------------------------------------------- dispatch

@@ -24,10 +24,16 @@
 #define SCONV_GATHER_NT_STORES_LDS 1  // streaming stores for the 1 KB runs
 #endif
 // Neighbouring slots' windows overlap, so source rows are read again
-// through L2: streaming reads measured 25% slower (4.9 -> 6.1 us on the
-// 512-slot spec-decode extraction).
+// through L2: in the gather's own launch streaming reads measured slower
+// (5.14 -> 6.42 us with all 512 slots of the spec-decode extraction live).
+// Inside the conv's launch they measured faster (15.90 -> 15.73 us per
+// speculative step): there the conv's streaming input reads have already
+// passed the rows by.
 #ifndef SCONV_GATHER_NT_LOADS
-#define SCONV_GATHER_NT_LOADS 0  // streaming reads of the source rows
+#define SCONV_GATHER_NT_LOADS 0  // streaming reads of the source rows (own launch)
+#endif
+#ifndef SCONV_FUSED_GATHER_NT_LOADS
+#define SCONV_FUSED_GATHER_NT_LOADS 1  // the same, in the conv's launch
 #endif
 
 namespace sconv {
@@ -61,16 +67,17 @@ void gather_window_launch(const GatherParams& p, int vec, int d_conv, int32_t dt
 // LDS a gather workgroup stages its stores in: per wave, 64 lanes x up to
 // four 16-byte chunks (bf16 lanes of 8 channels x d_conv <= 4 taps).  One
 // array serves every d_conv, so a kernel holding several bodies reserves it
-// once.
+// once: kGatherLdsWave chunks per wave of the workgroup.
 typedef uint32_t GatherChunk __attribute__((ext_vector_type(4)));
 constexpr int kGatherLdsWave = 64 * 4;
-constexpr int kGatherLdsChunks = (256 / 64) * kGatherLdsWave;
+constexpr int kGatherLdsChunks = (256 / 64) * kGatherLdsWave;  // the gather's own 256-thread groups
 
-// The gather of one (channel block, slot) workgroup of up to 256 threads,
-// staging through `lds` (kGatherLdsChunks chunks).  It uses neither
+// The gather of one (channel block, slot) workgroup, staging through `lds`
+// (kGatherLdsWave chunks for each of its waves).  It uses neither
 // workgroup barriers nor the grid shape, so a larger kernel can run it in
 // some of its workgroups.
-template <typename D, int VEC, int DC>
+// NTL: source rows loaded as streaming reads.
+template <typename D, int VEC, int DC, bool NTL = SCONV_GATHER_NT_LOADS>
 __device__ __forceinline__ void gather_window_body(const GatherParams& p, int slot, int cb,
                                                    GatherChunk* lds) {
   using S = typename D::storage;
@@ -109,11 +116,8 @@ __device__ __forceinline__ void gather_window_body(const GatherParams& p, int sl
     row = row < 0 ? 0 : (row > p.seq_len - 1 ? p.seq_len - 1 : row);
     Pack<D, VEC> pk;
     if constexpr (VEC > 1) {
-#if SCONV_GATHER_NT_LOADS
-      pk.load_nt(src + row * p.src_ss + c0);
-#else
-      pk.load(src + row * p.src_ss + c0);
-#endif
+      if constexpr (NTL) pk.load_nt(src + row * p.src_ss + c0);
+      else pk.load(src + row * p.src_ss + c0);
     } else {
       pk.raw = __builtin_bit_cast(typename Pack<D, 1>::raw_t, src[row * p.src_ss + (int64_t)c0 * p.src_sc]);
     }
