@@ -948,6 +948,7 @@ def time_graph(graph, reps, stream):
 
 SPIN_CYCLES = 2_000_000   # ~1 ms of spinning ahead of a timed interval
 OTHER_LIB = None          # path of a library other than the in-tree build (--lib)
+PROFILED_FORM = True      # the run uses the launch forms the committed profiles were taken on
 
 
 class StepGraphs:
@@ -1025,14 +1026,16 @@ def measure(wl, name, K, Wm, reps, budget, stream):
     kern_us = graphs.kernel_us(reps)
     extra = wl.extra(stream, reps) if hasattr(wl, "extra") else {}
     achieved = wl.bytes_per_launch / (kern_us * 1e-6) / 1e9
-    # Stored trace and counter figures describe the in-tree build only.
-    trace_us = None if OTHER_LIB else stored_trace(wl.kernel_name, name)
+    # Stored trace and counter figures describe the in-tree build, in the
+    # default launch forms and batch size, only.
+    stored = PROFILED_FORM and not OTHER_LIB
+    trace_us = stored_trace(wl.kernel_name, name) if stored else None
     roof = {"bound": wl.bound, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "frac_trace": (round(wl.bytes_per_launch / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                            if trace_us else None),
             "headline": "frac: HIP events around graph replays of the kernel alone",
-            "traffic": None if OTHER_LIB else stored_traffic(name), "kernel": wl.kernel_name,
+            "traffic": stored_traffic(name) if stored else None, "kernel": wl.kernel_name,
             "bytes_per_launch": wl.bytes_per_launch, "launch_us": round(kern_us, 3),
             "launch_us_trace": trace_us,
             # the same bytes over the event-timed step, where a step is one
@@ -1262,6 +1265,9 @@ def main():
         del src, dst, evict
 
     import depthwise_causal_conv1d_amd as lib
+    global PROFILED_FORM
+    PROFILED_FORM = (args.metadata == "auto" and args.stream_launches == "auto" and
+                     args.gather_launch == "same" and args.requests == 256)
     if args.lib:
         global OTHER_LIB
         from depthwise_causal_conv1d_amd import _lib
