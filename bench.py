@@ -54,7 +54,10 @@ trace of the same command (profiles/), where tracing adds its own handling
 to every dispatch, and is null once the kernel sources have changed since.
 `cpu_baseline` times the oracle on a bounded sample of the same workload,
 on every host core the process may use (rows or channels split across
-threads) and single-threaded.
+threads) and single-threaded.  The default line's `machine` object gives
+what the same GPU reaches, in the same run, on the reference kernels of
+bench_probes.hip: the copy and the prefill's write patterns (TB/s) and
+the decode kernel's dependent chain at its launch shape (us).
 """
 from __future__ import annotations
 
@@ -1083,11 +1086,8 @@ def build_probes(verbose=False) -> str:
     return PROBE_LIB
 
 
-def run_probes(stream):
-    """Streaming ceilings and latency floors of this GPU (one JSON line)."""
+def _probe_lib():
     import ctypes
-
-    import torch
     if not os.path.exists(PROBE_LIB):
         raise ImportError(f"{PROBE_LIB} is missing: build it with `python -c 'import bench; "
                           "bench.build_probes()'` (or __graft_entry__.build())")
@@ -1100,33 +1100,37 @@ def run_probes(stream):
     P.probe_empty.argtypes = [I32, V]
     P.probe_load_store.argtypes = [V, V, I32, V]
     P.probe_chain.argtypes = [V, I32, V, V, V, I32, I32, V]
-    s = stream.cuda_stream
-    res = {"workload": "probe", "peak_GBs": HBM_PEAK_GBS}
+    return P
 
-    def ok(rc):
-        if rc != 0:
-            raise RuntimeError(f"probe launch failed ({rc})")
 
-    # Streaming ceilings: 1 GiB per stream, 32768 workgroups; each launch
-    # timed over graph replays, the buffers far larger than the MALL.
+def _ok(rc):
+    if rc != 0:
+        raise RuntimeError(f"probe launch failed ({rc})")
+
+
+def stream_ceilings(P, stream, names):
+    """TB/s of the streaming reference kernels `names` (1 GiB per stream,
+    32768 workgroups), each timed with HIP events over graph replays."""
+    import torch
     GiB = 1 << 30
-    n16 = GiB // 16
-    groups = 32768
+    n16, groups, s = GiB // 16, 32768, stream.cuda_stream
     a = torch.empty(GiB, dtype=torch.uint8, device="cuda").fill_(1)
     b = torch.empty(GiB, dtype=torch.uint8, device="cuda")
     c = torch.empty(GiB, dtype=torch.uint8, device="cuda")
-    sink = torch.empty(groups * 256 * 16, dtype=torch.uint8, device="cuda")
-    stream_cases = {
-        "read": (lambda: ok(P.probe_read(a.data_ptr(), n16, sink.data_ptr(), groups, s)), GiB),
-        "write": (lambda: ok(P.probe_write(b.data_ptr(), n16, groups, s)), GiB),
-        "copy": (lambda: ok(P.probe_copy(a.data_ptr(), b.data_ptr(), n16, groups, s)), 2 * GiB),
-        "read_write2_linear": (lambda: ok(P.probe_read_write2(
-            a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, 1024, 1024, groups, s)), 3 * GiB),
-    }
     d = torch.empty(4 * GiB, dtype=torch.uint8, device="cuda")  # 256-byte pieces of 1 KiB rows
-    stream_cases["read_write2_pieces_256_of_1024"] = (lambda: ok(P.probe_read_write2(
-        a.data_ptr(), b.data_ptr(), d.data_ptr(), n16, 256, 1024, groups, s)), 3 * GiB)
-    for name, (fn, nbytes) in stream_cases.items():
+    sink = torch.empty(groups * 256 * 16, dtype=torch.uint8, device="cuda")
+    cases = {
+        "read": (lambda: _ok(P.probe_read(a.data_ptr(), n16, sink.data_ptr(), groups, s)), GiB),
+        "write": (lambda: _ok(P.probe_write(b.data_ptr(), n16, groups, s)), GiB),
+        "copy": (lambda: _ok(P.probe_copy(a.data_ptr(), b.data_ptr(), n16, groups, s)), 2 * GiB),
+        "read_write2_linear": (lambda: _ok(P.probe_read_write2(
+            a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, 1024, 1024, groups, s)), 3 * GiB),
+        "read_write2_pieces_256_of_1024": (lambda: _ok(P.probe_read_write2(
+            a.data_ptr(), b.data_ptr(), d.data_ptr(), n16, 256, 1024, groups, s)), 3 * GiB),
+    }
+    res = {}
+    for name in names:
+        fn, nbytes = cases[name]
         g = capture(lambda i: fn(), range(1), stream)
         upload(g, stream)
         time_graph(g, 2, stream)
@@ -1136,49 +1140,87 @@ def run_probes(stream):
                      "ms": round(ms, 3), "bytes": nbytes}
     del a, b, c, d, sink
     torch.cuda.empty_cache()
+    return res
 
-    # Latency floors at the decode launch shape: 512 waves, one per
-    # workgroup; 512 launches per graph, each on its own 512 KiB of input
-    # and output (512 MiB apart from one visit to the next).
-    waves, R = 512, 512
+
+def decode_floors(P, stream, names):
+    """µs per launch of the latency probes `names` at the decode launch
+    shape: 512 waves, one per workgroup; 512 launches per graph, each on its
+    own 512 KiB of input and output."""
+    import torch
+    waves, R, s = 512, 512, stream.cuda_stream
     src = torch.empty(R * waves * 64 * 16, dtype=torch.uint8, device="cuda").fill_(3)
     dst = torch.empty_like(src)
     g = torch.Generator().manual_seed(5)
-    rows_per_launch = waves
-    table = torch.randint(0, 16384, (R * rows_per_launch, 256), generator=g).to(torch.int32)
+    # table rows name blocks of `data` in entry 0; entries 64, 128, 192 are 0
+    table = torch.randint(0, 16384, (R * waves, 256), generator=g).to(torch.int32)
     table[:, 64] = 0
     table[:, 128] = 0
     table[:, 192] = 0
     table = table.to("cuda")
     meta = torch.arange(R * waves, dtype=torch.int32, device="cuda")
     data = torch.empty(16384 * 8192 * 16, dtype=torch.uint8, device="cuda").fill_(4)
-    floors = {
-        "empty": lambda i: ok(P.probe_empty(waves, s)),
-        "load_store": lambda i: ok(P.probe_load_store(src.data_ptr() + i * waves * 1024,
-                                                      dst.data_ptr() + i * waves * 1024, waves, s)),
-        "table_row": lambda i: ok(P.probe_chain(
+    probes = {
+        "empty": lambda i: _ok(P.probe_empty(waves, s)),
+        "load_store": lambda i: _ok(P.probe_load_store(src.data_ptr() + i * waves * 1024,
+                                                       dst.data_ptr() + i * waves * 1024,
+                                                       waves, s)),
+        "table_row": lambda i: _ok(P.probe_chain(
             None, i * waves, table.data_ptr(), data.data_ptr(),
             dst.data_ptr() + i * waves * 1024, waves, 0, s)),
-        "table_row_then_3_tap_rows": lambda i: ok(P.probe_chain(
+        "table_row_then_3_tap_rows": lambda i: _ok(P.probe_chain(
             None, i * waves, table.data_ptr(), data.data_ptr(),
             dst.data_ptr() + i * waves * 1024, waves, 3, s)),
-        "meta_then_table_row": lambda i: ok(P.probe_chain(
+        "meta_then_table_row": lambda i: _ok(P.probe_chain(
             meta.data_ptr() + i * waves * 4, 0, table.data_ptr(), data.data_ptr(),
             dst.data_ptr() + i * waves * 1024, waves, 0, s)),
-        "meta_table_row_then_3_tap_rows": lambda i: ok(P.probe_chain(
+        "meta_table_row_then_3_tap_rows": lambda i: _ok(P.probe_chain(
             meta.data_ptr() + i * waves * 4, 0, table.data_ptr(), data.data_ptr(),
             dst.data_ptr() + i * waves * 1024, waves, 3, s)),
     }
     lat = {}
-    for name, fn in floors.items():
-        gr = capture(fn, range(R), stream)
+    for name in names:
+        gr = capture(probes[name], range(R), stream)
         upload(gr, stream)
         time_graph(gr, 1, stream)
         lat[name] = round(time_graph(gr, 3, stream) * 1e3 / (3 * R), 3)
-    res["decode_shape_floors_us"] = lat
-    res["decode_shape"] = {"waves": waves, "threads_per_workgroup": 64,
-                           "launches_per_graph": R}
+    del src, dst, table, meta, data
+    torch.cuda.empty_cache()
+    return lat
+
+
+def run_probes(stream):
+    """Streaming ceilings and latency floors of this GPU (one JSON line)."""
+    P = _probe_lib()
+    res = {"workload": "probe", "peak_GBs": HBM_PEAK_GBS}
+    res.update(stream_ceilings(P, stream, ["read", "write", "copy", "read_write2_linear",
+                                           "read_write2_pieces_256_of_1024"]))
+    res["decode_shape_floors_us"] = decode_floors(
+        P, stream, ["empty", "load_store", "table_row", "table_row_then_3_tap_rows",
+                    "meta_then_table_row", "meta_table_row_then_3_tap_rows"])
+    res["decode_shape"] = {"waves": 512, "threads_per_workgroup": 64, "launches_per_graph": 512}
     return res
+
+
+def machine_reference(stream):
+    """What the same GPU reaches on the headline's patterns, for the default
+    line: the copy and the mixed prefill's write patterns (TB/s), and the
+    decode kernel's dependent chain at its launch shape (µs).  None when the
+    probe kernels are not built."""
+    try:
+        P = _probe_lib()
+    except ImportError as e:
+        log(f"machine reference skipped: {e}")
+        return None
+    c = stream_ceilings(P, stream, ["copy", "read_write2_linear",
+                                    "read_write2_pieces_256_of_1024"])
+    f = decode_floors(P, stream, ["empty", "table_row_then_3_tap_rows"])
+    return {"source": "bench_probes.hip in this run (bench.py --probe measures all)",
+            "copy_TBs": c["copy"]["TB/s"],
+            "prefill_pattern_linear_TBs": c["read_write2_linear"]["TB/s"],
+            "prefill_pattern_TBs": c["read_write2_pieces_256_of_1024"]["TB/s"],
+            "empty_launch_us": f["empty"],
+            "decode_chain_floor_us": f["table_row_then_3_tap_rows"]}
 
 
 # ---------------------------------------------------------------- main
@@ -1297,6 +1339,17 @@ def main():
     if args.workload == "default":
         torch.cuda.empty_cache()
         line["prefill"] = {"workload": "mixed_prefill", **run("mixed_prefill")}
+        torch.cuda.empty_cache()
+        m = machine_reference(stream)
+        if m is not None:
+            # the kernels against what this GPU reaches on their patterns
+            line["roofline"]["floor_us"] = m["decode_chain_floor_us"]
+            line["roofline"]["launch_over_floor"] = round(
+                line["roofline"]["launch_us"] / m["decode_chain_floor_us"], 3)
+            pr = line["prefill"]["roofline"]
+            pr["ceiling_GBs"] = round(m["prefill_pattern_TBs"] * 1e3, 1)
+            pr["frac_of_ceiling"] = round(pr["achieved"] / pr["ceiling_GBs"], 4)
+        line["machine"] = m
     line["kernel_sources"] = kernel_source_digest()
     if OTHER_LIB:
         line["library"] = OTHER_LIB

@@ -46,6 +46,12 @@ def test_default_bench_line():
         assert cpu["unit"] == "tokens/s" and cpu["sample"] and cpu["cpu_model"]
         if cpu["cores"] > 1:
             assert cpu["single_thread"]["value"] > 0
+    m = j["machine"]  # the probe kernels are built with the library
+    assert 1.0 < m["copy_TBs"] < 8.0 and 1.0 < m["prefill_pattern_TBs"] < 8.0
+    assert 0 < m["empty_launch_us"] < m["decode_chain_floor_us"]
+    assert math.isclose(j["roofline"]["launch_over_floor"],
+                        j["roofline"]["launch_us"] / m["decode_chain_floor_us"], rel_tol=1e-2)
+    assert j["prefill"]["roofline"]["frac_of_ceiling"] > 0
     p = j["prefill"]
     assert p["workload"] == "mixed_prefill" and p["steps"] == 8 and p["warmup"] == 2
     assert p["config"]["streams"] == 4 and p["value"] > 0
