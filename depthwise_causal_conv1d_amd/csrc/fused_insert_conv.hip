@@ -1031,10 +1031,21 @@ static int fused_launch(
       for (int s = 0; s < num_streams && T > 0; ++s) {
         const int64_t x_bytes = ((T - 1) * streams[s].x_row_stride + C[s]) * es_;
         const int64_t o_bytes = ((T - 1) * streams[s].out_row_stride + C[s]) * es_;
+        const int64_t w_bytes =
+            ((C[s] - 1) * streams[s].w_stride_c + (int64_t)(W - 1) * streams[s].w_stride_k + 1) *
+            es_;
         bad = bad || overlap(g.out, go_bytes, streams[s].x, x_bytes) ||
               overlap(g.out, go_bytes, streams[s].out, o_bytes) ||
+              overlap(g.out, go_bytes, streams[s].weight, w_bytes) ||
               overlap(g.src, gs_bytes, streams[s].out, o_bytes);
       }
+      // ... nor the conv's per-row metadata
+      if (T > 0)
+        bad = bad || overlap(g.out, go_bytes, positions, T * 8) ||
+              overlap(g.out, go_bytes, slot_mapping, T * 8) ||
+              overlap(g.out, go_bytes, seq_idx, seq_idx ? T * 4 : 0) ||
+              overlap(g.out, go_bytes, query_start, query_start ? T * 4 : 0) ||
+              overlap(g.out, go_bytes, qsl, qsl ? ((int64_t)num_reqs + 1) * 4 : 0);
       if (bad)
         return fail(SCONV_ERR_INVALID,
                     "%s: the gather's output overlaps its source or the conv's buffers, or "

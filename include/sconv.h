@@ -330,8 +330,11 @@ int sconv_fused_plan(const sconv_stream_t* streams, int32_t num_streams, void* c
  *                       conv_dim == 0: no gather
  *
  * Host errors (SCONV_ERR_INVALID / _UNSUPPORTED): those of both calls; the
- * gather's out overlapping its source or any buffer of the conv; the
- * gather's source overlapping the cache or any stream's out.
+ * gather's out overlapping its source, the cache, any stream's x, weight
+ * or out, or the conv's per-row metadata (positions, slot_mapping,
+ * seq_idx, query_start, query_start_loc); the gather's source overlapping
+ * the cache or any stream's out.  (The block table is not checked: its
+ * row count is known only to the caller.)
  */
 int sconv_fused_insert_conv_gather(const sconv_stream_t* streams, int32_t num_streams,
                                    void* cache, int64_t num_blocks, int32_t H, int32_t N,

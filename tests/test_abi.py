@@ -447,3 +447,7 @@ def test_combined_entry_rejects_bad_gathers(lib):
     assert _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097,
                  gather=g)[0] == 1
     assert b"overlaps" in lib.sconv_last_error()
+    g.out = STAND_IN                 # the weights, positions and metadata in _plan
+    assert _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097,
+                 gather=g)[0] == 1
+    assert b"overlaps" in lib.sconv_last_error()
