@@ -1,0 +1,67 @@
+"""bench.py's host logic on the CPU: the kernel-source digest that decides
+whether committed profiles still describe the kernels, the lookup of those
+profiles, and the host facts of the CPU baseline."""
+from __future__ import annotations
+
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_digest_ignores_comments_and_blank_lines():
+    a = "int f() {  // one\n\n  return 1; /* two\n lines */\n}\n"
+    b = "int f() {\n  return 1;\n}\n"
+    assert bench._strip_comments(a) == bench._strip_comments(b)
+    assert bench._strip_comments("int g();") != bench._strip_comments(b)
+
+
+def test_stored_figures_follow_the_digest(tmp_path, monkeypatch):
+    digest = bench.kernel_source_digest()
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    (tmp_path / "fused_insert_conv_w.md").write_text(
+        f"trace_avg_us: 4.500\nkernel_sources: {digest}\n")
+    (tmp_path / "counters_w.md").write_text(
+        f"hbm_bytes_per_launch: 5205617\nkernel_sources: {digest}\n")
+    assert bench.stored_trace("fused_insert_conv_kernel", "w") == 4.5
+    assert bench.stored_traffic("w") == 5205617.0
+    (tmp_path / "fused_insert_conv_w.md").write_text(
+        "trace_avg_us: 4.500\nkernel_sources: 0000000000000000\n")
+    assert bench.stored_trace("fused_insert_conv_kernel", "w") is None
+    assert bench.stored_trace("fused_insert_conv_kernel", "missing") is None
+    assert bench.stored_traffic("missing") is None
+
+
+def test_committed_profiles_name_their_command_and_digest():
+    for name in os.listdir(bench.PROFILES):
+        text = open(os.path.join(bench.PROFILES, name)).read()
+        assert "rocprofv3" in text and "bench.py" in text, name
+        assert "kernel_sources:" in text, name
+        if not name.startswith("counters_"):
+            assert "trace_avg_us:" in text and "event_us:" in text, name
+
+
+def test_cpu_threads_honour_the_share(monkeypatch):
+    n = len(os.sched_getaffinity(0))
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.cpu_threads() == 1
+    monkeypatch.setenv("OMP_NUM_THREADS", "100000")
+    assert bench.cpu_threads() == min(n, 256)
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.cpu_threads() == min(n, 256)
+    assert bench.cpu_model()
+
+
+def test_repeat_until_spends_the_budget():
+    calls = []
+
+    def once(n):
+        calls.append(n)
+        return 10, 0.25
+    tokens, spent, n = bench.repeat_until(1.0, once)
+    assert (tokens, spent, n) == (40, 1.0, 4) and calls == [0, 1, 2, 3]
+    assert bench.repeat_until(0.0, once)[2] == 1   # at least once
