@@ -1014,11 +1014,13 @@ def test_gather_graph_replay_with_device_count():
 
 # ------------------------------------------------------------------ conv + gather, one launch
 
-def check_conv_gather(cases, gc, what, fold=True, expect_mode=1):
+def check_conv_gather(cases, gc, what, fold=True, expect_mode=1, own_src=False):
     """sconv_fused_insert_conv_gather against the oracle's two ops: every
     stream's output, the cache (referenced blocks bit for bit, the others
     still NaN), and the gathered windows bit for bit (dead slots keep their
-    sentinel).  The gather reads the first stream's x."""
+    sentinel).  The gather reads the first stream's x, or with own_src its
+    own gc.src.  expect_mode None accepts either launch form; the form
+    taken is returned."""
     import depthwise_causal_conv1d_amd as lib
     import oracle
     c0 = cases[0]
@@ -1030,7 +1032,7 @@ def check_conv_gather(cases, gc, what, fold=True, expect_mode=1):
     pos, bt, sm = c0.positions.to(DEV), c0.block_table.to(DEV), c0.slot_mapping.to(DEV)
     qsl = c0.query_start_loc.to(DEV)
     outs = [torch.full_like(x, SENTINEL) for x in xs]
-    src = xs[0].view(1, c0.T, c0.C)
+    src = gc.src.to(DEV) if own_src else xs[0].view(1, c0.T, c0.C)
     gpos = gc.abs_positions.to(DEV)
     rc = torch.tensor([gc.real_count], dtype=torch.int32, device=DEV)
     gout = gc.out_init.to(DEV).clone()
@@ -1046,7 +1048,10 @@ def check_conv_gather(cases, gc, what, fold=True, expect_mode=1):
     args = (xs, ws_, cache, pos, bt, sm, [c.off_s for c in cases], [c.ws for c in cases],
             c0.block_size)
     plan = lib.sconv_fused_plan(*args, gather=(src, gpos, rc, gout, gc.d_conv), **kw)
-    assert plan["gather_mode"] == expect_mode, plan
+    if expect_mode is not None:
+        assert plan["gather_mode"] == expect_mode, plan
+    n = max(0, min(gc.real_count, gc.out_init.shape[0]))
+    assert plan["gather_mode"] in ((1, 2) if n or gc.out_init.shape[0] else (0,)), plan
     lib.sconv_fused_insert_conv_gather(*args, src, gpos, rc, gout, gc.d_conv, **kw)
     torch.cuda.synchronize()
     cc, btc, smc = c0.compact()
@@ -1067,8 +1072,8 @@ def check_conv_gather(cases, gc, what, fold=True, expect_mode=1):
                                     to_np(gc.out_init), gc.d_conv)
     g_h = to_np(gout)
     assert_bits_equal(g_h, g_r, f"{what} gathered windows")
-    n = max(0, min(gc.real_count, gc.out_init.shape[0]))
     assert_finite(g_h[:n], f"{what} live gathered windows")
+    return plan["gather_mode"]
 
 
 @pytest.mark.parametrize("real_count", [0, 1, 256, 512, 600, -4])
@@ -1100,6 +1105,57 @@ def test_conv_gather_four_streams_f32_and_small_windows(fold):
                                  block_size=16, W=W, dtype=torch.float32, pad_count=9)
         gc = workloads.gather_case(98 + dc, c.x.view(1, c.T, c.C), max_count=200, d_conv=dc)
         check_conv_gather([c], gc, f"f32 W={W} d_conv={dc}", fold=fold)
+
+
+_CG_MODES = {}
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_conv_gather_random_sweep(k):
+    """12 seeded random conv + gather launches against the oracle's two ops.
+    Even cases have the one-generation shape that runs the gather in the
+    conv's launch (1024-1280 requests x 4 rows, four 16-byte-lane slabs per
+    row); odd ones reuse the random fused layouts, which mostly launch the
+    gather after the conv.  Dtype, W, streams, metadata form, window length,
+    slot count, live count (also negative or past the slots) and the
+    gather's source (the conv's x or a tensor of its own) are drawn per
+    case."""
+    rng = np.random.default_rng(7000 + k)
+    if k % 2 == 0:
+        dt = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+        lane = 8 if dt == torch.bfloat16 else 4
+        R = int(rng.integers(1024, 1281))
+        nst = int(rng.choice([1, 2]))
+        ws = 64 * lane // nst if dt == torch.bfloat16 else 128 // nst
+        H = 4 * 64 * lane // (ws * nst) // 1
+        c = dict(kind="one-generation", dt=dt, W=int(rng.integers(1, 5)),
+                 N=int(rng.choice([8, 16, 32])), H=H, D=ws * nst,
+                 streams=[(i * ws, ws) for i in range(nst)], new=[4] * R,
+                 ctx=[int(v) for v in rng.integers(0, 3000, R)], pad=int(rng.integers(0, 40)),
+                 tail=0, fold=bool(rng.random() < 0.5))
+    else:
+        c = _random_fused_spec(k)
+    cases = workloads.fused_streams_case(7100 + k, c["new"], c["ctx"], H=c["H"], D=c["D"],
+                                         streams=c["streams"], block_size=c["N"], W=c["W"],
+                                         dtype=c["dt"], pad_count=c["pad"], tail_pad=c["tail"])
+    c0 = cases[0]
+    own = bool(rng.random() < 0.4)
+    dc = int(rng.integers(1, 5))
+    if own:
+        S, Cg = int(rng.integers(1, 3000)), int(rng.choice([8, 24, 40, 1024]))
+        src = torch.randn(1, S, Cg, generator=torch.Generator().manual_seed(k)).to(c["dt"])
+    else:
+        src = c0.x.view(1, c0.T, c0.C)
+    mc = int(rng.integers(1, 600))
+    stride = max(1, src.shape[1] // mc)
+    rc = int(rng.choice([0, 1, mc // 2, mc, mc + 7, -3]))
+    gc = workloads.gather_case(7200 + k, src, max_count=mc, d_conv=dc, stride=stride,
+                               real_count=rc)
+    mode = check_conv_gather(cases, gc, f"random {k} ({c['kind']})", fold=c["fold"],
+                             expect_mode=None, own_src=own)
+    _CG_MODES[k] = mode
+    if k == 10:  # the even cases so far must have run in one launch
+        assert all(_CG_MODES[j] == 1 for j in _CG_MODES if j % 2 == 0), _CG_MODES
 
 
 def test_conv_gather_falls_back_to_two_launches():
