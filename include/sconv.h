@@ -10,8 +10,9 @@
  * - Every buffer is a caller-owned DEVICE pointer (hipMalloc / torch).  The
  *   library allocates nothing, never synchronizes and never reads device data
  *   on the host: each call enqueues one kernel on `stream` (NULL = the null
- *   stream) and returns.  This makes every call capturable in a hipGraph;
- *   grids depend on host scalars only.
+ *   stream; sconv_fused_insert_conv_gather may enqueue two) and returns.
+ *   This makes every call capturable in a hipGraph; grids depend on host
+ *   scalars only.
  * - Strides are in ELEMENTS.  Only host scalars are validated.  Properties of
  *   device data (index ranges, monotone offsets, distinct slots) are the
  *   caller's contract and are stated per function; breaking them is
