@@ -617,6 +617,8 @@ class SpecDecodeBench(Workload):
         for n in (0, 128, 256, 512):
             rc = torch.tensor([n], dtype=torch.int32, device="cuda")
             g = capture(lambda i: self.gather(i, rc), range(self.R), stream)
+            upload(g, stream)
+            time_graph(g, 1, stream)
             us = time_graph(g, reps, stream) * 1e3 / (reps * self.R)
             out[str(n)] = {"us": round(us, 3),
                            # 2 x 4096 channels x 3 rows x 2 bytes + 4 per live slot
@@ -1000,7 +1002,9 @@ class StepGraphs:
         return e0.elapsed_time(e1), wall
 
     def kernel_us(self, reps):
-        """Average duration of one launch of the dominant kernel (us)."""
+        """Average duration of one launch of the dominant kernel (us), after
+        one untimed replay of its graph."""
+        time_graph(self.kern, 1, self.stream)
         ms = time_graph(self.kern, reps, self.stream)
         return ms * 1e3 / (reps * self.wl.R * self.wl.kernels_per_call())
 
