@@ -22,7 +22,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sconv_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libsconv_oracle.so")
+# SCONV_ORACLE_LIB names another build of sconv_oracle.c to load instead
+# (the mutation tests plant mistakes in copies of the source); build() then
+# leaves it as it is.
+_OVERRIDE = os.environ.get("SCONV_ORACLE_LIB")
+_LIB_PATH = _OVERRIDE or os.path.join(_HERE, "libsconv_oracle.so")
 
 F32, BF16, F64 = 0, 1, 2
 ACT_NONE, ACT_SILU = 0, 1
@@ -40,16 +44,21 @@ _ERRORS = {
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (no GPU toolchain involved)."""
+    if _OVERRIDE:
+        return _LIB_PATH
     if force or not os.path.exists(_LIB_PATH) or (
         os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
     ):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-pthread",
-             "-o", tmp, _SRC, "-lm"]
-        )
+        subprocess.check_call(compile_command(_SRC, tmp))
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def compile_command(src: str, out: str):
+    """The gcc command that builds the oracle library from `src`."""
+    return ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-pthread",
+            "-o", out, src, "-lm"]
 
 
 _lib = None
