@@ -1097,10 +1097,12 @@ def _probe_lib():
                           "bench.build_probes()'` (or __graft_entry__.build())")
     P = ctypes.CDLL(PROBE_LIB)
     V, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
-    P.probe_read.argtypes = [V, I64, V, I32, V]
-    P.probe_write.argtypes = [V, I64, I32, V]
-    P.probe_copy.argtypes = [V, V, I64, I32, V]
-    P.probe_read_write2.argtypes = [V, V, V, I64, I32, I32, I32, V]
+    U32 = ctypes.c_uint32
+    P.probe_read.argtypes = [V, I64, V, I64, I32, U32, V]
+    P.probe_write.argtypes = [V, I64, I64, I32, I32, U32, V]
+    P.probe_copy.argtypes = [V, V, I64, I64, I32, I32, U32, V]
+    P.probe_read_write2.argtypes = [V, V, V, I64, I32, I32, I64, I32, I32, U32, V]
+    P.probe_prefill_layout.argtypes = [V, V, V, V, I32, I32, I32, U32, V]
     P.probe_empty.argtypes = [I32, V]
     P.probe_load_store.argtypes = [V, V, I32, V]
     P.probe_chain.argtypes = [V, I32, V, V, V, I32, I32, V]
@@ -1112,36 +1114,120 @@ def _ok(rc):
         raise RuntimeError(f"probe launch failed ({rc})")
 
 
-def stream_ceilings(P, stream, names):
-    """TB/s of the streaming reference kernels `names` (1 GiB per stream,
-    32768 workgroups), each timed with HIP events over graph replays."""
+# Shapes of the streaming probes: (vectors of 16 bytes per lane and pass,
+# vectors per 256-thread workgroup).  Which one is fastest depends on the
+# pattern and the size, so each ceiling is the best of them, with streaming
+# and with ordinary stores, at full occupancy and at 5 and 4 workgroups per
+# CU (dynamic LDS the kernels do not use: 160 KiB per CU).
+PROBE_SHAPES = ((1, 256), (2, 512), (4, 1024), (2, 2048))
+PROBE_LDS = (0, 32768, 40960)
+LDS_PER_CU = 163840
+
+
+def _occupancy(lds):
+    return "full" if lds == 0 else f"{LDS_PER_CU // lds} workgroups per CU"
+
+
+def _time_launches(fn, R, stream):
+    """Milliseconds per launch of fn(0..R-1), captured as one graph and
+    replayed back to back (after two untimed replays)."""
+    g = capture(fn, range(R), stream)
+    upload(g, stream)
+    time_graph(g, 2, stream)
+    reps = max(5, 40 // R)
+    ms = time_graph(g, reps, stream) / (reps * R)
+    del g
+    return ms
+
+
+def prefill_layout(P, stream, T=18432):
+    """TB/s of the mixed prefill's own traffic in its own layout (one stream
+    launch of T rows, C = 4096 bf16, sequential slots; bench_probes.hip),
+    alone and with the conv's other loads (3 halo rows, 4 filter-tap
+    vectors per lane), each the best of the PROBE_LDS occupancies.  Bytes
+    are the algorithmic ones: x read, out written, cache pieces written."""
+    import torch
+    R = 2
+    xb, cb = T * 512 * 16, T * 2048 * 16
+    x = torch.empty(R * xb, dtype=torch.uint8, device="cuda").fill_(1)
+    o = torch.empty(R * xb, dtype=torch.uint8, device="cuda")
+    c = torch.empty(R * cb, dtype=torch.uint8, device="cuda")
+    w = torch.empty(2048 * 16, dtype=torch.uint8, device="cuda").fill_(2)
+    s = stream.cuda_stream
+    res = {}
+    for halo, wts in ((0, 0), (0, 4), (3, 0), (3, 4)):
+        runs = []
+        for lds in PROBE_LDS:
+            ms = _time_launches(lambda i: _ok(P.probe_prefill_layout(
+                x.data_ptr() + i * xb, w.data_ptr(), o.data_ptr() + i * xb,
+                c.data_ptr() + i * cb, T, halo, wts, lds, s)), R, stream)
+            runs.append((round(3 * xb / (ms * 1e-3) / 1e12, 3), _occupancy(lds), round(ms * 1e3, 2)))
+        tbs, occ, us = max(runs)
+        name = {(0, 0): "traffic", (0, 4): "traffic_and_taps", (3, 0): "traffic_and_halo",
+                (3, 4): "traffic_taps_and_halo"}[(halo, wts)]
+        res[name] = {"TB/s": tbs, "us": us, "occupancy": occ}
+    res["rows"] = T
+    res["bytes"] = 3 * xb
+    del x, o, c, w
+    torch.cuda.empty_cache()
+    return res
+
+
+def stream_ceilings(P, stream, names, n16=None, forms=False):
+    """TB/s of the streaming reference kernels `names`, each the best of
+    PROBE_SHAPES x {streaming, ordinary stores} x PROBE_LDS, timed with HIP
+    events over graph replays.  Each stream moves n16 vectors of 16 bytes (default
+    1 GiB); smaller streams cycle through replicas at least 1 GiB apart, so
+    that every launch reads HBM.  forms: also list every form's figure."""
     import torch
     GiB = 1 << 30
-    n16, groups, s = GiB // 16, 32768, stream.cuda_stream
+    n16 = GiB // 16 if n16 is None else int(n16)
+    if n16 < 16 or n16 % 16 or 16 * n16 > GiB:
+        raise ValueError(f"stream of {n16} vectors: need a multiple of 16 up to 1 GiB")
+    R = GiB // (16 * n16)
+    s = stream.cuda_stream
     a = torch.empty(GiB, dtype=torch.uint8, device="cuda").fill_(1)
     b = torch.empty(GiB, dtype=torch.uint8, device="cuda")
     c = torch.empty(GiB, dtype=torch.uint8, device="cuda")
     d = torch.empty(4 * GiB, dtype=torch.uint8, device="cuda")  # 256-byte pieces of 1 KiB rows
-    sink = torch.empty(groups * 256 * 16, dtype=torch.uint8, device="cuda")
-    cases = {
-        "read": (lambda: _ok(P.probe_read(a.data_ptr(), n16, sink.data_ptr(), groups, s)), GiB),
-        "write": (lambda: _ok(P.probe_write(b.data_ptr(), n16, groups, s)), GiB),
-        "copy": (lambda: _ok(P.probe_copy(a.data_ptr(), b.data_ptr(), n16, groups, s)), 2 * GiB),
-        "read_write2_linear": (lambda: _ok(P.probe_read_write2(
-            a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, 1024, 1024, groups, s)), 3 * GiB),
-        "read_write2_pieces_256_of_1024": (lambda: _ok(P.probe_read_write2(
-            a.data_ptr(), b.data_ptr(), d.data_ptr(), n16, 256, 1024, groups, s)), 3 * GiB),
-    }
+    sink = torch.empty(256 * 16, dtype=torch.uint8, device="cuda")
+    nb = 16 * n16
+
+    def case(name, i, per, u, nt, lds):
+        A, B, C, Dd = (x.data_ptr() + i * k * nb for x, k in ((a, 1), (b, 1), (c, 1), (d, 4)))
+        if name == "read":
+            return P.probe_read(A, n16, sink.data_ptr(), per, u, lds, s)
+        if name == "write":
+            return P.probe_write(B, n16, per, u, nt, lds, s)
+        if name == "copy":
+            return P.probe_copy(A, B, n16, per, u, nt, lds, s)
+        if name == "read_write2_linear":
+            return P.probe_read_write2(A, B, C, n16, 1024, 1024, per, u, nt, lds, s)
+        return P.probe_read_write2(A, B, Dd, n16, 256, 1024, per, u, nt, lds, s)
+
+    moved = {"read": 1, "write": 1, "copy": 2, "read_write2_linear": 3,
+             "read_write2_pieces_256_of_1024": 3}
     res = {}
     for name in names:
-        fn, nbytes = cases[name]
-        g = capture(lambda i: fn(), range(1), stream)
-        upload(g, stream)
-        time_graph(g, 2, stream)
-        ms = time_graph(g, 5, stream) / 5
-        res[name] = {"TB/s": round(nbytes / (ms * 1e-3) / 1e12, 3),
-                     "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "ms": round(ms, 3), "bytes": nbytes}
+        runs = []
+        for u, per in PROBE_SHAPES:
+            for nt in ((1,) if name == "read" else (1, 0)):
+                for lds in PROBE_LDS:
+                    ms = _time_launches(lambda i: _ok(case(name, i, per, u, nt, lds)), R, stream)
+                    nbytes = moved[name] * nb
+                    runs.append({"lane_vectors": u, "workgroup_KiB": per * 16 // 1024,
+                                 "stores": "streaming" if nt else "ordinary",
+                                 "occupancy": _occupancy(lds),
+                                 "TB/s": round(nbytes / (ms * 1e-3) / 1e12, 3),
+                                 "ms": round(ms, 4)})
+        best = max(runs, key=lambda r: r["TB/s"])
+        res[name] = {"TB/s": best["TB/s"],
+                     "frac_of_peak": round(best["TB/s"] * 1e3 / HBM_PEAK_GBS, 4),
+                     "ms": best["ms"], "bytes": moved[name] * nb,
+                     "form": {k: best[k] for k in ("lane_vectors", "workgroup_KiB", "stores",
+                                                   "occupancy")}}
+        if forms:
+            res[name]["forms"] = runs
     del a, b, c, d, sink
     torch.cuda.empty_cache()
     return res
@@ -1193,12 +1279,28 @@ def decode_floors(P, stream, names):
     return lat
 
 
+# One mixed-prefill stream launch moves 469.7 MB (config 3): the prefill
+# pattern is also measured at that size, as read n : write 2n.
+PREFILL_LAUNCH_BYTES = 469_712_208
+
+
+def _launch_n16(launch_bytes):
+    return int(launch_bytes) // 3 // 256 * 16
+
+
 def run_probes(stream):
     """Streaming ceilings and latency floors of this GPU (one JSON line)."""
     P = _probe_lib()
-    res = {"workload": "probe", "peak_GBs": HBM_PEAK_GBS}
+    res = {"workload": "probe", "peak_GBs": HBM_PEAK_GBS,
+           "shapes": [{"lane_vectors": u, "workgroup_KiB": per * 16 // 1024}
+                      for u, per in PROBE_SHAPES]}
     res.update(stream_ceilings(P, stream, ["read", "write", "copy", "read_write2_linear",
-                                           "read_write2_pieces_256_of_1024"]))
+                                           "read_write2_pieces_256_of_1024"], forms=True))
+    at = stream_ceilings(P, stream, ["read_write2_pieces_256_of_1024"],
+                         n16=_launch_n16(PREFILL_LAUNCH_BYTES), forms=True)
+    res["read_write2_pieces_256_of_1024_at_prefill_launch_size"] = at[
+        "read_write2_pieces_256_of_1024"]
+    res["prefill_layout"] = prefill_layout(P, stream)
     res["decode_shape_floors_us"] = decode_floors(
         P, stream, ["empty", "load_store", "table_row", "table_row_then_3_tap_rows",
                     "meta_then_table_row", "meta_table_row_then_3_tap_rows"])
@@ -1206,11 +1308,12 @@ def run_probes(stream):
     return res
 
 
-def machine_reference(stream):
+def machine_reference(stream, prefill_launch_bytes=PREFILL_LAUNCH_BYTES):
     """What the same GPU reaches on the headline's patterns, for the default
-    line: the copy and the mixed prefill's write patterns (TB/s), and the
-    decode kernel's dependent chain at its launch shape (µs).  None when the
-    probe kernels are not built."""
+    line: the copy and the mixed prefill's write patterns (TB/s; the pieces
+    pattern at 1 GiB per stream and at the prefill launch's own size), and
+    the decode kernel's dependent chain at its launch shape (µs).  None when
+    the probe kernels are not built."""
     try:
         P = _probe_lib()
     except ImportError as e:
@@ -1218,11 +1321,22 @@ def machine_reference(stream):
         return None
     c = stream_ceilings(P, stream, ["copy", "read_write2_linear",
                                     "read_write2_pieces_256_of_1024"])
+    at = stream_ceilings(P, stream, ["read_write2_pieces_256_of_1024"],
+                         n16=_launch_n16(prefill_launch_bytes))["read_write2_pieces_256_of_1024"]
+    lay = prefill_layout(P, stream)
     f = decode_floors(P, stream, ["empty", "table_row_then_3_tap_rows"])
+    pieces = c["read_write2_pieces_256_of_1024"]
     return {"source": "bench_probes.hip in this run (bench.py --probe measures all)",
+            "forms": "best of %d workgroup shapes x 2 store forms x %d occupancies" % (
+                len(PROBE_SHAPES), len(PROBE_LDS)),
             "copy_TBs": c["copy"]["TB/s"],
             "prefill_pattern_linear_TBs": c["read_write2_linear"]["TB/s"],
-            "prefill_pattern_TBs": c["read_write2_pieces_256_of_1024"]["TB/s"],
+            "prefill_pattern_TBs": pieces["TB/s"],
+            "prefill_pattern_form": pieces["form"],
+            "prefill_pattern_at_launch_size_TBs": at["TB/s"],
+            "prefill_pattern_at_launch_size_form": at["form"],
+            "prefill_layout_TBs": lay["traffic"]["TB/s"],
+            "prefill_layout_with_taps_and_halo_TBs": lay["traffic_taps_and_halo"]["TB/s"],
             "empty_launch_us": f["empty"],
             "decode_chain_floor_us": f["table_row_then_3_tap_rows"]}
 
@@ -1344,14 +1458,18 @@ def main():
         torch.cuda.empty_cache()
         line["prefill"] = {"workload": "mixed_prefill", **run("mixed_prefill")}
         torch.cuda.empty_cache()
-        m = machine_reference(stream)
+        m = machine_reference(stream, line["prefill"]["roofline"]["bytes_per_launch"])
         if m is not None:
             # the kernels against what this GPU reaches on their patterns
             line["roofline"]["floor_us"] = m["decode_chain_floor_us"]
             line["roofline"]["launch_over_floor"] = round(
                 line["roofline"]["launch_us"] / m["decode_chain_floor_us"], 3)
             pr = line["prefill"]["roofline"]
-            pr["ceiling_GBs"] = round(m["prefill_pattern_TBs"] * 1e3, 1)
+            # the best this GPU reached on the prefill's traffic: the pattern
+            # at either size, or the launch's own layout
+            pr["ceiling_GBs"] = round(max(m["prefill_pattern_TBs"],
+                                          m["prefill_pattern_at_launch_size_TBs"],
+                                          m["prefill_layout_TBs"]) * 1e3, 1)
             pr["frac_of_ceiling"] = round(pr["achieved"] / pr["ceiling_GBs"], 4)
         line["machine"] = m
     line["kernel_sources"] = kernel_source_digest()

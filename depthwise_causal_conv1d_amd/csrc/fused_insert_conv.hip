@@ -148,6 +148,14 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_GROUP_STORES 2  // stores after all rows' arithmetic: 0 never, 1 always,
                                     // 2 in multi-generation launches (no streaming x loads)
 #endif
+#ifndef SCONV_FUSED_EXTRA_LDS
+#define SCONV_FUSED_EXTRA_LDS 0  // unused dynamic LDS bytes per workgroup of multi-generation
+                                 // launches: fewer workgroups per CU (measured no faster)
+#endif
+#ifndef SCONV_FUSED_LDS_WEIGHTS
+#define SCONV_FUSED_LDS_WEIGHTS 0  // filter taps shared through LDS by the waves of a workgroup
+                                   // (measured slower: the barrier then waits for them too)
+#endif
 #ifndef SCONV_FUSED_LDS_HALO
 #define SCONV_FUSED_LDS_HALO 1  // halo rows passed between the waves of a workgroup
 #endif
@@ -292,9 +300,9 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // batch) rather than from the implicit arguments, which would cost a
   // second dependent round trip before any data load could start.
   // Wave counts are below 2^31 (checked on the host): 32-bit arithmetic.
-  uint32_t wave = (kXcdRuns ? xcd_contiguous(blockIdx.x, p.num_groups) : blockIdx.x) *
-                      (uint32_t)p.waves_per_group +
-                  (uint32_t)uniform(threadIdx.x >> 6);
+  const uint32_t group_wave0 =
+      (kXcdRuns ? xcd_contiguous(blockIdx.x, p.num_groups) : blockIdx.x) * (uint32_t)p.waves_per_group;
+  uint32_t wave = group_wave0 + (uint32_t)uniform(threadIdx.x >> 6);
   // A wave past the end works on the last tile and writes nothing (no early
   // return: it would split the parameter loads around the branch).
   const uint32_t total_waves = (uint32_t)p.num_tiles * (uint32_t)p.num_slabs;
@@ -439,11 +447,37 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   constexpr int kNChunks = kN / kChunk > 0 ? kN / kChunk : 1;
   Pack<D, kChunk> wpk[kNChunks];
   struct WRaw { S e[kN]; } wr;
+  // Launches of several wave generations in slab-major order hand halo rows
+  // between the waves of a workgroup through LDS, behind one barrier (see
+  // the halo below).  The same barrier lets waves that work on one slab
+  // share its filter taps: wave w loads chunks w, w + waves, ... for all
+  // 64 lanes and leaves them in LDS, so each wave issues one load for its
+  // taps instead of kNChunks.  Whether every wave of the workgroup is on
+  // one slab is the same test in each of them (first and last wave).
+#if SCONV_FUSED_LDS_HALO
+  constexpr bool kLdsHalo = kSlabMajor && !NTX && W > 1 && BT >= W - 1;
+#else
+  constexpr bool kLdsHalo = false;
+#endif
+  constexpr bool kLdsWts = kLdsHalo && VEC > 1 && SCONV_FUSED_LDS_WEIGHTS;
+  const int wpg = (int)p.waves_per_group;
+  const int wig = (int)(threadIdx.x >> 6);  // wave in workgroup
+  bool wts_shared = false;
+  if constexpr (kLdsWts) {
+    const uint32_t last = total_waves - 1;
+    const uint32_t wa = group_wave0 < last ? group_wave0 : last;
+    const uint32_t wb = group_wave0 + (uint32_t)wpg - 1 < last ? group_wave0 + (uint32_t)wpg - 1 : last;
+    wts_shared = wa / (uint32_t)p.num_tiles == wb / (uint32_t)p.num_tiles;
+  }
   if constexpr (VEC > 1) {
     static_assert(kN % kChunk == 0, "packed weights come in whole 16-byte chunks");
+    if (wts_shared) {
 #pragma unroll
-    for (int ch = 0; ch < kN / kChunk; ++ch) {
-      wpk[ch].load(wt + (int64_t)cl * W + ch * kChunk);
+      for (int ch = 0; ch < kNChunks; ++ch)
+        if (ch % wpg == wig) wpk[ch].load(wt + (int64_t)cl * W + ch * kChunk);
+    } else {
+#pragma unroll
+      for (int ch = 0; ch < kNChunks; ++ch) wpk[ch].load(wt + (int64_t)cl * W + ch * kChunk);
     }
   } else {
 #pragma unroll
@@ -592,19 +626,27 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // of its slab, still load their halo.  Only launches of several wave
   // generations do this: when all waves are resident at once, the barrier
   // would hold back the history lookups that bound such launches.
-#if SCONV_FUSED_LDS_HALO
-  constexpr bool kLdsHalo = kSlabMajor && !NTX && W > 1 && BT >= W - 1;
-#else
-  constexpr bool kLdsHalo = false;
-#endif
   constexpr int kWavesMax = SCONV_FUSED_WG_THREADS / 64;
   __shared__ typename P::raw_t s_halo[kLdsHalo ? kWavesMax : 1][kHalo][64];
-  const int wig = (int)(threadIdx.x >> 6);  // wave in workgroup
+  __shared__ typename Pack<D, kChunk>::raw_t s_wts[kLdsWts ? kNChunks : 1][64];
   bool halo_from_lds = false;
   if constexpr (kLdsHalo) {
 #pragma unroll
     for (int m = 1; m <= W - 1; ++m) s_halo[wig][m - 1][lane] = xr[BT - m].raw;
+    if constexpr (kLdsWts) {
+      if (wts_shared) {
+#pragma unroll
+        for (int ch = 0; ch < kNChunks; ++ch)
+          if (ch % wpg == wig) s_wts[ch][lane] = wpk[ch].raw;
+      }
+    }
     __syncthreads();
+    if constexpr (kLdsWts) {
+      if (wts_shared) {
+#pragma unroll
+        for (int ch = 0; ch < kNChunks; ++ch) wpk[ch].raw = s_wts[ch][lane];
+      }
+    }
     halo_from_lds = wig > 0 && tile > 0;
   }
   if (halo_from_lds) {
@@ -811,22 +853,23 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
 
 template <typename D, int VEC, int W, int BT, bool NTX, bool MS, bool NTH = false>
 static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
+  constexpr uint32_t kExtraLds = NTX ? 0u : (uint32_t)SCONV_FUSED_EXTRA_LDS;
   if constexpr (W > 1) {
     if (p.guess) {
       hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslGuess, NTX, MS, NTH>),
-                         dim3(grid), dim3(threads), 0, s, p);
+                         dim3(grid), dim3(threads), kExtraLds, s, p);
       return;
     }
   }
   if (p.qsl && p.num_reqs <= kQslRegMax) {
     hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs, NTX, MS, NTH>),
-                       dim3(grid), dim3(threads), 0, s, p);
+                       dim3(grid), dim3(threads), kExtraLds, s, p);
   } else if (p.qsl) {
     hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslSearch, NTX, MS, NTH>),
-                       dim3(grid), dim3(threads), 0, s, p);
+                       dim3(grid), dim3(threads), kExtraLds, s, p);
   } else {
     hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslOff, NTX, MS, NTH>),
-                       dim3(grid), dim3(threads), 0, s, p);
+                       dim3(grid), dim3(threads), kExtraLds, s, p);
   }
 }
 

@@ -48,6 +48,12 @@ def test_default_bench_line():
             assert cpu["single_thread"]["value"] > 0
     m = j["machine"]  # the probe kernels are built with the library
     assert 1.0 < m["copy_TBs"] < 8.0 and 1.0 < m["prefill_pattern_TBs"] < 8.0
+    assert 1.0 < m["prefill_pattern_at_launch_size_TBs"] < 8.0
+    assert 1.0 < m["prefill_layout_with_taps_and_halo_TBs"] < m["prefill_layout_TBs"] < 8.0
+    # the prefill's ceiling is the best of the machine's figures for its traffic
+    assert math.isclose(j["prefill"]["roofline"]["ceiling_GBs"],
+                        1e3 * max(m["prefill_pattern_TBs"], m["prefill_pattern_at_launch_size_TBs"],
+                                  m["prefill_layout_TBs"]), rel_tol=1e-3)
     assert 0 < m["empty_launch_us"] < m["decode_chain_floor_us"]
     assert math.isclose(j["roofline"]["launch_over_floor"],
                         j["roofline"]["launch_us"] / m["decode_chain_floor_us"], rel_tol=1e-2)
