@@ -148,9 +148,16 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_GROUP_STORES 2  // stores after all rows' arithmetic: 0 never, 1 always,
                                     // 2 in multi-generation launches (no streaming x loads)
 #endif
+// Launches of several wave generations with multi-row tiles (the prefill)
+// reserve LDS they do not use, to hold 4 workgroups per CU instead of the 5
+// their registers allow: with the 12 KiB halo buffer 40 KiB of the CU's
+// 160 KiB each.  HBM delivers more with fewer bytes in flight per CU
+// (0.7-0.8% shorter prefill launches on two boxes; 3 per CU is much slower).
 #ifndef SCONV_FUSED_EXTRA_LDS
-#define SCONV_FUSED_EXTRA_LDS 0  // unused dynamic LDS bytes per workgroup of multi-generation
-                                 // launches: fewer workgroups per CU (measured no faster)
+#define SCONV_FUSED_EXTRA_LDS 28672
+#endif
+#ifndef SCONV_FUSED_SERIAL_X
+#define SCONV_FUSED_SERIAL_X 0  // one input row in flight per lane (multi-generation launches)
 #endif
 #ifndef SCONV_FUSED_LDS_WEIGHTS
 #define SCONV_FUSED_LDS_WEIGHTS 0  // filter taps shared through LDS by the waves of a workgroup
@@ -428,11 +435,20 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   const bool on = c0 < s_C;
   const int cl = on ? c0 : 0;               // clamped for the loads
   P xr[BT];
+  // SCONV_FUSED_SERIAL_X: in launches of several wave generations, each row
+  // is loaded only once the previous one has arrived (its address takes a
+  // zero computed from that row's data), so a lane has one input row in
+  // flight at a time rather than the whole tile.
+  constexpr bool kSerialX = SCONV_FUSED_SERIAL_X && !NTX && BT > 1 && VEC > 1;
+  int32_t dep = 0;
 #pragma unroll
   for (int i = 0; i < BT; ++i) {
     const int64_t t = t0 + i < t_last ? t0 + i : t_last;
     if constexpr (NTX) xr[i].load_nt(x + t * x_rs + cl);
-    else xr[i].load(x + t * x_rs + cl);
+    else xr[i].load(x + t * x_rs + cl + dep);
+    if constexpr (kSerialX) {
+      if (i + 1 < BT) asm volatile("v_mov_b32 %0, 0" : "=v"(dep) : "v"(xr[i].raw[0]));
+    }
   }
   const int h = on ? c0 / s_ws : 0;
   const int j = c0 - h * s_ws;
@@ -853,7 +869,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
 
 template <typename D, int VEC, int W, int BT, bool NTX, bool MS, bool NTH = false>
 static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
-  constexpr uint32_t kExtraLds = NTX ? 0u : (uint32_t)SCONV_FUSED_EXTRA_LDS;
+  constexpr uint32_t kExtraLds = NTX || BT == 1 ? 0u : (uint32_t)SCONV_FUSED_EXTRA_LDS;
   if constexpr (W > 1) {
     if (p.guess) {
       hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslGuess, NTX, MS, NTH>),
