@@ -25,6 +25,9 @@ namespace sconv {
 #ifndef SCONV_VARLEN_GROUP
 #define SCONV_VARLEN_GROUP 4       // chunks loaded together per wave
 #endif
+#ifndef SCONV_VARLEN_EXTRA_LDS
+#define SCONV_VARLEN_EXTRA_LDS 0   // unused dynamic LDS bytes per workgroup (fewer per CU)
+#endif
 #ifndef SCONV_VARLEN_NT_LOADS
 #define SCONV_VARLEN_NT_LOADS 1    // streaming loads of the inputs (read once)
 #endif
@@ -759,10 +762,10 @@ static int update_tokens_launch(
 template <typename D, int VEC>
 static void launch_varlen(int W, const VarlenParams& p, uint32_t g, hipStream_t s) {
   switch (W) {
-    case 1: hipLaunchKernelGGL((varlen_fwd_kernel<D, VEC, 1>), dim3(g), dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((varlen_fwd_kernel<D, VEC, 2>), dim3(g), dim3(256), 0, s, p); break;
-    case 3: hipLaunchKernelGGL((varlen_fwd_kernel<D, VEC, 3>), dim3(g), dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((varlen_fwd_kernel<D, VEC, 4>), dim3(g), dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((varlen_fwd_kernel<D, VEC, 1>), dim3(g), dim3(256), SCONV_VARLEN_EXTRA_LDS, s, p); break;
+    case 2: hipLaunchKernelGGL((varlen_fwd_kernel<D, VEC, 2>), dim3(g), dim3(256), SCONV_VARLEN_EXTRA_LDS, s, p); break;
+    case 3: hipLaunchKernelGGL((varlen_fwd_kernel<D, VEC, 3>), dim3(g), dim3(256), SCONV_VARLEN_EXTRA_LDS, s, p); break;
+    default: hipLaunchKernelGGL((varlen_fwd_kernel<D, VEC, 4>), dim3(g), dim3(256), SCONV_VARLEN_EXTRA_LDS, s, p); break;
   }
 }
 

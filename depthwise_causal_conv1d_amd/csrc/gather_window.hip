@@ -39,6 +39,9 @@ struct SsmGatherParams {
 #ifndef SCONV_SSM_GATHER_NT_LOADS
 #define SCONV_SSM_GATHER_NT_LOADS 1  // streaming reads of the source rows (read once)
 #endif
+#ifndef SCONV_SSM_GATHER_EXTRA_LDS
+#define SCONV_SSM_GATHER_EXTRA_LDS 0  // unused dynamic LDS bytes per workgroup (fewer per CU)
+#endif
 
 // One workgroup per (column block, slot): the live count and the slot's
 // source row are fetched in one round trip, dead slots leave at once, and
@@ -78,7 +81,7 @@ template <typename T>
 static void launch_ssm(const SsmGatherParams& p, hipStream_t s) {
   constexpr int U = SCONV_SSM_GATHER_UNROLL;
   const dim3 grid((uint32_t)cdiv(p.nvec, (int64_t)p.threads * U), (uint32_t)p.max_count);
-  hipLaunchKernelGGL((gather_ssm_kernel<T, U>), grid, dim3(p.threads), 0, s, p);
+  hipLaunchKernelGGL((gather_ssm_kernel<T, U>), grid, dim3(p.threads), SCONV_SSM_GATHER_EXTRA_LDS, s, p);
 }
 
 }  // namespace sconv
