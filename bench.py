@@ -277,6 +277,7 @@ class Workload:
     kernel_name = "fused_insert_conv_kernel"
     bound = "hbm"
     dtype = "bf16"
+    unit = "tokens/s"     # of `value`: units of tokens_per_step per second
     oracle_split = True   # the oracle op of its CPU baseline has a threaded form
 
     def kernel(self, i):          # the dominant kernel alone
@@ -830,6 +831,7 @@ class SsmStateGatherBench(Workload):
     whole state row (64 heads x 64 x 128 fp32 = 2 MiB) gathered from 128
     chunk states at distinct indices; three replicas, so a step reads HBM,
     not the MALL."""
+    unit = "slots/s"
     kernel_name = "gather_ssm_kernel"
     dtype = "f32"
     oracle_split = False
@@ -1015,12 +1017,16 @@ def cpu_baseline(wl, budget):
         return None
     n = cpu_threads() if wl.oracle_split else 1
     v, sample, spent = wl.oracle_sample(budget, threads=n)
-    out = {"value": round(v, 1), "unit": "tokens/s", "cores": n, "kind": "oracle",
+    # the GPU step's algorithmic bytes per unit, applied to the oracle's rate
+    per_unit = wl.bytes_per_launch * wl.kernels_per_call() / wl.tokens_per_step
+    out = {"value": round(v, 1), "unit": wl.unit, "cores": n, "kind": "oracle",
+           "GBs": round(v * per_unit / 1e9, 3),
            "sample": f"{sample}; {spent:.1f} s on {n} thread{'s' if n > 1 else ''}",
            "hardware_concurrency": os.cpu_count(), "cpu_model": cpu_model()}
     if n > 1:
         v1, sample1, spent1 = wl.oracle_sample(budget, threads=1)
         out["single_thread"] = {"value": round(v1, 1), "cores": 1,
+                                "GBs": round(v1 * per_unit / 1e9, 3),
                                 "sample": f"{sample1}; {spent1:.1f} s on 1 thread"}
     return out
 
@@ -1051,7 +1057,7 @@ def measure(wl, name, K, Wm, reps, budget, stream):
             if wl.step_is_kernel() else None}
     line = {
         "value": round(wl.tokens_per_step * K / (ms * 1e-3), 1),
-        "unit": "tokens/s",
+        "unit": wl.unit,
         "steps": K,
         "warmup": Wm,
         "ms_per_step": round(ms / K, 6),

@@ -44,6 +44,10 @@ def test_default_bench_line():
         cpu = part["cpu_baseline"]
         assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
         assert cpu["unit"] == "tokens/s" and cpu["sample"] and cpu["cpu_model"]
+        # the same algorithmic bytes per token as the GPU line
+        per_token = rf["bytes_per_launch"] * (4 if part is j["prefill"] else 1) / (
+            256 if part is j else part["config"]["non_pad_tokens"])
+        assert math.isclose(cpu["GBs"], cpu["value"] * per_token / 1e9, rel_tol=1e-2, abs_tol=2e-3)
         if cpu["cores"] > 1:
             assert cpu["single_thread"]["value"] > 0
     m = j["machine"]  # the probe kernels are built with the library
