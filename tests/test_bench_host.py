@@ -65,3 +65,31 @@ def test_repeat_until_spends_the_budget():
     tokens, spent, n = bench.repeat_until(1.0, once)
     assert (tokens, spent, n) == (40, 1.0, 4) and calls == [0, 1, 2, 3]
     assert bench.repeat_until(0.0, once)[2] == 1   # at least once
+
+
+def test_probe_launchers_reject_shapes_they_are_not_built_for():
+    """Each streaming probe and the prefill-layout probe checks its shape on
+    the host and returns -1 before any HIP call (NULL buffers are never
+    touched), so these run without a GPU."""
+    import pytest
+    if not os.path.exists(bench.PROBE_LIB):
+        pytest.skip("bench_probes.so is not built")
+    P = bench._probe_lib()
+    n = 1 << 16
+    # lane depths other than 1, 2 and 4, and empty or non-positive shares
+    for u in (0, 3, 8):
+        assert P.probe_read(None, n, None, 256, u, 0, None) == -1
+        assert P.probe_write(None, n, 256, u, 1, 0, None) == -1
+        assert P.probe_copy(None, None, n, 256, u, 1, 0, None) == -1
+    assert P.probe_copy(None, None, n, 0, 1, 1, 0, None) == -1
+    assert P.probe_write(None, 0, 256, 1, 1, 0, None) == -1
+    # more workgroups than a grid holds
+    assert P.probe_read(None, 1 << 40, None, 1, 1, 0, None) == -1
+    # pieces: multiples of 16 bytes, piece <= row, n a multiple of a piece
+    assert P.probe_read_write2(None, None, None, n, 24, 1024, 256, 1, 1, 0, None) == -1
+    assert P.probe_read_write2(None, None, None, n, 2048, 1024, 256, 1, 1, 0, None) == -1
+    assert P.probe_read_write2(None, None, None, n + 1, 256, 1024, 256, 1, 1, 0, None) == -1
+    # the layout probe: T a positive multiple of 16; halo 0 or 3; taps 0 or 4
+    for T, halo, wts in ((8, 0, 0), (24, 0, 0), (32, 2, 0), (32, 0, 3)):
+        assert P.probe_prefill_layout(None, None, None, None, T, halo, wts, 0, None) == -1
+    assert P.probe_chain(None, 0, None, None, None, 1, 17, None) == -1
