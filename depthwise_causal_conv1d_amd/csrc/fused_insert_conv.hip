@@ -156,6 +156,11 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #ifndef SCONV_FUSED_EXTRA_LDS
 #define SCONV_FUSED_EXTRA_LDS 28672
 #endif
+#ifndef SCONV_FUSED_EARLY_INSERT
+#define SCONV_FUSED_EARLY_INSERT 1  // cache inserts issued behind the history loads:
+                                    // 0 never, 1 one-stream one-row (decode) launches,
+                                    // 2 always
+#endif
 #ifndef SCONV_FUSED_SERIAL_X
 #define SCONV_FUSED_SERIAL_X 0  // one input row in flight per lane (multi-generation launches)
 #endif
@@ -689,6 +694,26 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // Stores of row i (lanes past C store nothing): its output and its input
   // row into the cache slot.
   P outv[BT];
+  // The insert of row i: its input row into its cache slot.
+  auto insert_row = [&](int i) {
+    const uint32_t blk = div_n((uint32_t)slot[i], p);
+    const int32_t off = slot[i] - (int32_t)blk * p.N;
+#if SCONV_FUSED_NT_CACHE
+    xr[i].store_nt(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
+#else
+    xr[i].store(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
+#endif
+  };
+  // A decode wave's stores would otherwise all start after its history
+  // arrives; the insert needs only the slot and the input row, so it is
+  // issued as soon as the history loads are, and overlaps that round trip.
+  // No slot written by a call is a pre-forward tap of the same call (the
+  // caller's contract), so an early insert cannot change what the history
+  // loads read.  In larger one-generation launches (speculative decode, a
+  // layer's four streams) the early stores slow the history loads they
+  // travel with, and measured slower.
+  constexpr bool kEarlyInsert =
+      SCONV_FUSED_EARLY_INSERT == 2 || (SCONV_FUSED_EARLY_INSERT == 1 && NTH && !MS);
   auto store_row = [&](int i) {
     if (on) {
       const int64_t t = t0 + i;
@@ -697,13 +722,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
 #else
       outv[i].store(out + t * out_rs + c0);
 #endif
-      const uint32_t blk = div_n((uint32_t)slot[i], p);
-      const int32_t off = slot[i] - (int32_t)blk * p.N;
-#if SCONV_FUSED_NT_CACHE
-      xr[i].store_nt(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
-#else
-      xr[i].store(cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2 + lane_off);
-#endif
+      if constexpr (!kEarlyInsert) insert_row(i);
     }
   };
   // Output of row i from its fp32 accumulators: SiLU, residual, round.
@@ -809,6 +828,13 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
       if constexpr (W > 2) fetch(2, hist2);
       if constexpr (W > 3) fetch(3, hist3);
       hist_req = req[i];
+    }
+    if constexpr (kEarlyInsert) {
+      if (i == 0 && on) {
+#pragma unroll
+        for (int r = 0; r < BT; ++r)
+          if (slot[r] >= 0) insert_row(r);
+      }
     }
     // Widening here rather than before the loop keeps the wait for the
     // weights (which, counted in order, also waits for the halo loads)
