@@ -53,7 +53,8 @@ class FusedPlan(ctypes.Structure):
     _fields_ = [("lane_elems", I32), ("rows_per_tile", I32), ("request_mode", I32),
                 ("rows_per_request", I32), ("bt_row_entries", I32), ("stream_x_loads", I32),
                 ("stream_hist_loads", I32), ("tile_major", I32), ("wg_threads", I32),
-                ("gather_mode", I32), ("waves", I64), ("workgroups", I64)]
+                ("gather_mode", I32), ("waves", I64), ("workgroups", I64),
+                ("early_inserts", I32)]
 
 
 class WindowGather(ctypes.Structure):

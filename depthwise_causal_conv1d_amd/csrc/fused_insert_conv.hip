@@ -71,6 +71,7 @@ struct FusedParams {
   uint32_t k_magic, k_s1, k_s2;  // division by k = rows per request (same scheme as N)
   int32_t bt_pref;          // block-table entries of row t read ahead (kQslGuess; 0: off)
   int32_t nt_hist;          // host choice: streaming history loads (one-row tiles)
+  int32_t early_insert;     // host choice: cache inserts issued behind the history loads
   void* cache;
   const int64_t* positions;
   const int32_t* bt;
@@ -158,8 +159,8 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #endif
 #ifndef SCONV_FUSED_EARLY_INSERT
 #define SCONV_FUSED_EARLY_INSERT 1  // cache inserts issued behind the history loads:
-                                    // 0 never, 1 one-stream one-row (decode) launches,
-                                    // 2 always
+                                    // 0 never, 1 one-generation one-stream one-row
+                                    // (decode) launches, 2 always
 #endif
 #ifndef SCONV_FUSED_SERIAL_X
 #define SCONV_FUSED_SERIAL_X 0  // one input row in flight per lane (multi-generation launches)
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // arrive while the loads above are in flight; fetched at first use they
   // would add a dependent round trip after the metadata returns.  An empty
   // statement taking them as scalar inputs pins their loads here.
-  asm volatile("" ::"s"(p.n_magic), "s"(p.n_s1), "s"(p.n_s2), "s"(p.N),
+  asm volatile("" ::"s"(p.n_magic), "s"(p.n_s1), "s"(p.n_s2), "s"(p.N), "s"(p.early_insert),
                "s"(s_silu), "s"(s_res), "s"(p.cs0), "s"(p.cs2), "s"(p.bt_rs),
                "s"(out_rs));
 
@@ -714,6 +715,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // travel with, and measured slower.
   constexpr bool kEarlyInsert =
       SCONV_FUSED_EARLY_INSERT == 2 || (SCONV_FUSED_EARLY_INSERT == 1 && NTH && !MS);
+  const bool early = kEarlyInsert && p.early_insert;  // the host's choice, per launch
   auto store_row = [&](int i) {
     if (on) {
       const int64_t t = t0 + i;
@@ -722,7 +724,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
 #else
       outv[i].store(out + t * out_rs + c0);
 #endif
-      if constexpr (!kEarlyInsert) insert_row(i);
+      if (!early) insert_row(i);
     }
   };
   // Output of row i from its fp32 accumulators: SiLU, residual, round.
@@ -830,7 +832,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
       hist_req = req[i];
     }
     if constexpr (kEarlyInsert) {
-      if (i == 0 && on) {
+      if (early && i == 0 && on) {
 #pragma unroll
         for (int r = 0; r < BT; ++r)
           if (slot[r] >= 0) insert_row(r);
@@ -1249,6 +1251,13 @@ static int fused_launch(
   int64_t widest = 0;  // the largest piece of any stream, in elements
   for (int s = 0; s < num_streams; ++s) widest = streams[s].ws > widest ? streams[s].ws : widest;
   p.nt_hist = SCONV_FUSED_NT_HIST && bt == 1 && widest * es < 128;
+  // A one-stream decode launch whose waves are all resident at once issues
+  // each row's cache insert right behind its history loads (4.150 -> 4.125
+  // us at 256 requests).  Larger launches keep the stores after the
+  // arithmetic: their early stores slow the history loads they travel with.
+  p.early_insert = SCONV_FUSED_EARLY_INSERT == 2 ||
+                   (SCONV_FUSED_EARLY_INSERT == 1 && p.nt_hist && num_streams == 1 &&
+                    waves <= SCONV_FUSED_NT_LOADS_MAX_WAVES);
   p.waves_per_group = (int32_t)(threads / 64);
 
   // The gather runs in the conv's launch when this configuration has a
@@ -1276,6 +1285,7 @@ static int fused_launch(
     plan->bt_row_entries = p.bt_pref;
     plan->stream_x_loads = p.nt_x;
     plan->stream_hist_loads = p.nt_hist;
+    plan->early_inserts = p.early_insert;
     plan->tile_major = !slab_major_order(num_streams > 1, bt);
     plan->wg_threads = (int32_t)threads;
     plan->waves = waves;

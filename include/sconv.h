@@ -277,6 +277,9 @@ typedef struct sconv_fused_plan {
                                 2 its own launch right after the conv's */
   int64_t waves;             /* tiles x slabs */
   int64_t workgroups;        /* grid size (with the gather's, if in it) */
+  int32_t early_inserts;     /* cache inserts issued behind the history loads
+                                (one-stream decode launches that fit the chip
+                                in one wave generation) */
 } sconv_fused_plan_t;
 
 /*

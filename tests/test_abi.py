@@ -387,8 +387,28 @@ def test_plan_shapes_of_the_benchmarked_launches(lib):
     rc, p = _plan(lib, 256, 256, streams=4)
     assert rc == 0 and p.tile_major == 1 and p.waves == 4 * 256 * 2
     rc, p = _plan(lib, 0, 1)
-    assert rc == 0 and p.waves == 0 and p.workgroups == 0
+    assert rc == 0 and p.waves == 0 and p.workgroups == 0 and p.early_inserts == 0
     assert _plan(lib, 10, 2, W=5)[0] == 1 and b"W=5" in lib.sconv_last_error()
+
+
+def test_plan_early_inserts_only_for_one_generation_decode(lib):
+    """Cache inserts go behind the history loads only in one-stream decode
+    launches whose waves fit the chip at once (5120 waves of one-row tiles);
+    the speculative conv, a layer's four streams, the prefill and larger
+    decode batches keep them after the arithmetic."""
+    for T, expect in ((256, 1), (1024, 1), (2560, 1), (2561, 0), (4096, 0)):
+        rc, p = _plan(lib, T, T, max_blocks=min(4097, T + 1))
+        assert rc == 0 and p.rows_per_tile == 1 and p.stream_hist_loads == 1
+        assert p.early_inserts == expect, (T, p.waves)
+    rc, p = _plan(lib, 256, 256, streams=4)
+    assert rc == 0 and p.early_inserts == 0
+    rc, p = _plan(lib, 2048, 512, H=64, ws=64, D=64, N=32, max_blocks=4097)
+    assert rc == 0 and p.rows_per_tile == 4 and p.early_inserts == 0
+    rc, p = _plan(lib, 20450, 16, H=32, ws=128, D=512, max_blocks=641, folded=False)
+    assert rc == 0 and p.early_inserts == 0
+    # whole-line history pieces (no streaming history loads): no early inserts
+    rc, p = _plan(lib, 256, 256, H=16, ws=64, D=128)
+    assert rc == 0 and p.rows_per_tile == 1 and p.stream_hist_loads == 0 and p.early_inserts == 0
 
 
 def _gather_struct(conv_dim=4096, max_count=512, d_conv=3, seq_len=2048, src_ss=4096,
