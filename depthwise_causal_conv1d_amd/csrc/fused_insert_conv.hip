@@ -91,11 +91,17 @@ struct FusedParams {
 // gather's workgroups take the room its resident waves leave, then its
 // tail.  (Measured on the 512 x 4-draft step: 16.0 us per launch; gather
 // workgroups first 18.2 us; a few gather workgroups looping over the items
-// beside the conv 17.0 us; two launches 18.3 us.)
+// beside the conv 17.0 us; two launches 18.3 us; gather workgroups spread
+// among the conv's, SCONV_FUSED_GATHER_INTERLEAVE, 21.0 against 16.3 us.)
 struct FusedGatherParams : FusedParams {
   GatherParams g;
   int32_t g_dc;      // window length d_conv, 1..4
   uint32_t g_groups;
+  // Interleaved order (SCONV_FUSED_GATHER_INTERLEAVE): the grid is cut into
+  // units of 8 workgroups (one per XCD); of all_units units, g_units are the
+  // gather's, spread evenly among the conv's.  0: the conv's come first.
+  int32_t g_interleave;
+  uint32_t g_units, all_units;
 };
 
 // Request of row t: the last r in [0, n) with off[r] <= t (rows past the
@@ -161,6 +167,10 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_EARLY_INSERT 1  // cache inserts issued behind the history loads:
                                     // 0 never, 1 one-generation one-stream one-row
                                     // (decode) launches, 2 always
+#endif
+#ifndef SCONV_FUSED_GATHER_INTERLEAVE
+#define SCONV_FUSED_GATHER_INTERLEAVE 0  // combined launch: gather workgroups among the conv's
+                                         // (measured slower)
 #endif
 #ifndef SCONV_FUSED_SERIAL_X
 #define SCONV_FUSED_SERIAL_X 0  // one input row in flight per lane (multi-generation launches)
@@ -252,6 +262,7 @@ template <typename D, int VEC, int W, int BT, int QM, bool NTX, bool MS, bool NT
           bool GW = false>
 __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kernel(
     const std::conditional_t<GW, FusedGatherParams, FusedParams> p) {
+  uint32_t conv_wg = blockIdx.x;  // this workgroup's number among the conv's
   if constexpr (GW) {
     // Gather workgroups come after every conv workgroup, so the hardware
     // hands them out as the conv's resident waves leave room: they fill the
@@ -259,8 +270,20 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     // the gather body's staging, one kGatherLdsWave slice per wave
     __shared__ GatherChunk g_lds[(SCONV_FUSED_WG_THREADS / 64) * kGatherLdsWave];
     constexpr bool kGNt = SCONV_FUSED_GATHER_NT_LOADS;
-    if (blockIdx.x >= p.num_groups) {
-      const uint32_t it = blockIdx.x - p.num_groups;
+    bool gather_wg = blockIdx.x >= p.num_groups;
+    uint32_t it = blockIdx.x - p.num_groups;
+    if (p.g_interleave) {
+      // Unit u holds gather items g0*8.. (one per lane x of the unit) when
+      // the count of gather units up to u grows at u, else conv workgroups
+      // (u - g0)*8 + x; both numberings keep x = blockIdx % 8, the XCD.
+      const uint32_t u = blockIdx.x >> 3, x = blockIdx.x & 7;
+      const uint32_t g0 = (uint32_t)((uint64_t)u * p.g_units / p.all_units);
+      const uint32_t g1 = (uint32_t)((uint64_t)(u + 1) * p.g_units / p.all_units);
+      gather_wg = g1 > g0;
+      it = g0 * 8 + x;
+      conv_wg = (u - g1) * 8 + x;
+    }
+    if (gather_wg) {
       const uint32_t cbs = (uint32_t)p.g.cblocks;
       const int slot = (int)(it / cbs), cb = (int)(it - (it / cbs) * cbs);
       switch (p.g_dc) {
@@ -314,7 +337,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // second dependent round trip before any data load could start.
   // Wave counts are below 2^31 (checked on the host): 32-bit arithmetic.
   const uint32_t group_wave0 =
-      (kXcdRuns ? xcd_contiguous(blockIdx.x, p.num_groups) : blockIdx.x) * (uint32_t)p.waves_per_group;
+      (kXcdRuns ? xcd_contiguous(conv_wg, p.num_groups) : conv_wg) * (uint32_t)p.waves_per_group;
   uint32_t wave = group_wave0 + (uint32_t)uniform(threadIdx.x >> 6);
   // A wave past the end works on the last tile and writes nothing (no early
   // return: it would split the parameter loads around the branch).
@@ -1300,6 +1323,9 @@ static int fused_launch(
     q.g_dc = gather->d_conv;
     q.g_groups = (uint32_t)g_groups;
     const uint32_t all = (uint32_t)(grid + g_groups);
+    q.g_interleave = SCONV_FUSED_GATHER_INTERLEAVE && grid % 8 == 0 && g_groups % 8 == 0;
+    q.g_units = (uint32_t)(g_groups / 8);
+    q.all_units = all / 8;
     if (dtype == SCONV_BF16) launch_gw_w<Bf16, 8>(W, q, all, threads, stream);
     else launch_gw_w<F32, 4>(W, q, all, threads, stream);
     return check_launch(fn);
