@@ -272,7 +272,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     constexpr bool kGNt = SCONV_FUSED_GATHER_NT_LOADS;
     bool gather_wg = blockIdx.x >= p.num_groups;
     uint32_t it = blockIdx.x - p.num_groups;
-    if (p.g_interleave) {
+    if (SCONV_FUSED_GATHER_INTERLEAVE && p.g_interleave) {
       // Unit u holds gather items g0*8.. (one per lane x of the unit) when
       // the count of gather units up to u grows at u, else conv workgroups
       // (u - g0)*8 + x; both numberings keep x = blockIdx % 8, the XCD.
