@@ -1285,8 +1285,9 @@ def decode_floors(P, stream, names):
     return lat
 
 
-# One mixed-prefill stream launch moves 469.7 MB (config 3): the prefill
-# pattern is also measured at that size, as read n : write 2n.
+# One mixed-prefill stream launch (16 requests, 4 streams of C = 4096) moves
+# 469.7 MB: the prefill pattern is also measured at that size, as read n :
+# write 2n.
 PREFILL_LAUNCH_BYTES = 469_712_208
 
 
