@@ -1075,33 +1075,40 @@ def measure(wl, name, K, Wm, reps, budget, stream):
 
 PROBE_SRC = os.path.join(ROOT, "bench_probes.hip")
 PROBE_LIB = os.path.join(ROOT, "bench_probes.so")
+PROBE_LIB_PRELOAD = os.path.join(ROOT, "bench_probes_preload.so")
 
 
 def build_probes(verbose=False) -> str:
-    """Compile the measurement probes (bench_probes.hip) for gfx950."""
+    """Compile the measurement probes (bench_probes.hip) for gfx950, twice:
+    as they are, and with their leading kernel arguments preloaded into
+    SGPRs by the compiler (PROBE_LIB_PRELOAD), so that the latency floors
+    show what an argument load costs at the decode launch shape."""
     import subprocess
 
     from depthwise_causal_conv1d_amd import build as b
-    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
-    cmd = [b.hipcc(), f"--offload-arch={b.ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", tmp,
-           PROBE_SRC]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building bench_probes.so")
-    os.replace(tmp, PROBE_LIB)
+    for out, extra in ((PROBE_LIB, []),
+                       (PROBE_LIB_PRELOAD, ["-mllvm", "-amdgpu-kernarg-preload-count=16"])):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [b.hipcc(), f"--offload-arch={b.ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+               "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *extra,
+               "-o", tmp, PROBE_SRC]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+        os.replace(tmp, out)
     return PROBE_LIB
 
 
-def _probe_lib():
+def _probe_lib(path=None):
     import ctypes
-    if not os.path.exists(PROBE_LIB):
-        raise ImportError(f"{PROBE_LIB} is missing: build it with `python -c 'import bench; "
+    path = path or PROBE_LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -c 'import bench; "
                           "bench.build_probes()'` (or __graft_entry__.build())")
-    P = ctypes.CDLL(PROBE_LIB)
+    P = ctypes.CDLL(path)
     V, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     U32 = ctypes.c_uint32
     P.probe_read.argtypes = [V, I64, V, I64, I32, U32, V]
@@ -1308,9 +1315,12 @@ def run_probes(stream):
     res["read_write2_pieces_256_of_1024_at_prefill_launch_size"] = at[
         "read_write2_pieces_256_of_1024"]
     res["prefill_layout"] = prefill_layout(P, stream)
-    res["decode_shape_floors_us"] = decode_floors(
-        P, stream, ["empty", "load_store", "table_row", "table_row_then_3_tap_rows",
-                    "meta_then_table_row", "meta_table_row_then_3_tap_rows"])
+    floors = ["empty", "load_store", "table_row", "table_row_then_3_tap_rows",
+              "meta_then_table_row", "meta_table_row_then_3_tap_rows"]
+    res["decode_shape_floors_us"] = decode_floors(P, stream, floors)
+    # the same probes with their kernel arguments preloaded into SGPRs
+    res["decode_shape_floors_us_args_preloaded"] = decode_floors(
+        _probe_lib(PROBE_LIB_PRELOAD), stream, floors)
     res["decode_shape"] = {"waves": 512, "threads_per_workgroup": 64, "launches_per_graph": 512}
     return res
 
