@@ -36,6 +36,9 @@ def flags(defines=()):
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # leading scalar kernel arguments preloaded into SGPRs by the
+            # hardware (the fused kernel's first-hop values)
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-I", os.path.join(HERE, "..", "include"), *[f"-D{d}" for d in defines]]
 
 

@@ -53,8 +53,9 @@ struct FusedStream {
 };
 
 struct FusedParams {
-  // Small fields first: they are needed before anything else and then come
-  // in with the first scalar load of the parameters.
+  // The kernel takes the launch geometry, the metadata and block-table
+  // pointers and the request divider from its leading arguments (built
+  // from these fields by launch_fused); the rest it reads here.
   uint32_t num_groups;      // grid size in workgroups
   int32_t waves_per_group;  // workgroup size / 64
   int32_t num_slabs;        // over all streams
@@ -261,7 +262,17 @@ static_assert(kQslRegMax <= 512, "8 offsets per lane");
 template <typename D, int VEC, int W, int BT, int QM, bool NTX, bool MS, bool NTH = false,
           bool GW = false>
 __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kernel(
-    const std::conditional_t<GW, FusedGatherParams, FusedParams> p) {
+    const int64_t* __restrict__ a_positions, const int64_t* __restrict__ a_slot,
+    const int32_t* __restrict__ a_qsl, const int32_t* __restrict__ a_bt, int32_t a_T,
+    uint32_t a_k_magic, int32_t a_num_reqs, int32_t a_bt_rs, int32_t a_num_slabs,
+    uint32_t a_packed, const std::conditional_t<GW, FusedGatherParams, FusedParams> p) {
+  // Launch geometry from the leading arguments: tiles, the conv's waves and
+  // its workgroups (the host sizes the conv's grid by the same ceiling).
+  const uint32_t num_tiles = ((uint32_t)a_T + (uint32_t)(BT - 1)) / (uint32_t)BT;
+  const uint32_t wpg_log2 = a_packed >> 20;
+  const uint32_t waves_per_group = 1u << wpg_log2;
+  const uint32_t total_waves = num_tiles * (uint32_t)a_num_slabs;
+  const uint32_t num_groups = (total_waves + waves_per_group - 1) >> wpg_log2;
   uint32_t conv_wg = blockIdx.x;  // this workgroup's number among the conv's
   if constexpr (GW) {
     // Gather workgroups come after every conv workgroup, so the hardware
@@ -270,8 +281,8 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     // the gather body's staging, one kGatherLdsWave slice per wave
     __shared__ GatherChunk g_lds[(SCONV_FUSED_WG_THREADS / 64) * kGatherLdsWave];
     constexpr bool kGNt = SCONV_FUSED_GATHER_NT_LOADS;
-    bool gather_wg = blockIdx.x >= p.num_groups;
-    uint32_t it = blockIdx.x - p.num_groups;
+    bool gather_wg = blockIdx.x >= num_groups;
+    uint32_t it = blockIdx.x - num_groups;
     if (SCONV_FUSED_GATHER_INTERLEAVE && p.g_interleave) {
       // Unit u holds gather items g0*8.. (one per lane x of the unit) when
       // the count of gather units up to u grows at u, else conv workgroups
@@ -298,25 +309,37 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   using S = typename D::storage;
   using P = Pack<D, VEC>;
   S* __restrict__ cache = static_cast<S*>(p.cache);
-  const int64_t* __restrict__ positions = p.positions;
-  const int64_t* __restrict__ slots = p.slot;
+  const int64_t* __restrict__ positions = a_positions;
+  const int64_t* __restrict__ slots = a_slot;
   const int32_t* __restrict__ seq_idx = p.seq_idx;
   const int32_t* __restrict__ qstart = p.qs;
-  const int32_t* __restrict__ btab = p.bt;
+  const int32_t* __restrict__ btab = a_bt;
+  // The leading arguments (lead_args on the host) arrive preloaded in
+  // scalar registers; unpack the packed word.
+  const uint32_t k_s1 = a_packed & 1u, k_s2 = (a_packed >> 1) & 31u;
+  const int32_t bt_pref = (int32_t)((a_packed >> 8) & 0xfffu);
 
-  // Fields needed to place this wave and to issue its metadata loads (the
-  // geometry, the streams' first slabs, the metadata pointers) all come in
-  // the first batch of parameter loads.
-  asm volatile("" ::"s"(p.num_groups), "s"(p.waves_per_group), "s"(p.num_tiles),
-               "s"(p.positions), "s"(p.slot), "s"(p.qsl), "s"(p.seq_idx), "s"(p.qs),
-               "s"(p.num_reqs), "s"(p.T));
-  if constexpr (MS)
-    asm volatile("" ::"s"(p.num_streams), "s"(p.st[1].slab0), "s"(p.st[2].slab0),
-                 "s"(p.st[3].slab0));
+  // Fields of the parameter block needed to place this wave and to issue
+  // its metadata loads (the streams' first slabs, the per-row metadata
+  // pointers) all come in the first batch of parameter loads.  A one-stream
+  // launch that guesses requests finds everything for its first loads in
+  // the leading arguments and waits for the block only behind those loads
+  // (below).  A several-stream one waits here for all of it: its waves need
+  // the streams' first slabs before they can find their input rows, and
+  // waiting behind the first loads added scalar round trips in front of
+  // them (a layer's decode step, 5.58-6.05 against 5.36 us).
   constexpr bool kGuess = QM == kQslGuess;
+  constexpr bool kPinEarly = !kGuess || MS;
+  if constexpr (kPinEarly) {
+    asm volatile("" ::"s"(p.seq_idx), "s"(p.qs));
+    if constexpr (MS)
+      asm volatile("" ::"s"(p.num_streams), "s"(p.st[1].slab0), "s"(p.st[2].slab0),
+                   "s"(p.st[3].slab0));
+    if constexpr (kGuess)
+      asm volatile("" ::"s"(p.n_magic), "s"(p.n_s1), "s"(p.n_s2), "s"(p.N), "s"(p.early_insert),
+                   "s"(p.cs0), "s"(p.cs1), "s"(p.cs2), "s"(p.bt_rs));
+  }
   constexpr bool kRowAhead = kGuess && BT == 1;  // block-table row read ahead
-  if constexpr (kGuess) asm volatile("" ::"s"(p.k_magic), "s"(p.k_s1), "s"(p.k_s2));
-  if constexpr (kRowAhead) asm volatile("" ::"s"(p.bt), "s"(p.bt_rs), "s"(p.bt_pref));
   constexpr int kOrder = wave_order(MS, BT);
   constexpr bool kSlabMajor = kOrder == kOrderSlabMajor;
   // Workgroups are renumbered so that each XCD runs one contiguous range of
@@ -337,11 +360,10 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // second dependent round trip before any data load could start.
   // Wave counts are below 2^31 (checked on the host): 32-bit arithmetic.
   const uint32_t group_wave0 =
-      (kXcdRuns ? xcd_contiguous(conv_wg, p.num_groups) : conv_wg) * (uint32_t)p.waves_per_group;
+      (kXcdRuns ? xcd_contiguous(conv_wg, num_groups) : conv_wg) * waves_per_group;
   uint32_t wave = group_wave0 + (uint32_t)uniform(threadIdx.x >> 6);
   // A wave past the end works on the last tile and writes nothing (no early
   // return: it would split the parameter loads around the branch).
-  const uint32_t total_waves = (uint32_t)p.num_tiles * (uint32_t)p.num_slabs;
   const bool live_wave = wave < total_waves;
   if (!live_wave) wave = total_waves - 1;
   // Slab-major: consecutive waves walk consecutive tiles of one slab, so
@@ -353,19 +375,19 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   uint32_t tile;
   int slab;
   if constexpr (kSlabMajor) {
-    const uint32_t slab_u = wave / (uint32_t)p.num_tiles;
-    tile = wave - slab_u * (uint32_t)p.num_tiles;
+    const uint32_t slab_u = wave / num_tiles;
+    tile = wave - slab_u * num_tiles;
     slab = (int)slab_u;
   } else if constexpr (kOrder == kOrderStreamInner) {
     // every stream has num_slabs / num_streams slabs (checked on the host)
     const uint32_t S = (uint32_t)p.num_streams;
     const uint32_t rest = wave / S;
-    const uint32_t j = rest / (uint32_t)p.num_tiles;
-    tile = rest - j * (uint32_t)p.num_tiles;
-    slab = (int)((wave - rest * S) * ((uint32_t)p.num_slabs / S) + j);
+    const uint32_t j = rest / num_tiles;
+    tile = rest - j * num_tiles;
+    slab = (int)((wave - rest * S) * ((uint32_t)a_num_slabs / S) + j);
   } else {
-    tile = wave / (uint32_t)p.num_slabs;
-    slab = (int)(wave - tile * (uint32_t)p.num_slabs);
+    tile = wave / (uint32_t)a_num_slabs;
+    slab = (int)(wave - tile * (uint32_t)a_num_slabs);
   }
   const int64_t t0 = (int64_t)tile * BT;
 
@@ -378,7 +400,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // Every load below is unconditional, from an address clamped into the
   // buffers (rows past T, lanes past C): a conditional load would join its
   // value with a default and force an immediate wait for it.
-  const int64_t t_last = p.T - 1;
+  const int64_t t_last = (int64_t)a_T - 1;
   constexpr int QSL = QM != kQslOff;
   constexpr int F = QSL && !kGuess ? 3 : 5;
   constexpr int NM = F * BT;
@@ -394,10 +416,10 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     if constexpr (kGuess) {
       // offsets g and g+1 of the row's guessed request (clamped below
       // num_reqs: both exist)
-      const int32_t gr = (int32_t)div_magic((uint32_t)t, p.k_magic, p.k_s1, p.k_s2);
-      const int32_t gq = gr < p.num_reqs - 1 ? gr : p.num_reqs - 1;
+      const int32_t gr = (int32_t)div_magic((uint32_t)t, a_k_magic, k_s1, k_s2);
+      const int32_t gq = gr < a_num_reqs - 1 ? gr : a_num_reqs - 1;
       src = f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
-                  : p.qsl + gq + (f == 4);
+                  : a_qsl + gq + (f == 4);
     } else {
       src = f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
                   : (f == 3 ? seq_idx : qstart) + t;
@@ -412,20 +434,33 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = j * 64 + lane;
-      ov[j] = p.qsl[r < p.num_reqs ? r : p.num_reqs - 1];
+      ov[j] = a_qsl[r < a_num_reqs ? r : a_num_reqs - 1];
     }
   }
   // Block-table row t (the row's guessed request, clamped into the table):
   // entry 64*j + L in brow[j] of lane L, bt_pref entries, clamped.
   int32_t brow[4];
-  const int32_t row_guess = (int32_t)(t0 < (int64_t)p.num_reqs - 1 ? t0 : p.num_reqs - 1);
+  const int32_t row_guess = (int32_t)(t0 < (int64_t)a_num_reqs - 1 ? t0 : a_num_reqs - 1);
   if constexpr (kRowAhead) {
-    const int32_t* row = btab + (int64_t)row_guess * p.bt_rs;
+    const int32_t* row = btab + (int64_t)row_guess * a_bt_rs;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = j * 64 + lane;
-      brow[j] = row[e < p.bt_pref ? e : p.bt_pref - 1];
+      brow[j] = row[e < bt_pref ? e : bt_pref - 1];
     }
+  }
+
+  // A one-stream guessing launch has now issued its first loads: the
+  // parameter block's fields that the rest of the wave needs are waited for
+  // here, in one batch whose loads were issued at the start; fetched at
+  // first use, some would add a dependent round trip in front of the
+  // history loads.
+  if constexpr (kGuess && !kPinEarly) {
+    asm volatile("" ::"s"(p.n_magic), "s"(p.n_s1), "s"(p.n_s2), "s"(p.N), "s"(p.early_insert),
+                 "s"(p.cs0), "s"(p.cs1), "s"(p.cs2), "s"(p.bt_rs));
+    asm volatile("" ::"s"(p.st[0].x), "s"(p.st[0].w), "s"(p.st[0].out), "s"(p.st[0].x_rs),
+                 "s"(p.st[0].out_rs), "s"(p.st[0].C), "s"(p.st[0].ws), "s"(p.st[0].off_s),
+                 "s"(p.st[0].silu), "s"(p.st[0].residual));
   }
 
   // The stream owning this slab (its first slab is the last one <= slab).
@@ -505,14 +540,14 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   constexpr bool kLdsHalo = false;
 #endif
   constexpr bool kLdsWts = kLdsHalo && VEC > 1 && SCONV_FUSED_LDS_WEIGHTS;
-  const int wpg = (int)p.waves_per_group;
+  const int wpg = (int)waves_per_group;
   const int wig = (int)(threadIdx.x >> 6);  // wave in workgroup
   bool wts_shared = false;
   if constexpr (kLdsWts) {
     const uint32_t last = total_waves - 1;
     const uint32_t wa = group_wave0 < last ? group_wave0 : last;
     const uint32_t wb = group_wave0 + (uint32_t)wpg - 1 < last ? group_wave0 + (uint32_t)wpg - 1 : last;
-    wts_shared = wa / (uint32_t)p.num_tiles == wb / (uint32_t)p.num_tiles;
+    wts_shared = wa / num_tiles == wb / num_tiles;
   }
   if constexpr (VEC > 1) {
     static_assert(kN % kChunk == 0, "packed weights come in whole 16-byte chunks");
@@ -565,15 +600,15 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
 #pragma unroll
     for (int i = 0; i < BT; ++i) {
       const int32_t t = (int32_t)(t0 + i < t_last ? t0 + i : t_last);
-      const int32_t g = (int32_t)div_magic((uint32_t)t, p.k_magic, p.k_s1, p.k_s2);
-      const int32_t gq = g < p.num_reqs - 1 ? g : p.num_reqs - 1;
+      const int32_t g = (int32_t)div_magic((uint32_t)t, a_k_magic, k_s1, k_s2);
+      const int32_t gq = g < a_num_reqs - 1 ? g : a_num_reqs - 1;
       const int32_t lo = req[i], hi = qs[i];
       if (lo <= t && t < hi) {
         req[i] = gq;
         qs[i] = lo;
       } else if (slot[i] >= 0) {
-        req[i] = find_request(p.qsl, p.num_reqs, t, lane);
-        qs[i] = uniform(p.qsl[req[i]]);
+        req[i] = find_request(a_qsl, a_num_reqs, t, lane);
+        qs[i] = uniform(a_qsl[req[i]]);
       } else {
         req[i] = 0;
         qs[i] = 0;
@@ -588,7 +623,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     // one request.
 #pragma unroll
     for (int run = 0; run < 8; ++run)
-      if (run * 64 + lane >= p.num_reqs) ov[run] = INT32_MAX;
+      if (run * 64 + lane >= a_num_reqs) ov[run] = INT32_MAX;
     auto count_le = [&](int32_t row) -> int32_t {
       int32_t c = 0;
 #pragma unroll
@@ -639,10 +674,10 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
     // tile (empty requests) can a row lie past that window; such a row
     // searches on its own.  (Staging the offsets in LDS per workgroup was
     // measured slower: it moves every offset to every workgroup.)
-    const int32_t n = p.num_reqs;
+    const int32_t n = a_num_reqs;
     const int64_t tf = t0 < t_last ? t0 : t_last;
-    const int32_t r0 = find_request(p.qsl, n, tf, lane);
-    const int32_t wnd = p.qsl[r0 + lane < n ? r0 + lane : n - 1];
+    const int32_t r0 = find_request(a_qsl, n, tf, lane);
+    const int32_t wnd = a_qsl[r0 + lane < n ? r0 + lane : n - 1];
     const bool in_window = lane < n - r0;
     const bool beyond = r0 + 64 < n;
 #pragma unroll
@@ -653,8 +688,8 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
       req[i] = r0 + k;
       qs[i] = __builtin_amdgcn_readlane(wnd, k);
       if (k == 63 && beyond && slot[i] >= 0) {
-        req[i] = find_request(p.qsl, n, t, lane);
-        qs[i] = uniform(p.qsl[req[i]]);
+        req[i] = find_request(a_qsl, n, t, lane);
+        qs[i] = uniform(a_qsl[req[i]]);
       }
     }
   }
@@ -817,7 +852,7 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
       }
       // History row 1 has the largest block index of the W-1.
       bool in_regs = false;
-      if constexpr (kRowAhead) in_regs = req[i] == row_guess && hlb[0] < (uint32_t)p.bt_pref;
+      if constexpr (kRowAhead) in_regs = req[i] == row_guess && hlb[0] < (uint32_t)bt_pref;
       if (in_regs) {
 #pragma unroll
         for (int m = 1; m <= W - 1; ++m) {
@@ -918,25 +953,46 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
 
 // ---------------------------------------------------------------- dispatch
 
+// A fused launch passes, ahead of its parameter block, the values every
+// wave needs before its first memory access as leading scalar arguments
+// (the kernel's a_* arguments; an aggregate argument is never preloaded):
+// the build has the compiler ask the hardware to preload the first 14
+// dwords of the argument segment into scalar registers
+// (-amdgpu-kernarg-preload-count), which takes the round trip of a first
+// parameter load off the front of a decode launch's dependent chain.
+// Packed word: bit 0 k_s1, bits 1-5 k_s2, bits 8-19 bt_pref, bits 20-31
+// log2 of the waves per workgroup (the host keeps each field in range).
+static_assert((SCONV_FUSED_WG_THREADS & (SCONV_FUSED_WG_THREADS - 1)) == 0,
+              "workgroups of a power-of-two number of waves");
+template <typename Kern, typename Prm>
+static void launch_fused(Kern kern, uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t s,
+                         const Prm& p) {
+  const uint32_t packed = (p.k_s1 & 1u) | ((p.k_s2 & 31u) << 1) | ((uint32_t)p.bt_pref << 8) |
+                          ((uint32_t)__builtin_ctz((uint32_t)p.waves_per_group) << 20);
+  const int32_t bt_rs = p.bt_rs <= INT32_MAX ? (int32_t)p.bt_rs : 0;  // read ahead only below
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, p.positions, p.slot, p.qsl, p.bt,
+                     (int32_t)p.T, p.k_magic, p.num_reqs, bt_rs, p.num_slabs, packed, p);
+}
+
 template <typename D, int VEC, int W, int BT, bool NTX, bool MS, bool NTH = false>
 static void launch_q(const FusedParams& p, uint32_t grid, uint32_t threads, hipStream_t s) {
   constexpr uint32_t kExtraLds = NTX || BT == 1 ? 0u : (uint32_t)SCONV_FUSED_EXTRA_LDS;
   if constexpr (W > 1) {
     if (p.guess) {
-      hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslGuess, NTX, MS, NTH>),
-                         dim3(grid), dim3(threads), kExtraLds, s, p);
+      launch_fused(fused_insert_conv_kernel<D, VEC, W, BT, kQslGuess, NTX, MS, NTH>,
+                 grid, threads, kExtraLds, s, p);
       return;
     }
   }
   if (p.qsl && p.num_reqs <= kQslRegMax) {
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs, NTX, MS, NTH>),
-                       dim3(grid), dim3(threads), kExtraLds, s, p);
+    launch_fused(fused_insert_conv_kernel<D, VEC, W, BT, kQslRegs, NTX, MS, NTH>,
+                 grid, threads, kExtraLds, s, p);
   } else if (p.qsl) {
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslSearch, NTX, MS, NTH>),
-                       dim3(grid), dim3(threads), kExtraLds, s, p);
+    launch_fused(fused_insert_conv_kernel<D, VEC, W, BT, kQslSearch, NTX, MS, NTH>,
+                 grid, threads, kExtraLds, s, p);
   } else {
-    hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, BT, kQslOff, NTX, MS, NTH>),
-                       dim3(grid), dim3(threads), kExtraLds, s, p);
+    launch_fused(fused_insert_conv_kernel<D, VEC, W, BT, kQslOff, NTX, MS, NTH>,
+                 grid, threads, kExtraLds, s, p);
   }
 }
 
@@ -949,22 +1005,20 @@ static void launch_gw(const FusedGatherParams& p, uint32_t grid, uint32_t thread
   if constexpr (VEC > 1) {
     if constexpr (W > 1) {
       if (p.guess) {
-        hipLaunchKernelGGL(
-            (fused_insert_conv_kernel<D, VEC, W, 4, kQslGuess, true, MS, false, true>),
-            dim3(grid), dim3(threads), 0, s, p);
+        launch_fused(fused_insert_conv_kernel<D, VEC, W, 4, kQslGuess, true, MS, false, true>,
+                 grid, threads, 0, s, p);
         return;
       }
     }
     if (p.qsl && p.num_reqs <= kQslRegMax) {
-      hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, 4, kQslRegs, true, MS, false, true>),
-                         dim3(grid), dim3(threads), 0, s, p);
+      launch_fused(fused_insert_conv_kernel<D, VEC, W, 4, kQslRegs, true, MS, false, true>,
+                 grid, threads, 0, s, p);
     } else if (p.qsl) {
-      hipLaunchKernelGGL(
-          (fused_insert_conv_kernel<D, VEC, W, 4, kQslSearch, true, MS, false, true>),
-          dim3(grid), dim3(threads), 0, s, p);
+      launch_fused(fused_insert_conv_kernel<D, VEC, W, 4, kQslSearch, true, MS, false, true>,
+                 grid, threads, 0, s, p);
     } else {
-      hipLaunchKernelGGL((fused_insert_conv_kernel<D, VEC, W, 4, kQslOff, true, MS, false, true>),
-                         dim3(grid), dim3(threads), 0, s, p);
+      launch_fused(fused_insert_conv_kernel<D, VEC, W, 4, kQslOff, true, MS, false, true>,
+                 grid, threads, 0, s, p);
     }
   }
 }
@@ -1241,7 +1295,7 @@ static int fused_launch(
   const bool folded = qsl != nullptr && num_reqs >= 1;
   const int64_t k = !folded || T <= num_reqs ? 1 : T / num_reqs;
   p.guess = SCONV_FUSED_BT_ROW && folded && W > 1 && k <= kGuessMaxRows &&
-            (T <= num_reqs || T % num_reqs == 0);
+            (T <= num_reqs || T % num_reqs == 0) && bt_row_stride <= INT32_MAX;
   magic_for((uint32_t)(k > 0 ? k : 1), p.k_magic, p.k_s1, p.k_s2);
   // Guessed one-row tiles read block-table row t ahead (the kernel's
   // kRowAhead form): with one row per request all of it that fits in the

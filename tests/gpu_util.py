@@ -39,6 +39,18 @@ def gpu_fused(case, dev="cuda", out_init=None, fold=False):
     return out, cache, seq_idx, qs
 
 
+def gpu_plan(case, dev="cuda"):
+    """The launch gpu_fused(case) makes for its fused call (per-row
+    request buffers), as sconv_fused_plan's dict; nothing is launched."""
+    import depthwise_causal_conv1d_amd as lib
+    seq_idx = torch.zeros(case.T, dtype=torch.int32, device=dev)
+    return lib.sconv_fused_plan([case.x.to(dev)], [case.weight.to(dev)], case.cache.to(dev),
+                                case.positions.to(dev), case.block_table.to(dev),
+                                case.slot_mapping.to(dev), [case.off_s], [case.ws],
+                                case.block_size, case.activation, case.use_residual,
+                                seq_idx=seq_idx, query_start=seq_idx.clone())
+
+
 def oracle_fused(case, cache=None, block_table=None, slot_mapping=None, out_init=None):
     """The oracle on the same inputs (optionally a compacted cache)."""
     import oracle

@@ -322,7 +322,7 @@ STAND_IN = 1 << 24
 
 
 def _plan(lib, T, num_reqs, H=32, ws=32, D=128, N=16, max_blocks=257, folded=True, W=4,
-          streams=1, dt=1, gather=None):
+          streams=1, dt=1, gather=None, bt_rs=None):
     """sconv_fused_plan on stand-in addresses (16-byte aligned, never
     dereferenced): returns (rc, plan)."""
     from depthwise_causal_conv1d_amd import _lib
@@ -337,7 +337,8 @@ def _plan(lib, T, num_reqs, H=32, ws=32, D=128, N=16, max_blocks=257, folded=Tru
     plan = _lib.FusedPlan()
     meta = (None, None, base, num_reqs) if folded else (base, base, None, 0)
     rc = lib.sconv_fused_plan(arr, streams, cache, 1 << 16, H, N, D, H * N * D, N * D, D, base,
-                              base, max_blocks, max_blocks, *meta, base, T, W, dt,
+                              base, max_blocks if bt_rs is None else bt_rs, max_blocks, *meta,
+                              base, T, W, dt,
                               None if gather is None else ctypes.byref(gather),
                               ctypes.byref(plan))
     return rc, plan
@@ -365,6 +366,16 @@ def test_plan_guessed_one_row_tiles_read_inside_the_table(lib):
         else:
             assert plan.bt_row_entries == 0, (T, R, mb)
     assert seen_guess_row > 20
+
+
+def test_plan_guess_needs_a_32_bit_table_stride(lib):
+    """The guessed forms take the block-table row stride as a 32-bit leading
+    kernel argument; a wider stride plans the searched form instead."""
+    for T, R in ((256, 256), (2048, 512)):
+        rc, p = _plan(lib, T, R, max_blocks=257, bt_rs=(1 << 31) - 1)
+        assert rc == 0 and p.request_mode == 3, lib.sconv_last_error()
+        rc, p = _plan(lib, T, R, max_blocks=257, bt_rs=1 << 31)
+        assert rc == 0 and p.request_mode == 1 and p.bt_row_entries == 0
 
 
 def test_plan_shapes_of_the_benchmarked_launches(lib):

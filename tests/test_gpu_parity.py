@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import workloads
-from tests.gpu_util import (SENTINEL, dtype_name, gpu_fused, gpu_fused_streams, live_rows,
-                            oracle_fused, oracle_fused_streams, written_cache_values)
+from tests.gpu_util import (SENTINEL, dtype_name, gpu_fused, gpu_fused_streams, gpu_plan,
+                            live_rows, oracle_fused, oracle_fused_streams, written_cache_values)
 from tests.helpers import assert_bits_equal, assert_close, assert_finite, to_np
 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("oracle_lib")]
@@ -147,6 +147,37 @@ def test_fused_tile_shapes(T_total, C_heads, fold):
                                 block_size=16, W=4, dtype=torch.bfloat16,
                                 pad_count=T_total // 10, tail_pad=5)
     check_fused(case, f"tiles T={T_total}", fold=fold)
+
+
+GENERATIONS = [
+    # name, dtype, W, H, ws, D, off_s, N, requests, pad
+    ("bf16-w4-c4096", torch.bfloat16, 4, 32, 128, 512, 128, 16, 19, 0.1),
+    ("bf16-w3-n24-partial-slab", torch.bfloat16, 3, 12, 64, 128, 0, 24, 7, 0.05),
+    ("bf16-w2-ragged-c", torch.bfloat16, 2, 18, 96, 96, 0, 16, 31, 0.2),
+    ("bf16-w1", torch.bfloat16, 1, 16, 64, 64, 0, 16, 5, 0.1),
+    ("f32-w4", torch.float32, 4, 32, 64, 128, 64, 32, 11, 0.1),
+]
+
+
+@pytest.mark.parametrize("spec", GENERATIONS, ids=[g[0] for g in GENERATIONS])
+def test_fused_several_wave_generations(spec):
+    """Prefill-shaped launches of several wave generations with per-row
+    request buffers: four-row tiles whose halo rows pass between the waves
+    of a workgroup through LDS.  Requests straddle tiles and workgroups,
+    some start at position 0, some continue long histories, PAD rows fall
+    anywhere (inside requests too), and the last slab may be partial."""
+    name, dt, W, H, ws, D, off, N, R, pad = spec
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    T_total = int(rng.integers(11000, 14000))
+    cuts = np.sort(rng.choice(np.arange(1, T_total), R - 1, replace=False))
+    new = np.diff(np.concatenate([[0], cuts, [T_total]])).tolist()
+    ctx = [0 if r % 4 == 0 else int(rng.integers(1, 3000)) for r in range(R)]
+    case = workloads.fused_case(zlib.crc32(name.encode()) % 1000, new, ctx, H=H, D=D, ws=ws,
+                                off_s=off, block_size=N, W=W, dtype=dt,
+                                pad_count=int(T_total * pad), tail_pad=7)
+    plan = gpu_plan(case)
+    assert (plan["rows_per_tile"], plan["stream_x_loads"], plan["request_mode"]) == (4, 0, 0), plan
+    check_fused(case, f"{name} T={case.T}")
 
 
 @pytest.mark.parametrize("fold", [False, True], ids=["meta", "qsl"])
