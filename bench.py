@@ -92,40 +92,69 @@ def _strip_comments(text: str) -> str:
     return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
-def kernel_source_digest() -> str:
-    """Hash of the GPU sources without their comments, to tell whether
-    stored counters were taken on the kernels as they are now."""
-    h = hashlib.sha256()
+def _kernel_sources(kernel: str):
+    """The csrc/ files a kernel is built from: the source that defines it
+    and the headers it includes, transitively."""
+    first = None
     for name in sorted(os.listdir(CSRC)):
+        if name.endswith(".hip"):
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                if re.search(r"\bvoid\s+" + re.escape(kernel) + r"\s*\(", f.read()):
+                    first = name
+                    break
+    if first is None:
+        raise KeyError(f"no source in {CSRC} defines {kernel}")
+    seen, todo = [], [first]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.append(name)
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            for inc in re.findall(r'#include\s+"([^"/]+)"', f.read()):
+                if os.path.exists(os.path.join(CSRC, inc)):
+                    todo.append(inc)
+    return sorted(seen)
+
+
+def kernel_source_digest(kernel: str = None) -> str:
+    """Hash of GPU sources without their comments, to tell whether stored
+    traces and counters were taken on the kernels as they are now: of the
+    files `kernel` is built from, or (no kernel) of every source."""
+    names = sorted(os.listdir(CSRC)) if kernel is None else _kernel_sources(kernel)
+    h = hashlib.sha256()
+    for name in names:
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(name.encode() + _strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, kernel: str):
     """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current sources."""
+    rocprofv3 counter summary, if it was taken on the kernel's current
+    sources."""
     path = os.path.join(PROFILES, f"counters_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"kernel_sources:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.e+]+)", text)
-    if not m or not t or m.group(1) != kernel_source_digest():
+    if not m or not t or m.group(1) != kernel_source_digest(kernel):
         return None
     return float(t.group(1))
 
 
 def stored_trace(kernel: str, workload: str):
     """Average duration (us) of the dominant kernel in the committed
-    rocprofv3 kernel-trace summary, if it was taken on the current sources."""
+    rocprofv3 kernel-trace summary, if it was taken on the kernel's current
+    sources."""
     path = os.path.join(PROFILES, f"{kernel.replace('_kernel', '')}_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"kernel_sources:\s*([0-9a-f]+)", text)
     t = re.search(r"trace_avg_us:\s*([0-9.]+)", text)
-    if not m or not t or m.group(1) != kernel_source_digest():
+    if not m or not t or m.group(1) != kernel_source_digest(kernel):
         return None
     return float(t.group(1))
 
@@ -1048,7 +1077,8 @@ def measure(wl, name, K, Wm, reps, budget, stream):
             "frac_trace": (round(wl.bytes_per_launch / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                            if trace_us else None),
             "headline": "frac: HIP events around graph replays of the kernel alone",
-            "traffic": stored_traffic(name) if stored else None, "kernel": wl.kernel_name,
+            "traffic": stored_traffic(name, wl.kernel_name) if stored else None,
+            "kernel": wl.kernel_name,
             "bytes_per_launch": wl.bytes_per_launch, "launch_us": round(kern_us, 3),
             "launch_us_trace": trace_us,
             # the same bytes over the event-timed step, where a step is one
@@ -1329,8 +1359,9 @@ def machine_reference(stream, prefill_launch_bytes=PREFILL_LAUNCH_BYTES):
     """What the same GPU reaches on the headline's patterns, for the default
     line: the copy and the mixed prefill's write patterns (TB/s; the pieces
     pattern at 1 GiB per stream and at the prefill launch's own size), and
-    the decode kernel's dependent chain at its launch shape (µs).  None when
-    the probe kernels are not built."""
+    the decode kernel's dependent chain at its launch shape (µs), with its
+    kernel arguments preloaded into SGPRs as the fused kernel's are.  None
+    when the probe kernels are not built."""
     try:
         P = _probe_lib()
     except ImportError as e:
@@ -1342,6 +1373,10 @@ def machine_reference(stream, prefill_launch_bytes=PREFILL_LAUNCH_BYTES):
                          n16=_launch_n16(prefill_launch_bytes))["read_write2_pieces_256_of_1024"]
     lay = prefill_layout(P, stream)
     f = decode_floors(P, stream, ["empty", "table_row_then_3_tap_rows"])
+    # The fused kernel takes its first-hop values as leading arguments that
+    # the hardware preloads into SGPRs: its floor is the chain probe built
+    # the same way (the unpreloaded chain is reported beside it).
+    fp = decode_floors(_probe_lib(PROBE_LIB_PRELOAD), stream, ["table_row_then_3_tap_rows"])
     pieces = c["read_write2_pieces_256_of_1024"]
     return {"source": "bench_probes.hip in this run (bench.py --probe measures all)",
             "forms": "best of %d workgroup shapes x 2 store forms x %d occupancies" % (
@@ -1355,7 +1390,8 @@ def machine_reference(stream, prefill_launch_bytes=PREFILL_LAUNCH_BYTES):
             "prefill_layout_TBs": lay["traffic"]["TB/s"],
             "prefill_layout_with_taps_and_halo_TBs": lay["traffic_taps_and_halo"]["TB/s"],
             "empty_launch_us": f["empty"],
-            "decode_chain_floor_us": f["table_row_then_3_tap_rows"]}
+            "decode_chain_floor_us": fp["table_row_then_3_tap_rows"],
+            "decode_chain_floor_us_args_loaded": f["table_row_then_3_tap_rows"]}
 
 
 # ---------------------------------------------------------------- main

@@ -21,19 +21,35 @@ def test_digest_ignores_comments_and_blank_lines():
 
 
 def test_stored_figures_follow_the_digest(tmp_path, monkeypatch):
-    digest = bench.kernel_source_digest()
+    k = "fused_insert_conv_kernel"
+    digest = bench.kernel_source_digest(k)
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     (tmp_path / "fused_insert_conv_w.md").write_text(
         f"trace_avg_us: 4.500\nkernel_sources: {digest}\n")
     (tmp_path / "counters_w.md").write_text(
         f"hbm_bytes_per_launch: 5205617\nkernel_sources: {digest}\n")
-    assert bench.stored_trace("fused_insert_conv_kernel", "w") == 4.5
-    assert bench.stored_traffic("w") == 5205617.0
+    assert bench.stored_trace(k, "w") == 4.5
+    assert bench.stored_traffic("w", k) == 5205617.0
+    # another kernel's sources do not match this summary
+    assert bench.stored_traffic("w", "update_kernel") is None
     (tmp_path / "fused_insert_conv_w.md").write_text(
         "trace_avg_us: 4.500\nkernel_sources: 0000000000000000\n")
-    assert bench.stored_trace("fused_insert_conv_kernel", "w") is None
-    assert bench.stored_trace("fused_insert_conv_kernel", "missing") is None
-    assert bench.stored_traffic("missing") is None
+    assert bench.stored_trace(k, "w") is None
+    assert bench.stored_trace(k, "missing") is None
+    assert bench.stored_traffic("missing", k) is None
+
+
+def test_kernel_digest_covers_its_source_and_headers():
+    assert bench._kernel_sources("fused_insert_conv_kernel") == [
+        "fused_insert_conv.hip", "gather_window.h", "sconv_device.h", "sconv_host.h"]
+    assert bench._kernel_sources("update_kernel") == [
+        "causal_conv1d.hip", "sconv_device.h", "sconv_host.h"]
+    assert bench._kernel_sources("gather_ssm_kernel") == [
+        "gather_window.h", "gather_window.hip", "sconv_device.h", "sconv_host.h"]
+    assert bench.kernel_source_digest("update_kernel") == bench.kernel_source_digest(
+        "varlen_fwd_kernel")
+    assert bench.kernel_source_digest("update_kernel") != bench.kernel_source_digest(
+        "fused_insert_conv_kernel")
 
 
 def test_committed_profiles_name_their_command_and_digest():

@@ -59,6 +59,7 @@ def test_default_bench_line():
                         1e3 * max(m["prefill_pattern_TBs"], m["prefill_pattern_at_launch_size_TBs"],
                                   m["prefill_layout_TBs"]), rel_tol=1e-3)
     assert 0 < m["empty_launch_us"] < m["decode_chain_floor_us"]
+    assert 0 < m["empty_launch_us"] < m["decode_chain_floor_us_args_loaded"]
     assert math.isclose(j["roofline"]["launch_over_floor"],
                         j["roofline"]["launch_us"] / m["decode_chain_floor_us"], rel_tol=1e-2)
     assert j["prefill"]["roofline"]["frac_of_ceiling"] > 0
