@@ -1363,6 +1363,8 @@ UPD_TOKENS_VEC = [
     ("vec-f32-w4-ring-3", torch.float32, 4, 3, 3, True, "btd", False, True, True, 40),
     ("vec-f32-w2-shift-8", torch.float32, 2, 1, 8, False, "btd", False, True, True, 40),
     ("vec-bf16-w4-ring-1-wide", torch.bfloat16, 4, 3, 1, True, "btd", False, True, True, 1024),
+    # ring positions without state indices (the index load reads a stand-in)
+    ("vec-bf16-w4-ring-3-noidx", torch.bfloat16, 4, 3, 3, True, "btd", False, True, False, 64),
 ]
 
 
