@@ -14,6 +14,9 @@
 //     channels; each lane owns VEC consecutive channels (16 bytes: 8 bf16 or
 //     4 fp32), so every x / out row access of a wave is one contiguous
 //     coalesced segment and every cache access is 16 bytes per lane;
+//   * the values a wave needs before its first load (metadata pointers,
+//     row count, request divider, slab count, ...) arrive as leading scalar
+//     kernel arguments that the hardware preloads into SGPRs;
 //   * the row index is wave-uniform: a tile's positions, slots and request
 //     data arrive in one per-lane gather and are broadcast to SGPRs, block-
 //     table entries come through scalar registers, and every PAD / same-
