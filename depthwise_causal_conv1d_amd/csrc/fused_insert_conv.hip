@@ -358,9 +358,9 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   constexpr bool kGroupStores =
       BT > 1 && (SCONV_FUSED_GROUP_STORES == 1 || (SCONV_FUSED_GROUP_STORES == 2 && !NTX));
   const int lane = threadIdx.x & 63;
-  // The launch geometry comes in the parameters (loaded with them in one
-  // batch) rather than from the implicit arguments, which would cost a
-  // second dependent round trip before any data load could start.
+  // The launch geometry comes from the preloaded leading arguments rather
+  // than from the implicit arguments, which would cost a dependent round
+  // trip before any data load could start.
   // Wave counts are below 2^31 (checked on the host): 32-bit arithmetic.
   const uint32_t group_wave0 =
       (kXcdRuns ? xcd_contiguous(conv_wg, num_groups) : conv_wg) * waves_per_group;
