@@ -318,6 +318,39 @@ def test_folded_table_needs_num_reqs_rows():
                                             query_start_loc=qsl, num_reqs=3)
 
 
+def test_folded_decode_wide_table_stride():
+    """A decode batch whose block table is a view into much wider rows: the
+    guessed launch reads block-table row t ahead through the table's row
+    stride, which it takes as a 32-bit leading kernel argument (here 70 257
+    entries; the entries past each row's first max_blocks are never read)."""
+    import depthwise_causal_conv1d_amd as lib
+    rng = np.random.default_rng(52)
+    R = 96
+    ctx = [int(v) for v in rng.integers(1, 1500, R)]
+    case = workloads.fused_case(52, [1] * R, ctx, H=8, D=128, ws=32, block_size=16, W=4,
+                                dtype=torch.bfloat16, pad_count=5)
+    mb = case.block_table.shape[1]
+    wide = torch.full((case.block_table.shape[0], mb + 70_000), -7, dtype=torch.int32)
+    wide[:, :mb] = case.block_table
+    bt = wide.to(DEV)[:, :mb]
+    assert bt.stride(0) == mb + 70_000
+    x, w, cache = case.x.to(DEV), case.weight.to(DEV), case.cache.to(DEV).clone()
+    pos, sm = case.positions.to(DEV), case.slot_mapping.to(DEV)
+    qsl = case.query_start_loc.to(DEV)
+    out = torch.full_like(x, SENTINEL)
+    say(f"folded decode R={R} table stride {bt.stride(0)}")
+    lib.sconv_fused_insert_conv_qsl(x, w, cache, pos, bt, qsl, case.num_reqs, sm, case.off_s,
+                                    case.ws, case.block_size, case.activation, case.use_residual,
+                                    out=out)
+    torch.cuda.synchronize()
+    out_r, cache_r, _, _ = oracle_fused(case)
+    live = live_rows(case)
+    out_h = to_np(out)
+    assert_close(out_h, out_r, "bf16", "wide-stride decode out", mask=live)
+    assert_bits_equal(out_h[~live], out_r[~live], "wide-stride decode PAD rows untouched")
+    assert_bits_equal(to_np(cache), cache_r, "wide-stride decode cache")
+
+
 def test_streams_decode_block_row_shifted():
     """The same read-ahead in a four-stream launch, rows shifted off their
     guess by empty and two-row requests."""
