@@ -321,8 +321,9 @@ def test_folded_table_needs_num_reqs_rows():
 def test_folded_decode_wide_table_stride():
     """A decode batch whose block table is a view into much wider rows: the
     guessed launch reads block-table row t ahead through the table's row
-    stride, which it takes as a 32-bit leading kernel argument (here 70 257
-    entries; the entries past each row's first max_blocks are never read)."""
+    stride, which it takes as a 32-bit leading kernel argument (here
+    max_blocks + 70 000 entries; the entries past each row's first
+    max_blocks are never read)."""
     import depthwise_causal_conv1d_amd as lib
     rng = np.random.default_rng(52)
     R = 96
