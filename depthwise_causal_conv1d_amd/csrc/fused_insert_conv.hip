@@ -85,6 +85,9 @@ struct FusedParams {
   const int32_t* qsl;       // request row offsets [num_reqs + 1] (or NULL)
   int64_t cs0, cs1, cs2, bt_rs, T;
   int64_t num_tiles;
+#if SCONV_FUSED_STRIDE
+  int32_t walk_per_slab;    // striding launches: waves per slab
+#endif
   FusedStream st[kMaxStreams];
 };
 
@@ -211,6 +214,20 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #ifndef SCONV_FUSED_MS_ORDER
 #define SCONV_FUSED_MS_ORDER 0  // several streams in multi-row tiles: 0 slab-major,
                                 // 1 stream-inner, 2 tile-major
+#endif
+#ifndef SCONV_FUSED_STRIDE
+#define SCONV_FUSED_STRIDE 0  // multi-generation one-stream prefill launches in striding waves:
+                              // 1 every R-th tile, 2 runs of consecutive tiles (measured slower)
+#endif
+#ifndef SCONV_FUSED_STRIDE_WAVES
+#define SCONV_FUSED_STRIDE_WAVES 4096  // waves of a striding launch (about one per resident slot)
+#endif
+#ifndef SCONV_FUSED_STRIDE_LDS
+#define SCONV_FUSED_STRIDE_LDS 40960  // unused LDS per striding workgroup: 4 workgroups per CU
+#endif
+#ifndef SCONV_FUSED_DECODE_LANE_BYTES
+#define SCONV_FUSED_DECODE_LANE_BYTES 16  // bytes per lane of bf16 one-row tiles: 16, or 8
+                                          // (measured slower)
 #endif
 #ifndef SCONV_FUSED_DECODE_TILE_MAJOR
 #define SCONV_FUSED_DECODE_TILE_MAJOR 0  // one stream in one-row tiles: tile-major
@@ -954,6 +971,253 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   }
 }
 
+#if SCONV_FUSED_STRIDE
+// ---------------------------------------------------------------- striding waves
+//
+// A measured alternative for the multi-generation prefill shape (one
+// stream, per-row request buffers, 16-byte lanes, four-row tiles), built
+// only with SCONV_FUSED_STRIDE: about one wave per resident slot, each
+// taking many tiles of one slab (every R-th tile, or a run of consecutive
+// ones) with its filter taps loaded once.  Each tile's halo rows come with
+// its input rows.  Stores are buffer stores issued for every row and lane,
+// a PAD row's or an idle lane's with an offset past the buffer's range
+// (dropped by the hardware), so that the number of stores per tile is
+// fixed and a wait for the next tile's loads never waits for them.  Per
+// row it computes what fused_insert_conv_kernel computes.  Both orders
+// measured slower than one-tile waves.
+constexpr int32_t kDropOffset = (int32_t)0x80000000;
+constexpr int32_t kRangeBytes = 0x7ffffff0;
+
+template <typename D, int VEC, int W>
+__global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_stride_kernel(const FusedParams p) {
+  using S = typename D::storage;
+  using P = Pack<D, VEC>;
+  static_assert(sizeof(typename P::raw_t) == 16, "16-byte lanes");
+  constexpr int BT = 4;
+  constexpr int F = 5;
+  constexpr int kHalo = W > 1 ? W - 1 : 1;
+  S* __restrict__ cache = static_cast<S*>(p.cache);
+  const S* __restrict__ x = static_cast<const S*>(p.st[0].x);
+  const S* __restrict__ wt = static_cast<const S*>(p.st[0].w);
+  S* __restrict__ out = static_cast<S*>(p.st[0].out);
+  const int64_t x_rs = p.st[0].x_rs, out_rs = p.st[0].out_rs;
+  const int lane = threadIdx.x & 63;
+  const uint32_t per_slab = (uint32_t)p.walk_per_slab;
+  const uint32_t num_tiles = (uint32_t)p.num_tiles;
+  const uint32_t wave = xcd_contiguous(blockIdx.x, p.num_groups) * (uint32_t)p.waves_per_group +
+                        (uint32_t)uniform(threadIdx.x >> 6);
+  if (wave >= per_slab * (uint32_t)p.num_slabs) return;
+  const uint32_t slab = wave / per_slab;
+  const uint32_t r0 = wave - slab * per_slab;
+  if (r0 >= num_tiles) return;
+  const int c0 = ((int)slab * 64 + lane) * VEC;
+  const bool on = c0 < p.st[0].C;
+  const int cl = on ? c0 : 0;
+  const int h = on ? c0 / p.st[0].ws : 0;
+  const int jc = c0 - h * p.st[0].ws;
+  const int64_t lane_off = (int64_t)h * p.cs1 + p.st[0].off_s + jc;
+  const int64_t t_last = p.T - 1;
+  const int32_t* __restrict__ seq_idx = p.seq_idx;
+  const int32_t* __restrict__ qstart = p.qs;
+  const int64_t* __restrict__ positions = p.positions;
+  const int64_t* __restrict__ slots = p.slot;
+  const int32_t* __restrict__ btab = p.bt;
+  const bool s_silu = p.st[0].silu != 0, s_res = p.st[0].residual != 0;
+  constexpr int kAux = SCONV_FUSED_NT_STORES ? 2 : 0;
+  auto load_tile = [&](uint32_t tile, int32_t& mv, P (&xr)[BT], P (&hl)[kHalo]) {
+    const int64_t t0 = (int64_t)tile * BT;
+    const int r = lane / F, f = lane - (lane / F) * F;
+    const int64_t t = t0 + r < t_last ? t0 + r : t_last;
+    const int32_t* src =
+        f < 3 ? reinterpret_cast<const int32_t*>(f == 0 ? positions : slots) + 2 * t + (f == 2)
+              : (f == 3 ? seq_idx : qstart) + t;
+    mv = *src;
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      const int64_t ti = t0 + i < t_last ? t0 + i : t_last;
+      xr[i].load(x + ti * x_rs + cl);
+    }
+#pragma unroll
+    for (int m = 1; m <= kHalo; ++m) {
+      const int64_t th = t0 - m >= 0 ? t0 - m : 0;
+      hl[m - 1].load(x + th * x_rs + cl);
+    }
+  };
+  constexpr int kChunk = 16 / (int)sizeof(S);
+  constexpr int kN = VEC * W;
+  static_assert(kN % kChunk == 0, "packed weights come in whole 16-byte chunks");
+  constexpr int kNChunks = kN / kChunk;
+  Pack<D, kChunk> wpk[kNChunks];
+#pragma unroll
+  for (int ch = 0; ch < kNChunks; ++ch) wpk[ch].load(wt + (int64_t)cl * W + ch * kChunk);
+  auto wk = [&](int k, int e) -> float {
+    const int flat = e * W + k;
+    return to_float<D>(__builtin_bit_cast(typename Pack<D, kChunk>::Elems,
+                                          wpk[flat / kChunk].raw).e[flat % kChunk]);
+  };
+  auto process = [&](uint32_t tile, const int32_t mv, const P (&xr)[BT], const P (&halo)[kHalo],
+                     auto&& between) {
+    const int64_t t0 = (int64_t)tile * BT;
+#pragma unroll
+    for (int ch = 0; ch < kNChunks; ++ch) asm volatile("" : "+v"(wpk[ch].raw));
+    int32_t pos[BT], slot[BT], req[BT], qs[BT];
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      pos[i] = __builtin_amdgcn_readlane(mv, F * i);
+      const int32_t lo = __builtin_amdgcn_readlane(mv, F * i + 1);
+      const int32_t hi = __builtin_amdgcn_readlane(mv, F * i + 2);
+      slot[i] = (hi < 0 || t0 + i > t_last) ? -1 : lo;
+      req[i] = __builtin_amdgcn_readlane(mv, F * i + 3);
+      qs[i] = __builtin_amdgcn_readlane(mv, F * i + 4);
+    }
+    P hist1, hist2, hist3;
+    hist1.zero();
+    hist2.zero();
+    hist3.zero();
+    int32_t hist_req = -1;
+    P outv[BT];
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      outv[i].zero();
+      const int64_t t = t0 + i;
+      const int32_t d = (int32_t)(t - qs[i]);
+      if (slot[i] >= 0 && d < W - 1 && req[i] != hist_req && pos[i] - d > 0) {
+        const int32_t first = pos[i] - d;
+        uint32_t hblk[kHalo];
+        int32_t hoff[kHalo];
+        uint32_t hlb[kHalo];
+#pragma unroll
+        for (int m = 1; m <= W - 1; ++m) {
+          const int32_t src = first - m >= 0 ? first - m : 0;
+          hlb[m - 1] = div_n((uint32_t)src, p);
+          hoff[m - 1] = src - (int32_t)hlb[m - 1] * p.N;
+        }
+#pragma unroll
+        for (int m = 2; m <= W - 1; ++m) {
+          if (!(m <= W - 1 - d && first - m >= 0)) {
+            hlb[m - 1] = hlb[0];
+            hoff[m - 1] = hoff[0];
+          }
+        }
+        const __attribute__((address_space(4))) int32_t* bt_c =
+            (const __attribute__((address_space(4))) int32_t*)btab;
+#pragma unroll
+        for (int m = 1; m <= W - 1; ++m)
+          hblk[m - 1] = (uint32_t)bt_c[(int64_t)req[i] * p.bt_rs + hlb[m - 1]];
+        __builtin_amdgcn_sched_barrier(0);
+        auto fetch = [&](int m, P& dst) {
+          dst.load(cache + (int64_t)hblk[m - 1] * p.cs0 + (int64_t)hoff[m - 1] * p.cs2 +
+                   (on ? lane_off : 0));
+        };
+        if constexpr (W > 1) fetch(1, hist1);
+        if constexpr (W > 2) fetch(2, hist2);
+        if constexpr (W > 3) fetch(3, hist3);
+        hist_req = req[i];
+      }
+      if (slot[i] < 0) continue;
+      float acc[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        const int lag = W - 1 - k;
+        P src;
+        if (lag == 0) {
+          src = xr[i];
+        } else if (pos[i] - lag < 0) {
+          src.zero();
+        } else if (lag <= d) {
+          src = i >= lag ? xr[i >= lag ? i - lag : 0] : halo[lag - i - 1 >= 0 ? lag - i - 1 : 0];
+        } else {
+          const int m = lag - d;
+          if (m == 1) src = hist1;
+          else if (m == 2) src = hist2;
+          else src = hist3;
+        }
+        float f[VEC];
+        src.to_float(f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(wk(k, e), f[e], acc[e]);
+      }
+      float y[VEC];
+      {
+        float cur[VEC];
+        xr[i].to_float(cur);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float v = acc[e];
+          if (s_silu) v = silu(v);
+          if (s_res) v += cur[e];
+          y[e] = v;
+        }
+      }
+      outv[i].from_float(y);
+    }
+    between();
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      const bool live = slot[i] >= 0;
+      const int64_t t = live ? t0 + i : 0;
+      const __amdgpu_buffer_rsrc_t ro =
+          __builtin_amdgcn_make_buffer_rsrc(out + t * out_rs, 0, kRangeBytes, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          outv[i].raw, ro, live && on ? c0 * (int32_t)sizeof(S) : kDropOffset, 0, kAux);
+      const uint32_t blk = live ? div_n((uint32_t)slot[i], p) : 0u;
+      const int32_t off = live ? slot[i] - (int32_t)blk * p.N : 0;
+      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+          cache + (int64_t)blk * p.cs0 + (int64_t)off * p.cs2, 0, kRangeBytes, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          xr[i].raw, rc, live && on ? (int32_t)(lane_off * (int64_t)sizeof(S)) : kDropOffset, 0,
+          kAux);
+    }
+  };
+  // Mode 1: wave r takes tiles r, r + R, r + 2R, ... (the chip works on
+  // one band of R tiles at a time).  Mode 2: wave r takes the run of
+  // ceil(tiles / R) consecutive tiles starting at r times that.
+  const uint32_t R = per_slab;
+  uint32_t first, step, end;
+  if constexpr (SCONV_FUSED_STRIDE == 2) {
+    const uint32_t L = (num_tiles + R - 1) / R;
+    first = r0 * L;
+    step = 1;
+    end = first + L < num_tiles ? first + L : num_tiles;
+    if (first >= end) return;
+  } else {
+    first = r0;
+    step = R;
+    end = num_tiles;
+  }
+  // Two register sets in turn; a tile's successor is loaded between its
+  // arithmetic and its stores (the last tile reloads its own rows); the
+  // first two tiles run ahead of the loop, so that every path into it has
+  // the same loads and stores outstanding.
+  int32_t mv_a, mv_b;
+  P xr_a[BT], xr_b[BT], hl_a[kHalo], hl_b[kHalo];
+  auto nxt = [&](uint32_t t) { return t + step < end ? t + step : t; };
+  uint32_t tile = first;
+  load_tile(tile, mv_a, xr_a, hl_a);
+  process(tile, mv_a, xr_a, hl_a, [&] { load_tile(nxt(tile), mv_b, xr_b, hl_b); });
+  if (tile + step >= end) return;
+  process(tile + step, mv_b, xr_b, hl_b, [&] { load_tile(nxt(tile + step), mv_a, xr_a, hl_a); });
+  for (tile += 2 * step; tile < end; tile += 2 * step) {
+    process(tile, mv_a, xr_a, hl_a, [&] { load_tile(nxt(tile), mv_b, xr_b, hl_b); });
+    if (tile + step >= end) break;
+    process(tile + step, mv_b, xr_b, hl_b, [&] { load_tile(nxt(tile + step), mv_a, xr_a, hl_a); });
+  }
+}
+
+template <typename D, int VEC>
+static void launch_stride(int W, const FusedParams& p, uint32_t g, uint32_t th, hipStream_t s) {
+  constexpr uint32_t kLds = SCONV_FUSED_STRIDE_LDS;
+  switch (W) {
+    case 1: hipLaunchKernelGGL((fused_stride_kernel<D, VEC, 1>), dim3(g), dim3(th), kLds, s, p); break;
+    case 2: hipLaunchKernelGGL((fused_stride_kernel<D, VEC, 2>), dim3(g), dim3(th), kLds, s, p); break;
+    case 3: hipLaunchKernelGGL((fused_stride_kernel<D, VEC, 3>), dim3(g), dim3(th), kLds, s, p); break;
+    default: hipLaunchKernelGGL((fused_stride_kernel<D, VEC, 4>), dim3(g), dim3(th), kLds, s, p); break;
+  }
+}
+#endif
+
 // ---------------------------------------------------------------- dispatch
 
 // A fused launch passes, ahead of its parameter block, the values every
@@ -1254,7 +1518,19 @@ static int fused_launch(
       }
     }
   }
-  const int VEC = vec ? vec16 : 1;
+  int VEC = vec ? vec16 : 1;
+  bool narrow = false;
+#if SCONV_FUSED_DECODE_LANE_BYTES == 8
+  // Narrow lanes (8 bytes) for bf16 one-row tiles with W = 2 or 4: twice
+  // the waves, half the arithmetic per lane after the history arrives
+  // (measured slower).
+  if (VEC == 8 && dtype == SCONV_BF16 && (W == 2 || W == 4) && !gather) {
+    int64_t s8 = 0;
+    for (int s = 0; s < num_streams; ++s) s8 += cdiv(C[s], 64 * 8);
+    narrow = pick_bt(T, s8) == 1;
+    if (narrow) VEC = 4;
+  }
+#endif
 
   FusedParams p = {};
   p.cache = cache; p.positions = positions; p.bt = block_table;
@@ -1280,7 +1556,7 @@ static int fused_launch(
     slabs += cdiv(C[s], 64 * VEC);
   }
   p.num_slabs = (int32_t)slabs;
-  const int bt = pick_bt(T, p.num_slabs);
+  const int bt = narrow ? 1 : pick_bt(T, p.num_slabs);
   if (num_streams > 1 && wave_order(true, bt) == kOrderStreamInner) {
     for (int s = 1; s < num_streams; ++s)
       if (p.st[s].slab0 - p.st[s - 1].slab0 != p.st[1].slab0)
@@ -1310,17 +1586,29 @@ static int fused_launch(
   else
     p.bt_pref = 0;
 
-  const int64_t waves = p.num_tiles * p.num_slabs;
+  int64_t waves = p.num_tiles * p.num_slabs;
   if (waves > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
-  const uint32_t threads = waves >= 4096 ? SCONV_FUSED_WG_THREADS : 64;
-  const int64_t grid = cdiv(waves, threads / 64);
-  if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
-  p.num_groups = (uint32_t)grid;
   // Input rows are read once, except the last W-1 rows of a tile, which the
   // next tile of the same slab reads again as its halo.  When all waves are
   // resident at once the launch is latency-bound and streaming loads win;
   // over several generations the halo re-reads must find the rows in L2.
   p.nt_x = waves <= SCONV_FUSED_NT_LOADS_MAX_WAVES;
+  bool stride = false;
+#if SCONV_FUSED_STRIDE
+  // SCONV_FUSED_STRIDE builds: the multi-generation one-stream prefill shape
+  // in striding waves, about SCONV_FUSED_STRIDE_WAVES of them.
+  stride = !qsl && num_streams == 1 && VEC > 1 && bt == 4 && !p.nt_x &&
+           waves > SCONV_FUSED_STRIDE_WAVES && !gather;
+  if (stride) {
+    p.walk_per_slab = (int32_t)((int64_t)SCONV_FUSED_STRIDE_WAVES / slabs > 0
+                                    ? (int64_t)SCONV_FUSED_STRIDE_WAVES / slabs : 1);
+    waves = (int64_t)p.walk_per_slab * slabs;
+  }
+#endif
+  const uint32_t threads = waves >= 4096 || stride ? SCONV_FUSED_WG_THREADS : 64;
+  const int64_t grid = cdiv(waves, threads / 64);
+  if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  p.num_groups = (uint32_t)grid;
   // A history piece of one head is ws elements of a cache row.  In one-row
   // tiles (decode) whose pieces are less than a 128-byte line, streaming
   // loads measured faster: one stream 4.48 -> 4.18 us at 256 requests and
@@ -1388,8 +1676,19 @@ static int fused_launch(
     return check_launch(fn);
   }
 
+#if SCONV_FUSED_STRIDE
+  if (stride) {
+    if (dtype == SCONV_BF16) launch_stride<Bf16, 8>(W, p, (uint32_t)grid, threads, stream);
+    else launch_stride<F32, 4>(W, p, (uint32_t)grid, threads, stream);
+    return check_launch(fn);
+  }
+#endif
   if (dtype == SCONV_BF16) {
     if (VEC == 8) launch_w<Bf16, 8>(W, bt, p, (uint32_t)grid, threads, stream);
+#if SCONV_FUSED_DECODE_LANE_BYTES == 8
+    else if (narrow && W == 4) launch<Bf16, 4, 4, 1>(p, (uint32_t)grid, threads, stream);
+    else if (narrow) launch<Bf16, 4, 2, 1>(p, (uint32_t)grid, threads, stream);
+#endif
     else launch_w<Bf16, 1>(W, bt, p, (uint32_t)grid, threads, stream);
   } else {
     if (VEC == 4) launch_w<F32, 4>(W, bt, p, (uint32_t)grid, threads, stream);
