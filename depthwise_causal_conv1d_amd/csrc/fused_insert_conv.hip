@@ -229,6 +229,9 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #define SCONV_FUSED_DECODE_LANE_BYTES 16  // bytes per lane of bf16 one-row tiles: 16, or 8
                                           // (measured slower)
 #endif
+#ifndef SCONV_FUSED_SMALL_WG_THREADS
+#define SCONV_FUSED_SMALL_WG_THREADS 64  // workgroup size of launches below 4096 waves
+#endif
 #ifndef SCONV_FUSED_DECODE_TILE_MAJOR
 #define SCONV_FUSED_DECODE_TILE_MAJOR 0  // one stream in one-row tiles: tile-major
 #endif
@@ -1605,7 +1608,8 @@ static int fused_launch(
     waves = (int64_t)p.walk_per_slab * slabs;
   }
 #endif
-  const uint32_t threads = waves >= 4096 || stride ? SCONV_FUSED_WG_THREADS : 64;
+  const uint32_t threads = waves >= 4096 || stride ? SCONV_FUSED_WG_THREADS
+                                                  : SCONV_FUSED_SMALL_WG_THREADS;
   const int64_t grid = cdiv(waves, threads / 64);
   if (grid > INT32_MAX) return fail(SCONV_ERR_UNSUPPORTED, "%s: grid too large", fn);
   p.num_groups = (uint32_t)grid;
