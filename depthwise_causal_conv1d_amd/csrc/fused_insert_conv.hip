@@ -232,6 +232,10 @@ __device__ __forceinline__ uint32_t div_n(uint32_t v, const FusedParams& p) {
 #ifndef SCONV_FUSED_SMALL_WG_THREADS
 #define SCONV_FUSED_SMALL_WG_THREADS 64  // workgroup size of launches below 4096 waves
 #endif
+#ifndef SCONV_FUSED_BAND_ORDER
+#define SCONV_FUSED_BAND_ORDER 0  // multi-generation one-stream launches: 8 bands of rows, one per
+                                  // XCD, each walked slab-major
+#endif
 #ifndef SCONV_FUSED_DECODE_TILE_MAJOR
 #define SCONV_FUSED_DECODE_TILE_MAJOR 0  // one stream in one-row tiles: tile-major
 #endif
@@ -294,7 +298,13 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   const uint32_t num_tiles = ((uint32_t)a_T + (uint32_t)(BT - 1)) / (uint32_t)BT;
   const uint32_t wpg_log2 = a_packed >> 20;
   const uint32_t waves_per_group = 1u << wpg_log2;
-  const uint32_t total_waves = num_tiles * (uint32_t)a_num_slabs;
+  // SCONV_FUSED_BAND_ORDER: multi-generation one-stream launches cut the
+  // rows into 8 bands of tb tiles (one per XCD, each walked slab-major),
+  // with the last band's waves past the rows idle.
+  constexpr bool kBand = SCONV_FUSED_BAND_ORDER && BT > 1 && !NTX && !MS && !GW;
+  const uint32_t tb = (num_tiles + 7u) / 8u;
+  const uint32_t total_waves = kBand ? 8u * tb * (uint32_t)a_num_slabs
+                                     : num_tiles * (uint32_t)a_num_slabs;
   const uint32_t num_groups = (total_waves + waves_per_group - 1) >> wpg_log2;
   uint32_t conv_wg = blockIdx.x;  // this workgroup's number among the conv's
   if constexpr (GW) {
@@ -397,7 +407,16 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
   // in one L2.
   uint32_t tile;
   int slab;
-  if constexpr (kSlabMajor) {
+  bool band_start = false;  // band order: the slab's first tile in the band
+  if constexpr (kBand) {
+    const uint32_t per_band = tb * (uint32_t)a_num_slabs;
+    const uint32_t band = wave / per_band;
+    const uint32_t l = wave - band * per_band;
+    const uint32_t slab_u = l / tb;
+    tile = band * tb + (l - slab_u * tb);  // past the rows: no row of it is live
+    slab = (int)slab_u;
+    band_start = l == slab_u * tb;
+  } else if constexpr (kSlabMajor) {
     const uint32_t slab_u = wave / num_tiles;
     tile = wave - slab_u * num_tiles;
     slab = (int)slab_u;
@@ -750,7 +769,9 @@ __global__ __launch_bounds__(SCONV_FUSED_WG_THREADS) void fused_insert_conv_kern
         for (int ch = 0; ch < kNChunks; ++ch) wpk[ch].raw = s_wts[ch][lane];
       }
     }
-    halo_from_lds = wig > 0 && tile > 0;
+    // (a slab's first tile takes no halo from the previous wave, which
+    // holds another slab's tile)
+    halo_from_lds = wig > 0 && (kBand ? !band_start : tile > 0);
   }
   if (halo_from_lds) {
 #pragma unroll
@@ -1607,6 +1628,12 @@ static int fused_launch(
                                     ? (int64_t)SCONV_FUSED_STRIDE_WAVES / slabs : 1);
     waves = (int64_t)p.walk_per_slab * slabs;
   }
+#endif
+#if SCONV_FUSED_BAND_ORDER
+  // band order, exactly where the kernel takes it (multi-row tiles without
+  // streaming input loads, one stream): 8 bands of ceil(tiles / 8) tiles
+  if (bt > 1 && !(VEC > 1 && bt == 4 && p.nt_x) && num_streams == 1 && !stride)
+    waves = 8 * cdiv(p.num_tiles, 8) * slabs;
 #endif
   const uint32_t threads = waves >= 4096 || stride ? SCONV_FUSED_WG_THREADS
                                                   : SCONV_FUSED_SMALL_WG_THREADS;
